@@ -1,0 +1,110 @@
+"""Pins for the oracle's block forward pass (CPU only):
+* agreement with an independent PyTorch float64 composition,
+* the nesting invariant (essay "LLM Inference: Speculative Decoding",
+  "The four sentences are already inside one sentence": a long pass and a
+  pass on a shorter prefix give the same early answers, printed difference
+  0.0000),
+* dead cache entries never read (essay "The loop", step 5),
+* one-block prefill == token-by-token prefill."""
+import numpy as np
+import pytest
+
+from oracle import model as om
+from target_model_verification_amd import synth
+from torch_reference import TorchRef
+
+SMALL = ["tiny", "small_f32", "small_bf16", "small_int4", "small_gqa", "small_moe"]
+
+
+def _model(name):
+    wl = synth.ALL_WORKLOADS[name]
+    W = synth.make_weights(wl.spec, wl.seed)
+    return wl, W, om.OracleModel(wl.spec, W)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_block_forward_matches_independent_torch(name):
+    wl, W, M = _model(name)
+    toks = synth.prompt_ids(wl, 29)
+    kv = om.KVCache.empty(wl.spec, 64)
+    got = om.forward_block(M, kv, toks[:20], 0).logits
+    got2 = om.forward_block(M, kv, toks[20:], 20).logits
+    ref = TorchRef(wl.spec, W).forward(toks)
+    allg = np.concatenate([got, got2])
+    assert np.max(np.abs(allg - ref)) < 1e-9, np.max(np.abs(allg - ref))
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_gqa", "small_moe", "small_int4"])
+def test_nesting_invariant(name):
+    wl, W, M = _model(name)
+    prompt = synth.prompt_ids(wl, 40)
+    kv, _ = om.prefill(M, prompt, 80)
+    block = synth.prompt_ids(wl, 49)[40:49]          # pending + 8 more ids
+    full = om.forward_block(M, kv.copy(), block, kv.length).logits
+    for j in range(len(block)):
+        short = om.forward_block(M, kv.copy(), block[:j + 1], kv.length).logits
+        assert np.max(np.abs(short[j] - full[j])) < 1e-12
+    # and one token at a time against the same cache
+    kv2 = kv.copy()
+    for j, t in enumerate(block):
+        row = om.forward_block(M, kv2, [t], kv.length + j).logits[0]
+        assert np.max(np.abs(row - full[j])) < 1e-12
+
+
+def test_dead_entries_are_never_read():
+    wl, W, M = _model("small_bf16")
+    prompt = synth.prompt_ids(wl, 50)
+    kv, _ = om.prefill(M, prompt, 90)
+    block = [5, 6, 7, 8]
+    ref = om.forward_block(M, kv.copy(), block, 50).logits
+    poisoned = kv.copy()
+    for l in range(wl.spec.n_layers):
+        poisoned.K[l][:, 50:] = np.nan
+        poisoned.V[l][:, 50:] = np.nan
+    got = om.forward_block(M, poisoned, block, 50).logits
+    assert np.array_equal(got, ref)
+    # rolling back: a rejected block's entries beyond the committed length are
+    # overwritten by the next block and leave no trace
+    kv3 = kv.copy()
+    om.forward_block(M, kv3, [1, 2, 3, 4, 9, 9], 50)      # a block that gets rolled back
+    assert np.array_equal(om.forward_block(M, kv3, block, 50).logits, ref)
+
+
+def test_prefill_block_equals_incremental():
+    wl, W, M = _model("small_gqa")
+    prompt = synth.prompt_ids(wl, 33)
+    kv, last = om.prefill(M, prompt, 40)
+    kv2 = om.KVCache.empty(wl.spec, 40)
+    for i, t in enumerate(prompt):
+        r = om.forward_block(M, kv2, [t], i).logits[0]
+    assert np.max(np.abs(r - last)) < 1e-12
+    for l in range(wl.spec.n_layers):
+        assert np.max(np.abs(kv.K[l][:, :33] - kv2.K[l][:, :33])) < 1e-12
+
+
+def test_moe_union_equals_per_token_loop():
+    wl, W, M = _model("small_moe")
+    spec = wl.spec
+    rng = np.random.default_rng(7)
+    h = rng.standard_normal((9, spec.d_model))
+    y, info = om.moe_ffn(M, 0, h)
+    for j in range(9):
+        r = h[j] @ M["l0.router"] + M["l0.router_bias"]
+        pi = np.exp(r - r.max())
+        pi /= pi.sum()
+        top = sorted(range(spec.n_experts), key=lambda e: (-pi[e], e))[:spec.top_k]
+        ref = sum(pi[e] * om.expert_ffn(M, 0, e, h[j:j + 1])[0] for e in top)
+        ref = ref + om.expert_ffn(M, 0, spec.n_experts, h[j:j + 1])[0]
+        assert np.max(np.abs(y[j] - ref)) < 1e-12
+        assert sorted(top) == sorted(int(e) for e in info["sel"][j])
+    assert info["union"] == sorted(set(int(e) for e in info["sel"].reshape(-1)))
+
+
+def test_router_bias_prior_is_zipf():
+    b = synth.zipf_router_bias(64, 1.1, [1, 2, 3])
+    p = np.exp(b) / np.exp(b).sum()
+    ranks = np.argsort(-p) + 1
+    z = np.arange(1, 65, dtype=np.float64) ** -1.1
+    z /= z.sum()
+    assert np.allclose(np.sort(p)[::-1], z, rtol=1e-6)
+    assert len(set(ranks.tolist())) == 64
