@@ -1,0 +1,217 @@
+/*
+ * spec_verify.h -- C ABI of the target-model verification step of
+ * speculative decoding, for one AMD Instinct MI355X (gfx950) GPU.
+ *
+ * What the step computes (one call of spec_verify_step):
+ *   One target pass over the block [pending, d_1 .. d_k] at cache positions
+ *   L .. L+k gives k+1 rows of logits; row j is what the target would write
+ *   after block token j.  (Essay "LLM Inference: Speculative Decoding",
+ *   section "The loop", step 2; why one pass answers every prefix: section
+ *   "The four sentences are already inside one sentence".)
+ *   Greedy acceptance keeps the longest prefix of drafts that agrees with the
+ *   row-wise argmax and returns the target's own token after it (same
+ *   section, steps 3-4).  Stochastic acceptance applies the rule of Leviathan
+ *   et al. that the essay names in "What is not here": accept d_i with
+ *   probability min(1, p/q), otherwise resample from the normalized positive
+ *   part of p - q; a bonus token is drawn from the last row when all drafts
+ *   pass.  Only accepted entries stay in the KV cache (essay "The loop",
+ *   step 5; S2-MoE section 4.3, "only accepted tokens are committed to the
+ *   shared cache").
+ *
+ * Conventions
+ *   - Every function returns a spec_status (0 = SPEC_OK) unless stated.
+ *     On error the handle's state is unchanged and spec_last_error()
+ *     describes the failure.  A GPU runtime failure in the middle of a step
+ *     (SPEC_EHIP) leaves the handle unusable: later calls return
+ *     SPEC_ESTATE.
+ *   - "host" pointers are ordinary CPU memory; "device" pointers are GPU
+ *     memory on the device that was current at spec_verify_create (for
+ *     example a torch tensor's data_ptr()).  The caller owns every pointer
+ *     it passes; the library keeps none of them after the call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream);
+ *     all work of a handle is enqueued on it.  Streams must have the
+ *     default priority.
+ *   - A handle is not thread-safe; calls on one handle must not overlap.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct spec_verify spec_verify_t;   /* opaque: device weights + KV pages */
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_EINVAL = -1,     /* invalid argument */
+  SPEC_ENOMEM = -2,     /* device or pinned-host allocation failed */
+  SPEC_ECAPACITY = -3,  /* block does not fit in max_ctx */
+  SPEC_EHIP = -4,       /* GPU runtime error */
+  SPEC_ESTATE = -5      /* handle unusable after an earlier GPU error */
+} spec_status;
+
+typedef enum { SPEC_DT_F32 = 0, SPEC_DT_BF16 = 1, SPEC_DT_INT4G128 = 2 } spec_dtype;
+
+typedef enum {
+  SPEC_ACCEPT_GREEDY = 0,
+  SPEC_ACCEPT_STOCHASTIC = 1,
+  /* commit the whole block (append / chunked prefill / resync):
+     n_accepted = k, kv_len = L+k+1, next_token = argmax of row k */
+  SPEC_ACCEPT_NONE = 2
+} spec_accept_mode;
+
+/* Model shape and capacity.  Decoder-only LM: RMSNorm (gain), rotate-half
+ * rotary embedding, causal attention with n_kv_heads groups (query head h
+ * reads KV head h*n_kv_heads/n_q_heads), SwiGLU FFN.  n_experts > 0 selects
+ * a MoE FFN: softmax router with bias over n_experts, each token keeps its
+ * top_k experts by probability (weights = those probabilities, not
+ * renormalized), plus n_shared always-on experts of width d_ff_expert
+ * (S2-MoE section 2.1 and Table 1 give the family). */
+typedef struct {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ff, vocab;
+  int32_t n_experts, top_k, n_shared, d_ff_expert;
+  int32_t weight_dtype;  /* spec_dtype of matmul weights (embedding: bf16 unless F32) */
+  int32_t kv_dtype;      /* SPEC_DT_F32 or SPEC_DT_BF16 */
+  float rope_theta, rms_eps;
+  int32_t max_ctx;       /* KV capacity in positions */
+  int32_t max_k;         /* largest k per step, 0..15 */
+  int32_t gemm_k_split;  /* K elements per split-K slice (multiple of 128); 0 = default */
+  int32_t reserved[7];   /* must be zero */
+} spec_config;
+
+/* Weight tensor kinds.  Matrices are row-major [K][N] with y = x . W. */
+typedef enum {
+  SPEC_T_EMBED = 0,       /* [vocab][d_model] */
+  SPEC_T_FINAL_NORM = 1,  /* [d_model] fp32 gain */
+  SPEC_T_LM_HEAD = 2,     /* [d_model][vocab] */
+  SPEC_T_ATTN_NORM = 3,   /* [d_model] fp32 gain, per layer */
+  SPEC_T_WQ = 4,          /* [d_model][n_q_heads*head_dim] */
+  SPEC_T_WK = 5,          /* [d_model][n_kv_heads*head_dim] */
+  SPEC_T_WV = 6,          /* [d_model][n_kv_heads*head_dim] */
+  SPEC_T_WO = 7,          /* [n_q_heads*head_dim][d_model] */
+  SPEC_T_FFN_NORM = 8,    /* [d_model] fp32 gain */
+  SPEC_T_W_GATE = 9,      /* [d_model][d_ff] (expert: [d_model][d_ff_expert]) */
+  SPEC_T_W_UP = 10,       /* same shape as gate */
+  SPEC_T_W_DOWN = 11,     /* [d_ff][d_model] */
+  SPEC_T_ROUTER = 12,     /* [d_model][n_experts], MoE only */
+  SPEC_T_ROUTER_BIAS = 13 /* [n_experts] fp32, MoE only */
+} spec_tensor_kind;
+
+/* One host weight buffer.  Element types: SPEC_DT_F32 models use fp32 for
+ * everything; otherwise the embedding is bf16 (uint16 bit patterns), gains
+ * and the router bias are fp32, and matrices are bf16 (weight_dtype BF16)
+ * or int4 (INT4G128): part 0 = packed nibbles uint8 [K/2][N] (even k in the
+ * low nibble, two's complement), part 1 = fp16 scales [K/128][N], value =
+ * nibble * scale.  expert = -1 except for MoE FFN matrices, where experts
+ * 0..n_experts-1 are routed and n_experts..n_experts+n_shared-1 shared.
+ * layer = -1 for embed / final norm / lm head. */
+typedef struct {
+  int32_t kind, layer, expert, part;
+  const void* data;   /* host */
+  uint64_t bytes;     /* must equal the size implied by the shape */
+} spec_tensor;
+
+typedef struct {
+  int32_t n_accepted;  /* accepted drafts, 0..k */
+  int32_t next_token;  /* new pending token (correction or bonus); its KV is not cached */
+  int32_t kv_len;      /* committed cache length after the step = L + 1 + n_accepted */
+} spec_step_result;
+
+/* Checks a configuration without touching the GPU.  Returns SPEC_OK or
+ * SPEC_EINVAL; a description of the first problem goes to `msg` (host
+ * buffer of msg_len bytes, may be NULL). */
+int spec_config_check(const spec_config* cfg, char* msg, int32_t msg_len);
+
+/* Creates a verifier: copies every weight to device memory (re-tiled for
+ * the GPU kernels), allocates KV pages for max_ctx positions and copies the
+ * prompt cache in.  prompt_k / prompt_v: host [n_layers][n_kv_heads]
+ * [prompt_len][head_dim] in the KV dtype (bf16 bit patterns or fp32), keys
+ * already rotated; NULL when prompt_len == 0.  Every tensor the config
+ * needs must appear exactly once in `tensors`.  Blocks until the copies are
+ * done.  On success *out owns all device memory until spec_verify_destroy. */
+int spec_verify_create(const spec_config* cfg, const spec_tensor* tensors, int32_t n_tensors,
+                       const void* prompt_k, const void* prompt_v, int32_t prompt_len,
+                       void* stream, spec_verify_t** out);
+
+/* One verification step.
+ *   tokens:  host int32 [k+1] = pending, d_1..d_k; every id in [0, vocab).
+ *   k:       0..max_k (k = 0 is one autoregressive step).
+ *   mode:    spec_accept_mode.
+ *   q_dev:   device fp32 [k][vocab], q_dev[i-1] = draft distribution of d_i
+ *            (STOCHASTIC only; else NULL).  Rows need not be normalized
+ *            beyond what the draft produced; q(d_i) must be > 0.
+ *   u_dev:   device fp32 [k+1] uniforms in [0,1): u_1..u_k for the tests,
+ *            u_{k+1} for the final draw (STOCHASTIC only; else NULL).
+ *   out:     host result.
+ *   logits_dev: NULL or device fp32 [k+1][vocab] receiving the block's logits.
+ * Requires kv_len + k + 1 <= max_ctx (else SPEC_ECAPACITY).  Enqueues the
+ * pass on the handle's stream and returns after the 12-byte result has
+ * reached the host (one stream synchronization).  The committed length
+ * becomes out->kv_len; cache entries at or beyond it are dead. */
+int spec_verify_step(spec_verify_t* h, const int32_t* tokens, int32_t k, int32_t mode,
+                     const float* q_dev, const float* u_dev, spec_step_result* out,
+                     float* logits_dev);
+
+/* Truncates the committed cache to new_kv_len (0 <= new_kv_len <= kv_len):
+ * entries at or beyond it become dead and are overwritten by later blocks.
+ * Metadata only; no device work. */
+int spec_kv_commit_rollback(spec_verify_t* h, int32_t new_kv_len);
+
+/* Committed cache length, or -1 for a NULL handle. */
+int32_t spec_kv_len(const spec_verify_t* h);
+
+/* Last error message of the handle ("" if none); a static message for a
+ * NULL handle.  Valid until the next call on the handle. */
+const char* spec_last_error(const spec_verify_t* h);
+
+/* Frees all device and pinned memory of the handle (synchronizes its
+ * stream first).  NULL is allowed. */
+void spec_verify_destroy(spec_verify_t* h);
+
+/* ---------------------------------------------------------------------
+ * Measurement and debugging hooks (same error conventions).
+ * ------------------------------------------------------------------- */
+
+/* Kernel classes timed by the profiling mode. */
+typedef enum {
+  SPEC_K_EMBED = 0, SPEC_K_QKV = 1, SPEC_K_ATTN = 2, SPEC_K_ATTN_COMBINE = 3,
+  SPEC_K_O = 4, SPEC_K_GATEUP = 5, SPEC_K_DOWN = 6, SPEC_K_ROUTER = 7,
+  SPEC_K_ROUTE = 8, SPEC_K_EXPERT_GATEUP = 9, SPEC_K_EXPERT_DOWN = 10,
+  SPEC_K_MOE_COMBINE = 11, SPEC_K_LMHEAD = 12, SPEC_K_ACCEPT = 13,
+  SPEC_K_NCLASSES = 14
+} spec_kernel_class;
+
+/* on != 0: every following step brackets each kernel launch with HIP
+ * events recorded on the handle's stream and accumulates per-class launch
+ * counts, elapsed milliseconds and algorithmic bytes (weights, KV and
+ * activations each kernel must move).  Enabling resets the counters. */
+int spec_profile_enable(spec_verify_t* h, int32_t on);
+
+/* Reads the accumulated per-class figures since the last enable.
+ * launches / ms / bytes: host arrays of SPEC_K_NCLASSES entries (any may
+ * be NULL). */
+int spec_profile_read(const spec_verify_t* h, int64_t* launches, double* ms, double* bytes);
+
+/* Like spec_verify_step, and additionally copies the residual stream after
+ * every layer into trace_dev (device fp32 [n_layers][k+1][d_model], may be
+ * NULL) and, for MoE models, the number of routed experts loaded by each
+ * layer into union_dev (device int32 [n_layers], may be NULL). */
+int spec_verify_step_debug(spec_verify_t* h, const int32_t* tokens, int32_t k, int32_t mode,
+                           const float* q_dev, const float* u_dev, spec_step_result* out,
+                           float* logits_dev, float* trace_dev, int32_t* union_dev);
+
+/* Algorithmic bytes one verification pass must move for this handle's
+ * model at committed length L with block size k+1 and (MoE) `experts_loaded`
+ * routed experts summed over layers: every weight once, live KV once, new
+ * KV rows, logits (and the draft distributions for stochastic mode). */
+double spec_pass_bytes(const spec_verify_t* h, int32_t L, int32_t k, int32_t mode,
+                       int64_t experts_loaded);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,135 @@
+"""Properties of the GPU path that hold at any size (checked here on the
+reduced variants): the nesting invariant holds bitwise (row j of a block
+pass equals the last row of a pass over the first j+1 tokens -- essay "LLM
+Inference: Speculative Decoding", "The four sentences are already inside
+one sentence"), runs are bitwise repeatable, speculative rounds on the GPU
+emit exactly the GPU's own greedy decode ("The output does not change"),
+rollback leaves no trace (step 5 of "The loop"), and bad calls leave the
+handle's state unchanged."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+from gpu_common import log, make_verifier  # noqa: E402
+from spec_harness import prepare  # noqa: E402
+from target_model_verification_amd import binding as B  # noqa: E402
+from target_model_verification_amd import synth  # noqa: E402
+
+
+def _logits(h, toks, mode=B.SPEC_ACCEPT_GREEDY):
+    V = h.spec.vocab
+    lg = torch.empty((len(toks), V), dtype=torch.float32, device="cuda")
+    res = h.step(toks, mode, 0, 0, lg.data_ptr())
+    return res, lg.cpu().numpy()
+
+
+@pytest.fixture(scope="module", params=["small_bf16", "small_int4", "small_moe", "small_gqa", "tiny"])
+def verifier(request):
+    pw = prepare(synth.ALL_WORKLOADS[request.param])
+    h = make_verifier(pw, max_k=15, gemm_k_split=256 if request.param != "tiny" else 128)
+    yield pw, h
+    h.close()
+
+
+def test_nesting_bitwise(verifier):
+    pw, h = verifier
+    L = h.kv_len
+    toks = synth.prompt_ids(pw.wl, 300)[200:216]
+    toks[0] = pw.pending0
+    _, full = _logits(h, toks)
+    h.rollback(L)
+    for j in range(len(toks)):
+        _, part = _logits(h, toks[:j + 1])
+        h.rollback(L)
+        assert np.array_equal(part[j], full[j]), f"row {j}: max diff {np.max(np.abs(part[j] - full[j]))}"
+
+
+def test_repeatable_bitwise(verifier):
+    pw, h = verifier
+    L = h.kv_len
+    toks = [pw.pending0, 3, 1, 4, 1, 5, 9, 2, 6]
+    r1, a = _logits(h, toks)
+    h.rollback(L)
+    r2, b = _logits(h, toks)
+    h.rollback(L)
+    assert np.array_equal(a, b)
+    assert (r1.n_accepted, r1.next_token, r1.kv_len) == (r2.n_accepted, r2.next_token, r2.kv_len)
+
+
+def test_gpu_spec_equals_gpu_autoregressive(verifier):
+    pw, h = verifier
+    L0 = h.kv_len
+    n = 40
+    ar = []
+    tok = pw.pending0
+    for _ in range(n):
+        r = h.step([tok], B.SPEC_ACCEPT_GREEDY)
+        tok = r.next_token
+        ar.append(tok)
+    h.rollback(L0)
+    seq = [pw.pending0] + ar
+    s, pending, emitted, rnd = 0, pw.pending0, [], 0
+    k = 6
+    while s + k + 1 < len(seq) - 1:
+        d = synth.corrupt_drafts(pw.wl, 1000 + rnd, np.asarray(seq[s + 1:s + 1 + k]), 0.3)
+        r = h.step([pending] + list(d), B.SPEC_ACCEPT_GREEDY)
+        emitted += list(d[:r.n_accepted]) + [r.next_token]
+        s += r.n_accepted + 1
+        pending = r.next_token
+        rnd += 1
+        assert h.kv_len == L0 + s
+    assert emitted == ar[:len(emitted)]
+    h.rollback(L0)
+
+
+def test_rollback_leaves_no_trace(verifier):
+    pw, h = verifier
+    L = h.kv_len
+    toks = [pw.pending0, 7, 8, 9, 10]
+    _, ref = _logits(h, toks)
+    h.rollback(L)
+    _, _ = _logits(h, [pw.pending0, 100, 200, 300, 400, 500, 600])   # a block that is rolled back
+    h.rollback(L)
+    _, again = _logits(h, toks)
+    h.rollback(L)
+    assert np.array_equal(ref, again)
+
+
+def test_bad_calls_leave_state_unchanged(verifier):
+    pw, h = verifier
+    L = h.kv_len
+    V = pw.wl.spec.vocab
+    with pytest.raises(B.SpecError) as e:
+        h.step([pw.pending0] + [1] * 16)                  # k = 16 > max_k
+    assert e.value.code == B.SPEC_EINVAL
+    with pytest.raises(B.SpecError) as e:
+        h.step([pw.pending0, V])                          # id out of range
+    assert e.value.code == B.SPEC_EINVAL
+    with pytest.raises(B.SpecError) as e:
+        h.step([pw.pending0, 1], B.SPEC_ACCEPT_STOCHASTIC)  # no q / u
+    assert e.value.code == B.SPEC_EINVAL
+    with pytest.raises(B.SpecError) as e:
+        h.rollback(L + 1)
+    assert e.value.code == B.SPEC_EINVAL
+    assert h.kv_len == L
+
+
+def test_capacity():
+    pw = prepare(synth.WORKLOADS["tiny"])
+    P = pw.kv0.length
+    h = make_verifier(pw, max_k=4, max_ctx=P + 5)
+    try:
+        r = h.step([pw.pending0, 1, 2, 3, 4], B.SPEC_ACCEPT_NONE)
+        assert r.kv_len == P + 5 and r.n_accepted == 4
+        with pytest.raises(B.SpecError) as e:
+            h.step([1])
+        assert e.value.code == B.SPEC_ECAPACITY
+        assert h.kv_len == P + 5
+        h.rollback(P)
+        assert h.step([pw.pending0]).kv_len == P + 1
+    finally:
+        h.close()
