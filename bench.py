@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Throughput of the target model's verification step on one MI355X.
+
+One "step" is one verification pass: a target forward pass over the block
+[pending, d_1..d_k] against the paged KV cache, then greedy acceptance and
+the KV commit (essay "LLM Inference: Speculative Decoding", section "The
+loop").  The default workload is the LLaMA-2-7B-shaped bf16 target (32
+layers, d 4096, 32 heads x 128, SwiGLU 11008, vocab 32000, weights
+N(0, 0.02)) with a 1024-token random prompt and k = 8 drafts per round, each
+draft the target's greedy continuation replaced by a uniform random id with
+probability 0.3.
+
+Timed region: `--steps` verification steps after `--warmup` untimed ones,
+bracketed by device synchronizations; inputs are resident in HBM (weights,
+KV cache); each step uploads its k+1 token ids and reads back the 12-byte
+result, as the C ABI defines.  Printed: one JSON line with accepted tokens/s
+(metric value), the HBM roofline of the dominant kernel (algorithmic bytes
+per launch over its mean launch time, from HIP events recorded on the
+library's stream while the same steps are replayed), and the CPU oracle
+timed on a bounded sample of the same workload as a baseline.
+
+Flags: --gpus N (only 1 is supported), --steps K, --warmup W, --workload
+NAME, --k K, --k-sweep (extra per-k lines on stderr), --no-cpu-baseline,
+--cpu-seconds S, --calib-copy (adds one plain 1 GiB device copy for
+counter calibration under rocprofv3 --pmc).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+GREEDY_WORKLOADS = ("llama7b", "llama7b_int4", "moe", "tiny")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+GEMM_SOURCE = os.path.join(ROOT, "target_model_verification_amd", "csrc", "gemm.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="llama7b", choices=GREEDY_WORKLOADS)
+    ap.add_argument("--k", type=int, default=None)
+    ap.add_argument("--k-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calib-copy", action="store_true")
+    return ap.parse_args()
+
+
+class Session:
+    """A verifier for one workload with its prompt prefilled on the GPU and
+    the target's greedy continuation (the drafts' source) computed once."""
+
+    def __init__(self, wl, W, max_k: int, rounds: int, stream):
+        import numpy as np
+        from target_model_verification_amd import binding as B
+        from target_model_verification_amd import synth
+        self.B, self.np = B, np
+        self.wl = wl
+        self.spec = wl.spec
+        self.max_k = max_k
+        self.n_ref = rounds * (max_k + 1) + 1
+        self.max_ctx = wl.context + self.n_ref + 2 * (max_k + 1) + 64
+        t = time.time()
+        self.h = B.Verifier(wl.spec, W, None, None, 0, self.max_ctx, 15, stream)
+        log(f"[bench] verifier created in {time.time() - t:.1f} s (max_ctx {self.max_ctx})")
+        # prompt: appended in blocks of 16 (accept mode NONE commits the block)
+        t = time.time()
+        prompt = synth.prompt_ids(wl)
+        res = None
+        for i in range(0, len(prompt), 16):
+            res = self.h.step(prompt[i:i + 16], B.SPEC_ACCEPT_NONE)
+        self.L0 = self.h.kv_len
+        self.pending0 = int(res.next_token)
+        # the target's greedy continuation after the prompt (k = 0 steps)
+        ref = [self.pending0]
+        for _ in range(self.n_ref):
+            ref.append(int(self.h.step([ref[-1]], B.SPEC_ACCEPT_GREEDY).next_token))
+        self.ref = np.asarray(ref, dtype=np.int64)
+        self.h.rollback(self.L0)
+        log(f"[bench] prompt {len(prompt)} prefilled and {self.n_ref} greedy tokens decoded in "
+            f"{time.time() - t:.1f} s")
+
+    def rounds(self, k: int, n: int, first_round: int = 0):
+        """Per-round corruption draws for rounds first_round.. (drawn ahead so
+        the timed loop does no random-number work)."""
+        from target_model_verification_amd import synth
+        return [synth.draft_corruption(self.wl, first_round + r, k) for r in range(n)]
+
+    def run(self, k: int, corr, s: int, pending: int, profile: bool = False):
+        """Runs len(corr) rounds from sequence index s.  Returns per-round
+        (L, n_acc), the new s and pending token, and the elapsed seconds."""
+        import torch
+        np, B = self.np, self.B
+        h = self.h
+        out = []
+        tok = np.empty(k + 1, dtype=np.int32)
+        if profile:
+            h.profile(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for flags, ids in corr:
+            tok[0] = pending
+            tok[1:] = np.where(flags, ids, self.ref[s + 1:s + 1 + k])
+            L = h.kv_len
+            res = h.step(tok, B.SPEC_ACCEPT_GREEDY)
+            out.append((L, res.n_accepted))
+            s += res.n_accepted + 1
+            pending = res.next_token
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        prof = h.profile_read() if profile else None
+        if profile:
+            h.profile(False)
+        return out, s, pending, dt, prof
+
+
+def measure_k(sess: Session, k: int, warmup: int, steps: int):
+    corr = sess.rounds(k, warmup + steps)
+    sess.h.rollback(sess.L0)
+    _, s, pending, _, _ = sess.run(k, corr[:warmup], 0, sess.pending0)
+    L_start = sess.h.kv_len
+    rec, s_end, _, dt, _ = sess.run(k, corr[warmup:], s, pending)
+    # the same steps again from the same state, with HIP events around
+    # every kernel launch on the library's stream
+    sess.h.rollback(L_start)
+    rec2, _, _, dt2, prof = sess.run(k, corr[warmup:], s, pending, profile=True)
+    if [r[1] for r in rec2] != [r[1] for r in rec]:
+        raise RuntimeError("replayed steps accepted different counts: the pass is not deterministic")
+    accepted = sum(n + 1 for _, n in rec)
+    bytes_total = sum(sess.h.pass_bytes(L, k) for L, _ in rec)
+    return dict(k=k, steps=steps, seconds=dt, ms_per_step=dt / steps * 1e3, accepted=accepted,
+                acc_tok_s=accepted / dt, verified_tok_s=steps * (k + 1) / dt,
+                mean_accept=accepted / steps, pass_gb=bytes_total / steps / 1e9,
+                wall_gbs=bytes_total / dt / 1e9, L_start=L_start, prof=prof, profiled_seconds=dt2)
+
+
+def dominant(prof):
+    """Kernel class with the largest total time: (name, launches, ms, bytes)."""
+    name = max(prof, key=lambda c: prof[c][1])
+    n, ms, by = prof[name]
+    return name, n, ms, by
+
+
+def traffic_for(kernel_class: str):
+    """HBM bytes per launch measured by rocprofv3 counters for this kernel,
+    if recorded for the current GEMM source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256_16") != source_digest(GEMM_SOURCE):
+        return None
+    return t.get("per_launch_bytes", {}).get(kernel_class)
+
+
+def cpu_baseline(wl, W, k: int, L: int, seconds: float, mean_accept: float):
+    """The CPU oracle (NumPy, fp32 BLAS) timed on a bounded sample: whole
+    verification steps (block pass + greedy acceptance) of the same model at
+    the same k and committed length."""
+    import numpy as np
+    from oracle import accept as oacc
+    from oracle import model as om
+    from target_model_verification_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    t = time.time()
+    M = om.OracleModel(wl.spec, W, np.float32)
+    kv = om.KVCache.empty(wl.spec, L + k + 1, np.float32)
+    for l in range(wl.spec.n_layers):
+        n = wl.spec.n_kv_heads * L * wl.spec.head_dim
+        kv.K[l][:, :L, :] = synth.normal_f32(n, 1.0, [wl.seed, 41, l]).reshape(wl.spec.n_kv_heads, L, -1)
+        kv.V[l][:, :L, :] = synth.normal_f32(n, 1.0, [wl.seed, 43, l]).reshape(wl.spec.n_kv_heads, L, -1)
+    kv.length = L
+    log(f"[bench] oracle fp32 model prepared in {time.time() - t:.1f} s")
+    toks = synth.prompt_ids(wl, k + 1)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        res = om.forward_block(M, kv, toks, L)
+        oacc.accept_greedy(res.logits, toks[1:], L)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or (n >= 2 and el + el / n > 2 * seconds):
+            break
+    step_s = el / n
+    return {"value": round(mean_accept / step_s, 3), "unit": "accepted tok/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"{n} verification steps (block pass over k+1={k + 1} tokens at committed length "
+                       f"{L} + greedy acceptance) of the full {wl.spec.name} model in the NumPy oracle, "
+                       f"weights as fp32 BLAS operands, {el:.1f} s; KV cache filled with seeded synthetic "
+                       f"values (the oracle's time does not depend on them); accepted tokens per step "
+                       f"({mean_accept:.3f}) taken from the GPU run, whose outcomes the oracle reproduces"),
+            "ms_per_step": round(step_s * 1e3, 1)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build measures the "
+              "verification step on a single MI355X; multi-GPU sharding is a design note, not a code path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from target_model_verification_amd import binding as B  # noqa: F401  (fails loudly if not built)
+    from target_model_verification_amd import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    k = wl.k if args.k is None else args.k
+    ks = sorted(set(list(wl.k_sweep) + [k])) if args.k_sweep else [k]
+    t = time.time()
+    W = synth.make_weights(wl.spec, wl.seed)
+    log(f"[bench] {wl.spec.name}: {synth.weight_nbytes(W) / 1e9:.2f} GB of weights generated in "
+        f"{time.time() - t:.1f} s")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        sess = Session(wl, W, max(ks), args.warmup + args.steps, stream.cuda_stream)
+        if args.calib_copy:
+            a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+            b = torch.empty_like(a)
+            b.copy_(a)
+            torch.cuda.synchronize()
+            log("[bench] calibration copy: 1 GiB read + 1 GiB written")
+            del a, b
+        results = {}
+        for kk in ks:
+            results[kk] = measure_k(sess, kk, args.warmup, args.steps)
+            r = results[kk]
+            log(f"[bench] k={kk}: {r['ms_per_step']:.3f} ms/step, {r['acc_tok_s']:.1f} accepted tok/s, "
+                f"{r['verified_tok_s']:.1f} verified tok/s, mean accepted+1 {r['mean_accept']:.3f}, "
+                f"{r['pass_gb']:.3f} GB/pass, wall {r['wall_gbs']:.0f} GB/s "
+                f"({r['wall_gbs'] / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+            for c, (n, ms, by) in r["prof"].items():
+                if n:
+                    log(f"[bench]   {c:14s} {n:6d} launches {ms / n * 1e3:9.1f} us/launch "
+                        f"{by / n / 1e6:9.2f} MB/launch {by / ms / 1e6 if ms else 0:8.0f} GB/s")
+    r = results[k]
+    name, n, ms, by = dominant(r["prof"])
+    per_launch_bytes = by / n
+    per_launch_s = ms / n / 1e3
+    achieved = per_launch_bytes / per_launch_s / 1e9
+    traffic = traffic_for(name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": f"gemm class '{name}'", "bytes_per_launch": round(per_launch_bytes),
+                "us_per_launch": round(per_launch_s * 1e6, 2),
+                "pass_wall_gbs": round(r["wall_gbs"], 1),
+                "pass_wall_frac": round(r["wall_gbs"] / HBM_PEAK_GBS, 4)}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, W, k, r["L_start"], args.cpu_seconds, r["mean_accept"])
+    line = {
+        "metric": "accepted tok/s + verify-pass HBM GB/s vs peak, 7B bf16 k=8, single sequence",
+        "value": round(r["acc_tok_s"], 2), "unit": "accepted tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.spec.weight_dtype,
+        "data": "synthetic: random-init weights N(0,0.02), uniform random prompt ids, drafts = target's "
+                "greedy continuation with per-token corruption",
+        "config": {"workload": f"{wl.spec.name} verify pass, k={k}, context {wl.context}, "
+                               f"draft corruption {wl.corruption}, greedy acceptance, single sequence",
+                   "k": k, "context": wl.context, "verified_tok_s": round(r["verified_tok_s"], 2),
+                   "mean_tokens_per_step": round(r["mean_accept"], 4),
+                   "pass_bytes_gb": round(r["pass_gb"], 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if args.k_sweep:
+        line["k_sweep"] = {str(kk): {"ms_per_step": round(v["ms_per_step"], 4),
+                                     "acc_tok_s": round(v["acc_tok_s"], 2),
+                                     "verified_tok_s": round(v["verified_tok_s"], 2),
+                                     "wall_gbs": round(v["wall_gbs"], 1)} for kk, v in results.items()}
+    sess.h.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -334,12 +334,18 @@ def corrupt_drafts(w: Workload, rnd: int, true_next: np.ndarray, c: Optional[flo
     (length k) with each id independently replaced, with probability c, by a
     uniform id on [0, V).  Exactly k flags and k ids are drawn per round, so
     the stream does not depend on acceptance."""
+    flags, ids = draft_corruption(w, rnd, len(true_next), c)
+    return np.where(flags, ids, np.asarray(true_next, dtype=np.int64)).astype(np.int32)
+
+
+def draft_corruption(w: Workload, rnd: int, k: int, c: Optional[float] = None):
+    """The k replacement flags and k replacement ids of round `rnd` (what
+    corrupt_drafts applies), so a timing loop can draw them ahead of time."""
     c = w.corruption if c is None else c
-    k = len(true_next)
     g = _rng(w.seed, 13, rnd, k)
     flags = g.random(k) < c
     ids = g.integers(0, w.spec.vocab, size=k, dtype=np.int64)
-    return np.where(flags, ids, np.asarray(true_next, dtype=np.int64)).astype(np.int32)
+    return flags, ids
 
 
 def round_uniforms(w: Workload, rnd: int, k: int) -> np.ndarray:
@@ -361,3 +367,27 @@ def draft_sample_uniform(w: Workload, rnd: int, i: int) -> float:
 
 def first_pending_uniform(w: Workload) -> float:
     return float(_rng(w.seed, 29).random())
+
+
+def synthetic_prompt_kv(w: Workload, length: Optional[int] = None):
+    """A seeded stand-in for a prefilled prompt cache at full model size:
+    keys and values [n_layers, n_kv_heads, P, head_dim] drawn from
+    N(0, (init_std * sqrt(d_model))^2) -- the spread of x.W for a unit-RMS
+    row x and N(0, init_std^2) weights -- and stored in the KV dtype (bf16
+    bit patterns as uint16, or fp32)."""
+    s = w.spec
+    P = w.context if length is None else length
+    std = s.init_std * math.sqrt(s.d_model)
+    shape = (s.n_layers, s.n_kv_heads, P, s.head_dim)
+    n = int(np.prod(shape))
+    K = normal_f32(n, std, [w.seed, 31]).reshape(shape)
+    V = normal_f32(n, std, [w.seed, 37]).reshape(shape)
+    if s.kv_dtype == "bf16":
+        return _bf16_parallel(K), _bf16_parallel(V)
+    return K, V
+
+
+def synthetic_pending(w: Workload) -> int:
+    """First pending token when the prompt cache is synthetic (no prefill
+    produced one): a seeded uniform id."""
+    return int(_rng(w.seed, 47).integers(0, w.spec.vocab))

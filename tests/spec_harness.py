@@ -28,6 +28,7 @@ class PreparedWorkload:
     kv0: om.KVCache             # prefilled cache (length = context)
     pending0: int
     max_ctx: int
+    prompt_kv: Optional[tuple] = None   # host cache arrays when synthetic
 
 
 def prepare(wl: synth.Workload, dtype=np.float64, prefill_dtype=None, max_ctx=None,
@@ -56,6 +57,8 @@ def prepare(wl: synth.Workload, dtype=np.float64, prefill_dtype=None, max_ctx=No
 def kv_to_host_arrays(pw: PreparedWorkload):
     """Prompt cache as [layers, Hkv, P, D] arrays in the KV storage type:
     bf16 bit patterns (uint16) or fp32."""
+    if getattr(pw, "prompt_kv", None) is not None:
+        return pw.prompt_kv
     P = pw.kv0.length
     K = np.stack([k[:, :P, :] for k in pw.kv0.K])
     V = np.stack([v[:, :P, :] for v in pw.kv0.V])
@@ -131,3 +134,28 @@ def oracle_greedy_rounds(pw: PreparedWorkload, k: int, rounds: int, c=None):
         s += out.n_accepted + 1
         pending = out.next_token
     return np.asarray(emitted, np.int32), outs, ref
+
+
+def prepare_full(wl: synth.Workload, max_ctx: Optional[int] = None) -> PreparedWorkload:
+    """Full-size workload for sampled parity: the oracle in float32 (BLAS)
+    and a seeded synthetic prompt cache of the workload's context length
+    (synth.synthetic_prompt_kv) in place of a CPU prefill, which at 7B scale
+    and 1-4k positions is far beyond the oracle's seconds budget.  The cache
+    values are inputs to both sides; the pending token is a seeded id."""
+    spec = wl.spec
+    W = synth.make_weights(spec, wl.seed)
+    M = om.OracleModel(spec, W, np.float32)
+    Kb, Vb = synth.synthetic_prompt_kv(wl)
+    P = wl.context
+    max_ctx = max_ctx or (P + 4 * 17 + 64)
+    kv = om.KVCache.empty(spec, max_ctx, np.float32)
+    for l in range(spec.n_layers):
+        if spec.kv_dtype == "bf16":
+            kv.K[l][:, :P] = synth.bf16_bits_to_f32(Kb[l])
+            kv.V[l][:, :P] = synth.bf16_bits_to_f32(Vb[l])
+        else:
+            kv.K[l][:, :P] = Kb[l]
+            kv.V[l][:, :P] = Vb[l]
+    kv.length = P
+    return PreparedWorkload(wl, W, M, np.zeros(0, np.int32), kv, synth.synthetic_pending(wl), max_ctx,
+                            (Kb, Vb))

@@ -1,0 +1,67 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (max_k = 15, default split-K): the LLaMA-2-7B-shaped bf16
+target at k = 8 and k = 15, its int4 group-128 quantization, the 64-expert
+MoE, and the Qwen2.5-7B-shaped GQA target with stochastic acceptance.
+
+Both sides start from the same seeded synthetic prompt cache of the
+workload's full context length (a CPU prefill at this scale is beyond the
+oracle's budget; see spec_harness.prepare_full) and run a few verification
+rounds on identical drafts.  Every logit of every round is compared with
+the float32 oracle (max-abs <= 2e-2), and the accepted count, next token and
+cache length must agree exactly unless the oracle flags a near-tie.  The
+nesting invariant (essay "LLM Inference: Speculative Decoding", "The four
+sentences are already inside one sentence") is checked bitwise on the GPU at
+7B size."""
+import gc
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+from gpu_common import log, make_verifier, run_parity_rounds  # noqa: E402
+from oracle import model as om  # noqa: E402
+from spec_harness import prepare_full  # noqa: E402
+from target_model_verification_amd import binding as B  # noqa: E402
+from target_model_verification_amd import synth  # noqa: E402
+
+CASES = [("llama7b", (8, 15), 2), ("llama7b_int4", (8,), 2), ("moe", (8,), 2), ("qwen7b", (10,), 2)]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,ks,rounds", CASES)
+def test_full_size_parity(name, ks, rounds):
+    wl = synth.WORKLOADS[name]
+    log(f"[full] {name}: preparing weights, oracle and synthetic prompt cache ({wl.context} positions)")
+    pw = prepare_full(wl)
+    h = make_verifier(pw, max_k=15)
+    try:
+        log(f"[full] {name}: verifier ready")
+        if name == "llama7b":
+            L = h.kv_len
+            toks = [pw.pending0] + list(synth.prompt_ids(wl, 9)[1:])
+            full = torch.empty((9, wl.spec.vocab), dtype=torch.float32, device="cuda")
+            h.step(toks, B.SPEC_ACCEPT_GREEDY, 0, 0, full.data_ptr())
+            h.rollback(L)
+            for j in (0, 3, 8):
+                part = torch.empty((j + 1, wl.spec.vocab), dtype=torch.float32, device="cuda")
+                h.step(toks[:j + 1], B.SPEC_ACCEPT_GREEDY, 0, 0, part.data_ptr())
+                h.rollback(L)
+                assert torch.equal(part[j], full[j]), f"nesting broken at row {j}"
+            log(f"[full] {name}: nesting bitwise at rows 0, 3, 8")
+        for k in ks:
+            ref = None
+            if wl.accept == "greedy":
+                ref = np.concatenate([[pw.pending0],
+                                      om.ar_decode(pw.M, pw.kv0, pw.pending0, rounds * (k + 1) + 1)])
+            h.rollback(pw.kv0.length)
+            st = run_parity_rounds(pw, h, k, rounds, wl.accept, ref)
+            log(f"[full] {name} k={k}: {st}")
+            assert st["rounds"] == rounds
+    finally:
+        h.close()
+        del pw
+        gc.collect()
