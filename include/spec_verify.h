@@ -63,7 +63,8 @@ typedef enum {
   SPEC_ACCEPT_NONE = 2
 } spec_accept_mode;
 
-/* Model shape and capacity.  Decoder-only LM: RMSNorm (gain), rotate-half
+/* Model shape and capacity.  fp32 weights go with an fp32 KV cache, bf16 and
+ * int4 weights with a bf16 cache.  Decoder-only LM: RMSNorm (gain), rotate-half
  * rotary embedding, causal attention with n_kv_heads groups (query head h
  * reads KV head h*n_kv_heads/n_q_heads), SwiGLU FFN.  n_experts > 0 selects
  * a MoE FFN: softmax router with bias over n_experts, each token keeps its
@@ -78,7 +79,9 @@ typedef struct {
   float rope_theta, rms_eps;
   int32_t max_ctx;       /* KV capacity in positions */
   int32_t max_k;         /* largest k per step, 0..15 */
-  int32_t gemm_k_split;  /* K elements per split-K slice (multiple of 128); 0 = default */
+  int32_t gemm_k_split;  /* K elements per staged activation window of the weight-streaming
+                            phases (multiple of 128, at most 1024); 0 = 1024.  Smaller windows
+                            split every output over more partial sums (a test knob). */
   int32_t reserved[7];   /* must be zero */
 } spec_config;
 
@@ -124,6 +127,15 @@ typedef struct {
  * SPEC_EINVAL; a description of the first problem goes to `msg` (host
  * buffer of msg_len bytes, may be NULL). */
 int spec_config_check(const spec_config* cfg, char* msg, int32_t msg_len);
+
+/* Host-only diagnostic of the work split: builds the weight-streaming plan
+ * a verifier of this configuration would use on a grid of n_wg workgroups
+ * (one per compute unit, 1 <= n_wg <= 4096) and replays every workgroup's
+ * walk over every weight matrix, checking each index it would form against
+ * the buffer sizes it would allocate.  spec_verify_create runs the same
+ * check for the device's compute-unit count.  Returns SPEC_OK, or
+ * SPEC_EINVAL with the first problem in `msg` (host buffer, may be NULL). */
+int spec_plan_check(const spec_config* cfg, int32_t n_wg, char* msg, int32_t msg_len);
 
 /* Creates a verifier: copies every weight to device memory (re-tiled for
  * the GPU kernels), allocates KV pages for max_ctx positions and copies the
@@ -176,18 +188,27 @@ void spec_verify_destroy(spec_verify_t* h);
  * ------------------------------------------------------------------- */
 
 /* Kernel classes timed by the profiling mode. */
+/* The pass runs as one persistent kernel made of phases separated by grid
+ * barriers; classes name the phases, plus the whole pass kernel and the
+ * acceptance kernel. */
 typedef enum {
   SPEC_K_EMBED = 0, SPEC_K_QKV = 1, SPEC_K_ATTN = 2, SPEC_K_ATTN_COMBINE = 3,
   SPEC_K_O = 4, SPEC_K_GATEUP = 5, SPEC_K_DOWN = 6, SPEC_K_ROUTER = 7,
   SPEC_K_ROUTE = 8, SPEC_K_EXPERT_GATEUP = 9, SPEC_K_EXPERT_DOWN = 10,
   SPEC_K_MOE_COMBINE = 11, SPEC_K_LMHEAD = 12, SPEC_K_ACCEPT = 13,
-  SPEC_K_NCLASSES = 14
+  SPEC_K_PASS = 14,
+  SPEC_K_NCLASSES = 15
 } spec_kernel_class;
 
-/* on != 0: every following step brackets each kernel launch with HIP
- * events recorded on the handle's stream and accumulates per-class launch
- * counts, elapsed milliseconds and algorithmic bytes (weights, KV and
- * activations each kernel must move).  Enabling resets the counters. */
+/* on != 0: every following step times the pass kernel and the acceptance
+ * kernel with HIP events recorded on the handle's stream, and each phase of
+ * the pass with device wall-clock stamps taken by workgroup 0 after every
+ * grid barrier (a phase's time includes its barrier); it accumulates per-
+ * class counts, elapsed milliseconds and algorithmic bytes (weights, KV and
+ * activations each phase must move).  SPEC_K_ATTN_COMBINE is the merge of
+ * the attention groups (no algorithmic bytes of its own: its partials are
+ * an artefact of the split); SPEC_K_ROUTE stays zero (routing runs inside
+ * SPEC_K_EXPERT_GATEUP).  Enabling resets the counters. */
 int spec_profile_enable(spec_verify_t* h, int32_t on);
 
 /* Reads the accumulated per-class figures since the last enable.

@@ -23,7 +23,7 @@ SPEC_ACCEPT_GREEDY, SPEC_ACCEPT_STOCHASTIC, SPEC_ACCEPT_NONE = 0, 1, 2
  SPEC_T_WO, SPEC_T_FFN_NORM, SPEC_T_W_GATE, SPEC_T_W_UP, SPEC_T_W_DOWN, SPEC_T_ROUTER,
  SPEC_T_ROUTER_BIAS) = range(14)
 KERNEL_CLASSES = ["embed", "qkv", "attn", "attn_combine", "o", "gateup", "down", "router", "route",
-                  "expert_gateup", "expert_down", "moe_combine", "lmhead", "accept"]
+                  "expert_gateup", "expert_down", "moe_combine", "lmhead", "accept", "pass"]
 SPEC_K_NCLASSES = len(KERNEL_CLASSES)
 
 
@@ -60,6 +60,7 @@ def _load():
     P, I, F, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_double
     sig = {
         "spec_config_check": (I, [ctypes.POINTER(SpecConfig), ctypes.c_char_p, I]),
+        "spec_plan_check": (I, [ctypes.POINTER(SpecConfig), I, ctypes.c_char_p, I]),
         "spec_verify_create": (I, [ctypes.POINTER(SpecConfig), ctypes.POINTER(SpecTensor), I, P, P, I, P,
                                    ctypes.POINTER(P)]),
         "spec_verify_step": (I, [P, ctypes.POINTER(ctypes.c_int32), I, I, P, P,
@@ -85,6 +86,7 @@ lib = _load()
 
 # same names as the C ABI -------------------------------------------------------
 spec_config_check = lib.spec_config_check
+spec_plan_check = lib.spec_plan_check
 spec_verify_create = lib.spec_verify_create
 spec_verify_step = lib.spec_verify_step
 spec_verify_step_debug = lib.spec_verify_step_debug

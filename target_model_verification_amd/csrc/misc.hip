@@ -1,143 +1,7 @@
-// Small kernels of the verification pass: embedding gather, MoE routing
-// and union build, MoE combine, and on-device acceptance.
+// On-device acceptance of the verification step (one workgroup).
 #include "sv_common.h"
 
 namespace sv {
-
-// ------------------------------------------------------------ embedding
-// x[j][:] = E[tokens[j]][:], plus per-64-column sum-of-squares partials for
-// the first RMSNorm (same grouping as the GEMM residual epilogue).
-template <bool F32>
-__global__ void k_embed(const void* __restrict__ table, const int* __restrict__ tok, int d,
-                        float* __restrict__ x, int ldx, float* __restrict__ ss, int n_ss) {
-  const int gcol = blockIdx.x, j = blockIdx.y, lane = threadIdx.x;
-  const int col = gcol * 64 + lane;
-  const long long row = tok[j];
-  float v = 0.f;
-  if (col < d) {
-    if constexpr (F32) v = static_cast<const float*>(table)[row * d + col];
-    else v = __uint_as_float(((uint32_t) static_cast<const uint16_t*>(table)[row * d + col]) << 16);
-    x[j * ldx + col] = v;
-  }
-  float s = v * v;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
-  if (lane == 0) ss[j * n_ss + gcol] = s;
-}
-
-hipError_t launch_embed(int emb_f32, const void* table, const int* tokens, int m, int d, float* x,
-                        float* ss_out, hipStream_t s) {
-  const int ng = (d + 63) / 64;
-  const int ldx = ((d + 31) / 32) * 32;
-  if (emb_f32)
-    hipLaunchKernelGGL(k_embed<true>, dim3(ng, m), dim3(64), 0, s, table, tokens, d, x, ldx, ss_out, ng);
-  else
-    hipLaunchKernelGGL(k_embed<false>, dim3(ng, m), dim3(64), 0, s, table, tokens, d, x, ldx, ss_out, ng);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------ MoE routing
-// One wave per block row: pi = softmax(r + b) over the experts; top_k by
-// probability, ties to the lower expert id.  Then the union of the rows'
-// selections, listed in ascending expert id; slot_of maps expert -> slot.
-__global__ __launch_bounds__(1024) void k_route(RouteParams p) {
-  __shared__ int used[256];
-  const int tid = threadIdx.x, lane = tid & 63, row = tid >> 6;
-  for (int e = tid; e < p.E; e += blockDim.x) used[e] = 0;
-  __syncthreads();
-  if (row < p.m) {
-    constexpr int EPL = 4;                 // experts per lane (E <= 256)
-    float z[EPL];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
-      z[i] = e < p.E ? p.rlogits[row * p.ldr + e] + p.bias[e] : -INFINITY;
-      mx = fmaxf(mx, z[i]);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    float pr[EPL], sum = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      pr[i] = (lane + 64 * i < p.E) ? expf(z[i] - mx) : 0.f;
-      sum += pr[i];
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
-    bool taken[EPL] = {false, false, false, false};
-    for (int r = 0; r < p.top_k; ++r) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        const int e = lane + 64 * i;
-        if (e < p.E && !taken[i] && (pr[i] > bv || (pr[i] == bv && e < bi))) { bv = pr[i]; bi = e; }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      if (bi >= p.E) bi = 0;               // only reachable with non-finite router logits
-      if ((bi & 63) == lane) taken[bi >> 6] = true;
-      if (lane == 0) {
-        p.sel[row * p.top_k + r] = bi;
-        p.selw[row * p.top_k + r] = bv / sum;
-        used[bi] = 1;
-      }
-    }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int cnt = 0;
-    for (int e = 0; e < p.E; ++e) {
-      if (used[e]) {
-        p.slot_of[e] = cnt;
-        p.union_list[cnt++] = e;
-      } else {
-        p.slot_of[e] = -1;
-      }
-    }
-    *p.union_count = cnt;
-    if (p.union_hist) *p.union_hist = cnt;
-  }
-}
-
-hipError_t launch_route(const RouteParams& p, hipStream_t s) {
-  if (p.E > 256 || p.m > 16) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_route, dim3(1), dim3(1024), 0, s, p);
-  return hipGetLastError();
-}
-
-// x_j += sum_r w_{j,r} y[slot(sel_{j,r})]_j + sum_s y[shared slot s]_j,
-// in rank order then shared; new sum-of-squares partials per 64 columns.
-__global__ void k_moe_combine(MoeCombineParams p) {
-  const int gcol = blockIdx.x, j = blockIdx.y, lane = threadIdx.x;
-  const int col = gcol * 64 + lane;
-  float v = 0.f;
-  if (col < p.d) {
-    const int uc = *p.union_count;
-    float y = 0.f;
-    for (int r = 0; r < p.top_k; ++r) {
-      const int slot = p.slot_of[p.sel[j * p.top_k + r]];
-      y += p.selw[j * p.top_k + r] * p.y[(long long)slot * p.y_stride + j * p.ldy + col];
-    }
-    for (int s = 0; s < p.n_shared; ++s) y += p.y[(long long)(uc + s) * p.y_stride + j * p.ldy + col];
-    v = p.x[j * p.ldx + col] + y;
-    p.x[j * p.ldx + col] = v;
-  }
-  float sq = v * v;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) sq += __shfl_xor(sq, o, 64);
-  if (lane == 0) p.ss_out[j * p.n_ss + gcol] = sq;
-}
-
-hipError_t launch_moe_combine(const MoeCombineParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_moe_combine, dim3((p.d + 63) / 64, p.m), dim3(64), 0, s, p);
-  return hipGetLastError();
-}
 
 // ------------------------------------------------------------ acceptance
 // Greedy (and NONE): a_j = argmax row j (lowest id on ties) from the LM-head

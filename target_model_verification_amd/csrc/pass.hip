@@ -1,0 +1,1257 @@
+// The verification pass as one persistent cooperative kernel (gfx950).
+//
+// One target forward pass over the block [pending, d_1..d_k] (m = k+1 rows)
+// at cache positions L..L+m-1: embedding, then per layer QKV projection,
+// causal attention over the paged KV cache (the block's rotated keys and
+// values are rounded to the KV dtype and appended), O projection, FFN
+// (dense SwiGLU, or MoE router + union of the block's experts + combine),
+// and the LM head.  (Essay "LLM Inference: Speculative Decoding", "The
+// loop" step 2: one target pass answers every block position; S2-MoE §3,
+// Challenge 2: a verification block activates a union of experts.)
+//
+// Why one kernel.  The pass is bound by HBM bandwidth: every weight byte is
+// used by at most 16 rows.  At 7B scale each layer streams ~400 MB in
+// ~60 us at 8 TB/s, so per-kernel launch gaps and ramp-up/drain would cost a
+// large share of the time.  Here one workgroup of 4 waves runs on every CU
+// for the whole pass; phases are separated by grid barriers, and before
+// waiting at a barrier each wave already issues the loads of its first
+// weight batches of the next phase (weights never depend on activations),
+// so HBM keeps streaming through the synchronization.
+//
+// Weight-streaming phases ("GEMM phases") compute Y[m][N] = A[m][K] W[K][N]
+// on v_mfma_f32_16x16x32_bf16 tiles:
+//  - W is pre-tiled into 1 KB B-operand fragments grouped in supergroups of
+//    4 output units (one per wave); the workgroups split the flattened
+//    (supergroup, K chunk) space into equal contiguous runs (stream-K), so
+//    every CU streams the same number of bytes whatever the shape;
+//  - A (the activations) is kept as pre-split bf16 hi + lo fragments; each
+//    weight fragment feeds two MFMAs (hi, lo) so products keep ~16 bits of
+//    activation precision with fp32 accumulation; A windows are staged in
+//    LDS once per workgroup and phase;
+//  - a unit whose K range was split between workgroups is finished by the
+//    last workgroup to arrive (atomic ticket), which sums the partials in
+//    ascending K order: results are deterministic and do not depend on m;
+//  - RMSNorm is applied as a row scale after the product
+//    ((x * s) . (g * W) = s * ((x * g) . W)); producers of A write x * g.
+#include "sv_common.h"
+#include "stream_plan.h"
+
+namespace sv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const u4 gu4;
+typedef __attribute__((address_space(1))) const uint16_t gu16;
+
+enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+
+// ------------------------------------------------------------ small helpers
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ f32x4 mfma(const u4& a, const u4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 8 signed nibbles of one dword -> 8 bf16 (exact: |q| <= 8)
+__device__ __forceinline__ u4 nib8_to_bf16(uint32_t d) {
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int lo = ((int)(d << (28 - 8 * i))) >> 28;
+    const int hi = ((int)(d << (24 - 8 * i))) >> 28;
+    o[i] = (__float_as_uint((float)lo) >> 16) | (__float_as_uint((float)hi) & 0xFFFF0000u);
+  }
+  return u4{o[0], o[1], o[2], o[3]};
+}
+
+// Element (row, col) of an A operand in hi/lo fragment layout: 32-k chunk
+// col/32 holds 128 uint4 (hi[64], lo[64]); lane l of a fragment holds 8
+// consecutive k of row l%16 starting at 8*(l/16).
+__device__ __forceinline__ void afrag_put(uint4* a, int row, int col, float v) {
+  const uint32_t h = f2bf(v);
+  const uint32_t l = f2bf(v - bf2f(h));
+  const int ch = col >> 5, kk = col & 31;
+  const int ln = row + 16 * (kk >> 3), e = kk & 7;
+  uint16_t* base = reinterpret_cast<uint16_t*>(a + (long long)ch * 128);
+  base[ln * 8 + e] = (uint16_t)h;
+  base[(64 + ln) * 8 + e] = (uint16_t)l;
+}
+
+// raw workgroup barrier: execution only; the compiler may not move memory
+// operations across it
+__device__ __forceinline__ void raw_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// ------------------------------------------------------------ grid barrier
+// Hierarchical: workgroups arrive on one of 8 group counters (by
+// blockIdx % 8, i.e. per XCD under round-robin dispatch), the last of a
+// group arrives on the top counter, the last group publishes the
+// generation on 8 flags, each workgroup polls its group's flag.  Counters
+// are 64-bit and monotonic over the handle's lifetime; the host passes the
+// generation reached before the launch.  Layout (u64, 128-byte lines):
+// group g at 16*g, top at 128, flag g at 16*(9+g).
+struct GridBar {
+  unsigned long long* bar;
+  unsigned long long gen;
+  int* err;          // set to 1 if a wait ran out (the pass then skips all later waits)
+  bool aborted;
+};
+
+// ~2^24 polls of 64 cycles: about half a second at 2.4 GHz, far beyond any
+// legitimate wait
+constexpr unsigned kSpinLimit = 1u << 24;
+
+// Every wave's global writes must be complete before the workgroup's one
+// signalling thread publishes them: the workgroup barrier does not wait for
+// other waves' outstanding stores.  Each wave waits for its own memory
+// operations (completed stores sit in the L2), then the signalling thread's
+// agent-scope release makes the L2 contents visible device-wide.  (A
+// per-wave agent release instead costs about three times as much per grid
+// barrier: every wave then writes back the L2.)
+__device__ __forceinline__ void release_all_waves() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+template <class PF>
+__device__ __forceinline__ void grid_sync(GridBar& gb, PF&& prefetch) {
+  release_all_waves();
+  __syncthreads();
+  ++gb.gen;
+  if (threadIdx.x == 0) {
+    const unsigned g = blockIdx.x & 7u;
+    const unsigned long long ng = (gridDim.x - g + 7u) / 8u;
+    const unsigned long long ngr = gridDim.x < 8 ? gridDim.x : 8;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const unsigned long long old =
+        __hip_atomic_fetch_add(gb.bar + 16 * g, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == gb.gen * ng - 1) {
+      const unsigned long long o2 =
+          __hip_atomic_fetch_add(gb.bar + 128, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (o2 == gb.gen * ngr - 1) {
+        for (int x = 0; x < 8; ++x)
+          __hip_atomic_store(gb.bar + 16 * (9 + x), gb.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  // weight loads of the next phase go out after the arrival, so they stream
+  // during the wait (wave 0 drains its own at its first poll)
+  prefetch();
+  if (threadIdx.x == 0 && !gb.aborted) {
+    const unsigned g = blockIdx.x & 7u;
+    unsigned spins = 0;
+    while (__hip_atomic_load(gb.bar + 16 * (9 + g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gb.gen) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins == kSpinLimit) {
+        gb.aborted = true;
+        __hip_atomic_store(gb.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  raw_barrier();
+}
+
+// ------------------------------------------------------------ LDS plan
+// [0, 2*kAWindowBytes): two staged A windows (GEMM phases) / attention
+// working set; then a small control area.
+constexpr int kCtlBytes = 4096;
+struct Ctl {
+  float rs[16];                 // RMSNorm row scales of the current phase
+  int pend_n;                   // split units this workgroup flushed in the phase
+  int pend[kMaxPending];        // split unit blocks flushed: slot << 20 | sg
+  unsigned char last[kMaxPending];   // 1 if this workgroup is the last arriver
+  int uc;                       // MoE: union size
+  int ulist[256];               // MoE: union (expert ids, ascending)
+  int misc[8];
+};
+static_assert(sizeof(Ctl) <= kCtlBytes, "control area overflows its LDS slot");
+
+__device__ __forceinline__ Ctl* ctl(unsigned char* smem, size_t lds) {
+  return reinterpret_cast<Ctl*>(smem + lds - kCtlBytes);
+}
+
+// ------------------------------------------------------------ GEMM phase
+template <int WF, int TPU>
+struct Fmt {
+  static constexpr int FPC = TPU * (WF == W_F32 ? 2 : 1);   // ring slots per chunk
+  static constexpr int U = batch_chunks(WF, TPU);           // chunks per batch
+  static constexpr int ACH = a_chunks(WF);                  // 32-k A chunks per weight chunk
+};
+
+// One batch of weight fragments per wave (int4 scales travel with their
+// fragments, so the compute loop never waits on another global load).
+// A wave computes on a batch, then issues the next one; the four waves of a
+// CU keep 4 x 32 KB in flight while they wait.
+struct Ring {
+  u4 r[kRing];
+  float s[kRing];
+};
+
+struct SlotMap {
+  const int* ulist;   // MoE union list in LDS (null: dense phase, one slot)
+  int uc, n_experts, n_slots;
+};
+
+// Load cursor: walks the range batch by batch (batches never cross a
+// segment, i.e. one (slot, win, sg) run of chunks).
+struct LCur {
+  Cur q;
+  bool done;
+};
+
+// Loads the next batch (up to U chunks of the current segment) into the ring
+// and advances the cursor.  Slots past the batch re-read its last fragment
+// (they are not used); idle waves (unit past the matrix) skip the loads.
+template <int WF, int TPU>
+__device__ __forceinline__ void next_batch(const Mat& M, const Lin& L, LCur& l, int u1, Ring& ring) {
+  using F = Fmt<WF, TPU>;
+  if (l.done) return;
+  const Cur& q = l.q;
+  const int n = min(F::U, seg_left(q, u1));
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (q.sg * kWaves + wave >= M.n_units) {
+    // idle wave: a defined ring (its compute is skipped), so the ring is
+    // provably overwritten by every batch and dead between phases
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {
+      ring.r[i] = u4{0u, 0u, 0u, 0u};
+      ring.s[i] = 0.f;
+    }
+  } else {
+    const long long fi0 = (((long long)q.sg * M.nkc + (long long)q.win * M.win + q.c) * kWaves + wave) * TPU;
+    const char* wb = static_cast<const char*>(M.w) + (long long)q.e * M.w_stride + fi0 * 1024 + lane * 16;
+    const char* wb2 = static_cast<const char*>(M.w2) + (long long)q.e * M.w2_stride;
+#pragma unroll
+    for (int i = 0; i < F::U; ++i) {
+      const int ii = i < n ? i : n - 1;
+#pragma unroll
+      for (int t = 0; t < TPU; ++t) {
+        const long long fo = ((long long)ii * kWaves * TPU + t) * 1024;
+        if constexpr (WF == W_F32) {
+          ring.r[(i * TPU + t) * 2 + 0] = __builtin_nontemporal_load((gu4*)(wb + fo));
+          ring.r[(i * TPU + t) * 2 + 1] = __builtin_nontemporal_load((gu4*)(wb2 + fi0 * 1024 + lane * 16 + fo));
+        } else {
+          ring.r[i * TPU + t] = __builtin_nontemporal_load((gu4*)(wb + fo));
+          if constexpr (WF == W_INT4) {
+            const gu16* sp = (gu16*)(wb2 + (fi0 + (long long)ii * kWaves * TPU + t) * 32 + (lane & 15) * 2);
+            ring.s[i * TPU + t] = (float)__builtin_bit_cast(_Float16, (uint16_t)*sp);
+          }
+        }
+      }
+    }
+  }
+  batch_advance(L, l.q, n, u1, l.done);
+}
+
+// What a GEMM phase reads and writes besides the weights.
+struct GemmIO {
+  const uint4* a;            // A operand (hi/lo fragments)
+  long long a_slot;          // uint4 per slot (0: shared by all slots)
+  float* out; int ldo; long long out_slot;   // STORE / LOGITS outputs
+  int scale;                 // STORE: multiply by the RMSNorm row scale
+  const float* gain;         // RESID: gain of the next norm
+  uint4* a_out; long long a_out_slot;        // RESID / SWIGLU: next A operand
+  float* trace;              // RESID: residual copy for this layer (nullable)
+};
+
+// Epilogue of one finished unit (one wave, acc[t] = tile t of the unit).
+template <int EPI, int TPU>
+__device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const GemmIO& io, const float* rs, int slot,
+                                         int unit, f32x4 (&acc)[TPU]) {
+  const int lane = threadIdx.x & 63;
+  const int cl = lane & 15, rg = lane >> 4;
+  if constexpr (EPI == EPI_STORE) {
+    const int col = unit * kTileN + cl;
+    float* out = io.out + (long long)slot * io.out_slot;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * rg + i;
+      if (row < P.m && col < M.N) out[(long long)row * io.ldo + col] = io.scale ? rs[row] * acc[0][i] : acc[0][i];
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+    const int col = unit * kTileN + cl;
+    float sq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * rg + i;
+      float v = 0.f;
+      if (row < P.m && col < M.N) {
+        v = P.x[(long long)row * P.ldx + col] + acc[0][i];
+        P.x[(long long)row * P.ldx + col] = v;
+        if (io.trace) io.trace[(long long)row * P.d + col] = v;
+      }
+      sq[i] = v * v;
+      if (col < M.N) afrag_put(io.a_out, row, col, v * io.gain[col]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) sq[i] += __shfl_xor(sq[i], o, 64);
+    }
+    if (cl == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * rg + i;
+        if (row < P.m) P.ss[row * P.n_ss + unit] = sq[i];
+      }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    const int col = unit * kTileN + cl;   // activation column
+    uint4* a_out = io.a_out + (long long)slot * io.a_out_slot;
+    if (col < M.N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * rg + i;
+        float a = 0.f;
+        if (row < P.m) {
+          const float g = rs[row] * acc[0][i];
+          const float u = rs[row] * acc[TPU - 1][i];
+          a = g / (1.0f + expf(-g)) * u;
+        }
+        afrag_put(a_out, row, col, a);
+      }
+    }
+  } else {  // EPI_LOGITS
+    const int col = unit * kTileN + cl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * rg + i;
+      const bool ok = row < P.m && col < M.N;
+      const float v = rs[row] * acc[0][i];
+      if (ok) io.out[(long long)row * io.ldo + col] = v;
+      float mx = ok ? v : -INFINITY;
+      int ix = ok ? col : 0x7fffffff;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float om = __shfl_xor(mx, o, 64);
+        const int oi = __shfl_xor(ix, o, 64);
+        if (om > mx || (om == mx && oi < ix)) { mx = om; ix = oi; }
+      }
+      float e = (ok && mx != -INFINITY) ? expf(v - mx) : 0.f;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) e += __shfl_xor(e, o, 64);
+      if (cl == 0 && row < P.m) {
+        P.st_max[row * P.n_stat + unit] = mx;
+        P.st_sum[row * P.n_stat + unit] = e;
+        P.st_idx[row * P.n_stat + unit] = ix;
+      }
+    }
+  }
+}
+
+// Row scales 1/sqrt(mean(x^2) + eps) from the sum-of-squares partials, in
+// a fixed order (identical in every workgroup).
+__device__ __forceinline__ void row_scales(const PassP& P, float* rs) {
+  const int t = threadIdx.x;
+  const int row = t >> 4, j = t & 15;   // 16 rows x 16 lanes
+  constexpr int B = 16;                 // loads in flight per lane
+  const float* src = P.ss + row * P.n_ss;
+  float s = 0.f;
+  if (row < P.m) {
+    for (int i0 = j; i0 < P.n_ss; i0 += 16 * B) {
+      float v[B];
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        const int i = i0 + 16 * q;
+        v[q] = i < P.n_ss ? src[i] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < B; ++q) s += v[q];
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o, 64);
+  if (j == 0) rs[row] = row < P.m ? 1.0f / sqrtf(s * P.inv_d + P.eps) : 0.f;
+}
+
+// Stages the A window of block (slot, win) into LDS window slot `ws`.
+template <int WF>
+__device__ __forceinline__ void stage_window(const Lin& L, const GemmIO& io, int slot, int win, unsigned char* smem,
+                                             int ws) {
+  constexpr int ACH = (WF == W_INT4) ? 4 : 1;
+  constexpr int B = 8;   // loads in flight per thread
+  const int n16 = L.wlen(win) * ACH * 128;    // uint4 to copy
+  const gu4* src = (const gu4*)(io.a + (long long)slot * io.a_slot + (long long)win * L.W * ACH * 128);
+  u4* dst = reinterpret_cast<u4*>(smem + ws * kAWindowBytes);
+  for (int i0 = threadIdx.x; i0 < n16; i0 += kThreads * B) {
+    u4 v[B];
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      const int i = i0 + q * kThreads;
+      if (i < n16) v[q] = src[i];
+    }
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      const int i = i0 + q * kThreads;
+      if (i < n16) dst[i] = v[q];
+    }
+  }
+}
+
+// One weight-streaming phase over `sm.n_slots` slots (experts) of M.
+template <int WF, int EPI, int TPU>
+__device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const GemmIO io, const SlotMap sm,
+                                        bool slot_major, Ring& ring, unsigned char* smem) {
+  using F = Fmt<WF, TPU>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = gridDim.x, g = blockIdx.x;
+  Ctl* C = ctl(smem, (size_t)P.lds_bytes);
+  const Lin L = make_lin(M, sm.n_slots, slot_major, sm.ulist, sm.uc, sm.n_experts);
+  const int u0 = range_begin(L.total, g, G), u1 = range_begin(L.total, g + 1, G);
+
+  if (threadIdx.x == 0) C->pend_n = 0;
+  if (EPI == EPI_SWIGLU || EPI == EPI_LOGITS || (EPI == EPI_STORE && io.scale)) row_scales(P, C->rs);
+
+  // A windows touched by [u0, u1), staged in order into LDS slots 0 and 1
+  // (key, win) of the blocks in LDS window slots 0 and 1
+  int sk0 = -1, sw0 = -1, sk1 = -1, sw1 = -1;
+  if (u0 < u1) {
+    const Cur a = cur_at(L, u0), b = cur_at(L, u1 - 1);
+    const int ka = slot_major ? a.slot : 0, kb = slot_major ? b.slot : 0;
+    sk0 = ka;
+    sw0 = a.win;
+    stage_window<WF>(L, io, ka, a.win, smem, 0);
+    if (ka != kb || a.win != b.win) {
+      int ns = ka, nw = a.win;
+      if (slot_major) {
+        if (++nw == L.n_win) { nw = 0; ++ns; }
+      } else {
+        ++nw;
+      }
+      sk1 = ns;
+      sw1 = nw;
+      stage_window<WF>(L, io, ns, nw, smem, 1);
+    }
+  }
+  __syncthreads();
+  if (u0 >= u1) return;
+
+  // the caller issued the first batch (gemm_prefetch); advance the load
+  // cursor past it
+  LCur lc;
+  lc.q = cur_at(L, u0);
+  lc.done = false;
+  {
+    batch_advance(L, lc.q, min(F::U, seg_left(lc.q, u1)), u1, lc.done);
+  }
+
+  Cur cc = cur_at(L, u0);
+  int wi = 0;   // LDS window slot in use
+  f32x4 acc[TPU];
+
+  // one batch of n chunks starting at window chunk c0
+  auto compute = [&](int c0, int n, bool live) {
+    if (!live) return;
+    const uint4* aw = reinterpret_cast<const uint4*>(smem + (wi & 1) * kAWindowBytes) + (long long)c0 * F::ACH * 128;
+    const u4 z4 = u4{0u, 0u, 0u, 0u};
+    // branch-free over the batch: slots past n use zero weights and a valid
+    // (finite) A chunk, so they add exact zeros
+#pragma unroll
+    for (int i = 0; i < F::U; ++i) {
+      const bool ok = i < n;
+      const int ai = ok ? i : 0;
+      if constexpr (WF == W_INT4) {
+        f32x4 gacc[TPU];
+#pragma unroll
+        for (int t = 0; t < TPU; ++t) gacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const u4 ah = __builtin_bit_cast(u4, aw[(ai * 4 + q4) * 128 + lane]);
+          const u4 al = __builtin_bit_cast(u4, aw[(ai * 4 + q4) * 128 + 64 + lane]);
+#pragma unroll
+          for (int t = 0; t < TPU; ++t) {
+            const u4 wv = ok ? nib8_to_bf16(ring.r[i * TPU + t][q4]) : z4;
+            gacc[t] = mfma(ah, wv, gacc[t]);
+            gacc[t] = mfma(al, wv, gacc[t]);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < TPU; ++t) acc[t] += (ok ? ring.s[i * TPU + t] : 0.f) * gacc[t];
+      } else {
+        const u4 ah = __builtin_bit_cast(u4, aw[ai * 128 + lane]);
+        const u4 al = __builtin_bit_cast(u4, aw[ai * 128 + 64 + lane]);
+#pragma unroll
+        for (int t = 0; t < TPU; ++t) {
+          if constexpr (WF == W_F32) {
+            const u4 wh = ok ? ring.r[(i * TPU + t) * 2 + 0] : z4, wl = ok ? ring.r[(i * TPU + t) * 2 + 1] : z4;
+            acc[t] = mfma(ah, wh, acc[t]);
+            acc[t] = mfma(al, wh, acc[t]);
+            acc[t] = mfma(ah, wl, acc[t]);
+            acc[t] = mfma(al, wl, acc[t]);
+          } else {
+            const u4 wv = ok ? ring.r[i * TPU + t] : z4;
+            acc[t] = mfma(ah, wv, acc[t]);
+            acc[t] = mfma(al, wv, acc[t]);
+          }
+        }
+      }
+      // keep each chunk's A reads next to its MFMAs (bounded register use)
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    }
+  };
+
+  for (;;) {
+    // ---- one segment: (slot, win, sg), chunks [cc.c, cc.c + nch)
+    const int nch = seg_left(cc, u1);
+    const bool live = cc.sg * kWaves + wave < M.n_units;
+#pragma unroll
+    for (int t = 0; t < TPU; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < nch; c0 += F::U) {
+      const int n = min(F::U, nch - c0);
+      compute(cc.c + c0, n, live);
+      next_batch<WF, TPU>(M, L, lc, u1, ring);
+    }
+    cc.u += nch;
+    cc.c += nch;
+    // ---- flush the segment: epilogue if it covers the whole unit, else a
+    // partial for the last arriver
+    int idx, nseg;
+    seg_info(L, cc.slot, cc.sg, cc.win, g, G, idx, nseg);
+    if (live) {
+      if (nseg == 1) {
+        epilogue<EPI, TPU>(P, M, io, C->rs, cc.slot, cc.sg * kWaves + wave, acc);
+      } else {
+        float* p = P.ws + ((((long long)cc.slot * M.n_sg + cc.sg) * M.max_seg + idx) * kWaves + wave) * TPU * 256;
+#pragma unroll
+        for (int t = 0; t < TPU; ++t) *reinterpret_cast<f32x4*>(p + t * 256 + lane * 4) = acc[t];
+      }
+    }
+    if (nseg > 1 && threadIdx.x == 0) {
+      const int k = C->pend_n;   // capacity guaranteed by the host (kMaxPending)
+      C->pend[k] = cc.slot << 20 | cc.sg;
+      C->pend_n = k + 1;
+    }
+    if (cc.u >= u1) break;
+    seg_advance(L, cc);
+    const int key = slot_major ? cc.slot : 0;
+    const bool same = (wi & 1) ? (key == sk1 && cc.win == sw1) : (key == sk0 && cc.win == sw0);
+    if (!same) {
+      ++wi;
+      if (wi >= 2) {   // a third window: restage (rare)
+        __syncthreads();
+        if (wi & 1) { sk1 = key; sw1 = cc.win; } else { sk0 = key; sw0 = cc.win; }
+        stage_window<WF>(L, io, key, cc.win, smem, wi & 1);
+        __syncthreads();
+      }
+    }
+  }
+
+  // ---- split units: tickets, then the last arriver sums partials in K order
+  release_all_waves();
+  __syncthreads();
+  const int np = C->pend_n;
+  if (np == 0) return;
+  // one lane per split block: the tickets go out together, after one
+  // agent-scope release per signalling wave (every partial of this
+  // workgroup is complete in the L2 by now)
+  if (threadIdx.x < np) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  for (int k = threadIdx.x; k < np; k += kThreads) {
+    const int s = C->pend[k] >> 20, sg = C->pend[k] & 0xfffff;
+    int idx, n;
+    seg_info(L, s, sg, 0, g, G, idx, n);
+    unsigned* t = P.tickets + (long long)s * M.n_sg + sg;
+    const unsigned old = __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == (unsigned)(n - 1);
+    if (last) {
+      __hip_atomic_store(t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    C->last[k] = last ? 1 : 0;
+  }
+  __syncthreads();
+  constexpr int RB = 4;   // partial loads in flight per lane
+  for (int k = 0; k < np; ++k) {
+    if (!C->last[k]) continue;
+    const int s = C->pend[k] >> 20, sg = C->pend[k] & 0xfffff;
+    const int unit = sg * kWaves + wave;
+    if (unit >= M.n_units) continue;
+    int idx, n;
+    seg_info(L, s, sg, 0, g, G, idx, n);
+    f32x4 sum[TPU];
+#pragma unroll
+    for (int t = 0; t < TPU; ++t) sum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float* p = P.ws + ((((long long)s * M.n_sg + sg) * M.max_seg) * kWaves + wave) * TPU * 256 + lane * 4;
+    for (int j0 = 0; j0 < n; j0 += RB) {
+      f32x4 v[RB][TPU];
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+#pragma unroll
+        for (int t = 0; t < TPU; ++t)
+          v[q][t] = j0 + q < n ? *reinterpret_cast<const f32x4*>(p + (long long)(j0 + q) * kWaves * TPU * 256 + t * 256)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      // partials are added in K order
+#pragma unroll
+      for (int q = 0; q < RB; ++q) {
+        if (j0 + q < n) {
+#pragma unroll
+          for (int t = 0; t < TPU; ++t) sum[t] += v[q][t];
+        }
+      }
+    }
+    epilogue<EPI, TPU>(P, M, io, C->rs, s, unit, sum);
+  }
+}
+
+// Issues the first two weight batches of a GEMM phase (before the grid
+// barrier that precedes it, so they stream during the wait).  An empty
+// range loads nothing and the phase returns before using the ring.
+template <int WF, int TPU>
+__device__ __forceinline__ void gemm_prefetch(const Mat M, const SlotMap sm, bool slot_major, Ring& ring) {
+  const int G = gridDim.x, g = blockIdx.x;
+  const Lin L = make_lin(M, sm.n_slots, slot_major, sm.ulist, sm.uc, sm.n_experts);
+  const int u0 = range_begin(L.total, g, G), u1 = range_begin(L.total, g + 1, G);
+  if (u0 >= u1) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) {   // nothing to stream: a defined, unused ring
+      ring.r[i] = u4{0u, 0u, 0u, 0u};
+      ring.s[i] = 0.f;
+    }
+    return;
+  }
+  LCur lc;
+  lc.q = cur_at(L, u0);
+  lc.done = false;
+  next_batch<WF, TPU>(M, L, lc, u1, ring);
+}
+
+// ------------------------------------------------------------ embedding
+// x[j] = E[t_j]; A operand x * gain0; sum-of-squares partials per 16 columns.
+__device__ __forceinline__ void embed_phase(const PassP& P, bool emb_f32) {
+  const int n_tiles = (P.d + 15) / 16;
+  const int t = threadIdx.x;
+  const int row = t >> 4, cl = t & 15;
+  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    if (t >= 256) continue;
+    const int col = tile * 16 + cl;
+    float v = 0.f;
+    if (row < P.m && col < P.d) {
+      const long long tok = P.tokens[row];
+      v = emb_f32 ? static_cast<const float*>(P.embed)[tok * P.d + col]
+                  : bf2f(static_cast<const uint16_t*>(P.embed)[tok * P.d + col]);
+      P.x[(long long)row * P.ldx + col] = v;
+    }
+    if (col < P.d) afrag_put(P.a_norm, row, col, v * P.gain0[col]);
+    float sq = v * v;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o, 64);
+    if (cl == 0 && row < P.m) P.ss[row * P.n_ss + tile] = sq;
+  }
+}
+
+// ------------------------------------------------------------ attention
+// Work item (kv head g, group of kGroupPos positions); block rows
+// r = j*G + hh (block row j, query head g*G + hh) see positions t <= L + j.
+// The group is walked in kPage sub-chunks with a running (max, sum, output)
+// per row: S = Q K^T and O += P V on MFMA (Q and P split into bf16 hi + lo;
+// bf16 keys and values are exact operands, fp32 ones are split too).  An
+// item holding block positions first rotates the new keys, rounds keys and
+// values to the cache dtype and writes them; it then attends to the rounded
+// values like every other position.  Each item leaves per-row (max, sum,
+// unnormalised output); PH_ATTN_MERGE combines the groups in ascending
+// order.  The group grid is fixed, and a masked position or group adds
+// exact zeros, so a row's result does not depend on the block size or on
+// positions after it.
+template <bool KVF32>
+__device__ __forceinline__ float kv_ld(const void* base, long long i) {
+  if constexpr (KVF32) return static_cast<const float*>(base)[i];
+  else return bf2f(static_cast<const uint16_t*>(base)[i]);
+}
+template <bool KVF32>
+__device__ __forceinline__ void kv_st(void* base, long long i, float v) {
+  if constexpr (KVF32) static_cast<float*>(base)[i] = v;
+  else static_cast<uint16_t*>(base)[i] = (uint16_t)f2bf(v);
+}
+template <bool KVF32>
+__device__ __forceinline__ float kv_round(float v) {
+  if constexpr (KVF32) return v;
+  else return bf2f(f2bf(v));
+}
+
+// 8 fp32 -> bf16 hi and lo parts (hi + lo carries ~16 significant bits)
+__device__ __forceinline__ void split8(const float (&v)[8], u4& hi, u4& lo) {
+  uint32_t h[8], l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    h[e] = f2bf(v[e]);
+    l[e] = f2bf(v[e] - bf2f(h[e]));
+  }
+  hi = u4{h[0] | h[1] << 16, h[2] | h[3] << 16, h[4] | h[5] << 16, h[6] | h[7] << 16};
+  lo = u4{l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16, l[6] | l[7] << 16};
+}
+
+// 8 consecutive cache elements at element index i as MFMA operand(s)
+// (bf16: the raw word; fp32: hi and lo parts); lanes with keep == false
+// contribute zeros.
+template <bool KVF32>
+__device__ __forceinline__ void kv_operand(const void* kv, long long i, bool keep, u4& hi, u4& lo) {
+  if constexpr (KVF32) {
+    const gu4* p = (const gu4*)(static_cast<const float*>(kv) + i);
+    const u4 a = p[0], b = p[1];
+    float v[8] = {__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3]),
+                  __uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3])};
+    if (!keep)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    split8(v, hi, lo);
+  } else {
+    const u4 z{0u, 0u, 0u, 0u};
+    hi = keep ? *(const gu4*)(static_cast<const uint16_t*>(kv) + i) : z;
+    lo = z;
+  }
+}
+
+// value operand: 8 consecutive positions of one d from a transposed value
+// page; positions at or past nvalid are zeroed (they may hold any bits)
+template <bool KVF32>
+__device__ __forceinline__ void v_operand(const void* kv, long long i, int p0, int nvalid, u4& hi, u4& lo) {
+  if constexpr (KVF32) {
+    const gu4* p = (const gu4*)(static_cast<const float*>(kv) + i);
+    const u4 a = p[0], b = p[1];
+    float v[8] = {__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3]),
+                  __uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3])};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (p0 + e >= nvalid) v[e] = 0.f;
+    split8(v, hi, lo);
+  } else {
+    u4 w = *(const gu4*)(static_cast<const uint16_t*>(kv) + i);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (p0 + 2 * q >= nvalid) w[q] &= 0xFFFF0000u;
+      if (p0 + 2 * q + 1 >= nvalid) w[q] &= 0x0000FFFFu;
+    }
+    hi = w;
+    lo = u4{0u, 0u, 0u, 0u};
+  }
+}
+
+constexpr int kAttnRT = kMaxAttnRows / 16;   // row tiles at most
+constexpr int kPsStride = kPage + 4;         // floats per score row in LDS
+
+// LDS of the attention phase: Q fragments [RT][D/32][hi|lo][64 lanes],
+// scores / probabilities [RT*16][kPsStride], running max / sum / rescale.
+__host__ __device__ constexpr size_t attn_lds_bytes(int rt, int D) {
+  return (size_t)rt * (D / 32) * 2 * 1024 + (size_t)rt * 16 * kPsStride * 4 + (size_t)3 * rt * 16 * 4;
+}
+
+template <bool KVF32>
+__device__ __forceinline__ void attention_phase(const PassP& P, void* kv, unsigned char* smem) {
+  const int D = P.D, H = D / 2, KDC = D / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int R = P.m * P.G;
+  const int RT = (R + 15) >> 4;
+  const int T = P.L + P.m;
+  u4* Qf = reinterpret_cast<u4*>(smem);                              // [RT][KDC][2][64]
+  float* Ps = reinterpret_cast<float*>(smem + (size_t)RT * KDC * 2 * 1024);   // [RT*16][kPsStride]
+  float* mrun = Ps + RT * 16 * kPsStride;
+  float* lrun = mrun + RT * 16;
+  float* alpha = lrun + RT * 16;
+  const int n_items = P.Hkv * P.n_groups;
+  const int DTW = D / 16 / kWaves;   // value tiles (16 d) per wave: 1 or 2
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+    const int g = item / P.n_groups, grp = item % P.n_groups;
+    const int gt0 = grp * kGroupPos;
+    // ---- Q fragments (rotated, scaled, hi/lo); padding rows are zero
+    for (int i = tid; i < RT * 16 * (D / 8); i += kThreads) {
+      const int r = i / (D / 8), dg = i % (D / 8);
+      const int d0 = dg * 8;
+      float v[8];
+      if (r < R) {
+        const int j = r / P.G, h = g * P.G + r % P.G;
+        const float* qrow = P.qkv + (long long)j * P.ldqkv + h * D;
+        const int pos = P.L + j;
+        const int i0 = d0 < H ? d0 : d0 - H;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float cs = P.rope_cs[((long long)pos * H + i0 + e) * 2 + 0];
+          const float sn = P.rope_cs[((long long)pos * H + i0 + e) * 2 + 1];
+          const float a = qrow[i0 + e], b = qrow[i0 + e + H];
+          v[e] = (d0 < H ? (a * cs - b * sn) : (b * cs + a * sn)) * P.attn_scale;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.f;
+      }
+      u4 hi, lo;
+      split8(v, hi, lo);
+      const int rt = r >> 4, kc = d0 >> 5, ln = (r & 15) + 16 * ((d0 & 31) >> 3);
+      Qf[((rt * KDC + kc) * 2 + 0) * 64 + ln] = hi;
+      Qf[((rt * KDC + kc) * 2 + 1) * 64 + ln] = lo;
+    }
+    for (int r = tid; r < RT * 16; r += kThreads) {
+      mrun[r] = -INFINITY;
+      lrun[r] = 0.f;
+    }
+    // ---- new positions of the block inside this group -> cache
+    const int n0 = max(P.L, gt0), n1 = min(T, gt0 + kGroupPos);
+    if (n0 < n1) {
+      for (int i = tid; i < (n1 - n0) * D; i += kThreads) {
+        const int t = n0 + i / D, d = i % D;
+        const int j = t - P.L;
+        const int phys = P.page_table[t / kPage];
+        const long long kb = (((long long)phys * P.Hkv + g) * 2 + 0) * kPage * D;
+        const long long vb = kb + (long long)kPage * D;
+        const float* krow = P.qkv + (long long)j * P.ldqkv + (P.Hq + g) * D;
+        const float* vrow = P.qkv + (long long)j * P.ldqkv + (P.Hq + P.Hkv + g) * D;
+        const int ii = d < H ? d : d - H;
+        const float cs = P.rope_cs[((long long)t * H + ii) * 2 + 0];
+        const float sn = P.rope_cs[((long long)t * H + ii) * 2 + 1];
+        const float a = krow[ii], b = krow[ii + H];
+        kv_st<KVF32>(kv, kb + (long long)(t % kPage) * D + d, d < H ? (a * cs - b * sn) : (b * cs + a * sn));
+        kv_st<KVF32>(kv, vb + (long long)d * kPage + (t % kPage), vrow[d]);
+      }
+      // the writes must be visible to this workgroup's operand loads below
+      release_all_waves();
+      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+
+    f32x4 acc[kAttnRT][2];
+#pragma unroll
+    for (int rt = 0; rt < kAttnRT; ++rt)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) acc[rt][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int sc = 0; sc < kGroupPages; ++sc) {
+      const int t0 = gt0 + sc * kPage;
+      if (t0 >= T) break;
+      const int nkeys = min(kPage, T - t0);
+      const int phys = P.page_table[t0 / kPage];
+      const long long kb = (((long long)phys * P.Hkv + g) * 2 + 0) * kPage * D;
+      const long long vb = kb + (long long)kPage * D;
+      // operands of this wave: keys 16*wave .. +15 (scores), values of its
+      // d tiles (output)
+      const int key = 16 * wave + (lane & 15);
+      const int kq = 8 * (lane >> 4);
+      u4 kh[4], kl[4], vh[2][2], vl[2][2];
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        if (kc < KDC) kv_operand<KVF32>(kv, kb + (long long)key * D + kc * 32 + kq, key < nkeys, kh[kc], kl[kc]);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        if (q < DTW) {
+          const int d = (wave * DTW + q) * 16 + (lane & 15);
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc)
+            v_operand<KVF32>(kv, vb + (long long)d * kPage + kc * 32 + kq, kc * 32 + kq, nkeys, vh[q][kc], vl[q][kc]);
+        }
+      // ---- scores of this wave's 16 keys for every row tile
+#pragma unroll
+      for (int rt = 0; rt < kAttnRT; ++rt) {
+        if (rt >= RT) break;
+        f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          if (kc >= KDC) break;
+          const u4 qh = Qf[((rt * KDC + kc) * 2 + 0) * 64 + lane];
+          const u4 ql = Qf[((rt * KDC + kc) * 2 + 1) * 64 + lane];
+          s4 = mfma(qh, kh[kc], s4);
+          s4 = mfma(ql, kh[kc], s4);
+          if constexpr (KVF32) {
+            s4 = mfma(qh, kl[kc], s4);
+            s4 = mfma(ql, kl[kc], s4);
+          }
+        }
+        const int tk = t0 + key;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = rt * 16 + 4 * (lane >> 4) + i;
+          const bool vis = r < R && key < nkeys && tk <= P.L + r / P.G;
+          Ps[r * kPsStride + key] = vis ? s4[i] : -INFINITY;
+        }
+      }
+      __syncthreads();
+      // ---- running softmax per row (a wave per row, a lane per key)
+      for (int r = wave; r < RT * 16; r += kWaves) {
+        const float s = Ps[r * kPsStride + lane];
+        float mc = s;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mc = fmaxf(mc, __shfl_xor(mc, o, 64));
+        const float mo = mrun[r];
+        const float mn = fmaxf(mo, mc);
+        const float p = (mn == -INFINITY || s == -INFINITY) ? 0.f : expf(s - mn);
+        float sum = p;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+        Ps[r * kPsStride + lane] = p;
+        if (lane == 0) {
+          const float al = (mn == -INFINITY) ? 1.f : expf(mo - mn);
+          alpha[r] = al;
+          lrun[r] = lrun[r] * al + sum;
+          mrun[r] = mn;
+        }
+      }
+      __syncthreads();
+      // ---- O = O * alpha + P V for this wave's d tiles
+#pragma unroll
+      for (int rt = 0; rt < kAttnRT; ++rt) {
+        if (rt >= RT) break;
+        u4 ph[2], pl[2];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const float* pr = Ps + (rt * 16 + (lane & 15)) * kPsStride + kc * 32 + kq;
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = pr[e];
+          split8(v, ph[kc], pl[kc]);
+        }
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = alpha[rt * 16 + 4 * (lane >> 4) + i];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          if (q >= DTW) break;
+          f32x4 a4 = acc[rt][q];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a4[i] *= al[i];
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc) {
+            a4 = mfma(ph[kc], vh[q][kc], a4);
+            a4 = mfma(pl[kc], vh[q][kc], a4);
+            if constexpr (KVF32) {
+              a4 = mfma(ph[kc], vl[q][kc], a4);
+              a4 = mfma(pl[kc], vl[q][kc], a4);
+            }
+          }
+          acc[rt][q] = a4;
+        }
+      }
+      __syncthreads();
+    }
+    // ---- per-row partials of this group
+    const long long ib = ((long long)g * P.n_groups + grp) * R;
+#pragma unroll
+    for (int rt = 0; rt < kAttnRT; ++rt) {
+      if (rt >= RT) break;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if (q >= DTW) break;
+        const int d = (wave * DTW + q) * 16 + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = rt * 16 + 4 * (lane >> 4) + i;
+          if (r < R) P.pacc[(ib + r) * D + d] = acc[rt][q][i];
+        }
+      }
+    }
+    for (int r = tid; r < R; r += kThreads) {
+      P.pm[ib + r] = mrun[r];
+      P.ps[ib + r] = lrun[r];
+    }
+    __syncthreads();
+  }
+}
+
+// o[r][d] = sum_grp f_grp acc_grp / sum_grp f_grp l_grp with
+// f_grp = exp(m_grp - max m), groups in ascending order; one output element
+// per thread, written into the O projection's A operand.
+__device__ __forceinline__ void attn_merge_phase(const PassP& P) {
+  const int D = P.D, R = P.m * P.G, NG = P.n_groups;
+  const long long total = (long long)P.Hkv * R * D;
+  constexpr int B = 8;   // groups in flight per thread
+  for (long long e = (long long)blockIdx.x * kThreads + threadIdx.x; e < total; e += (long long)gridDim.x * kThreads) {
+    const int d = (int)(e % D);
+    const long long gr = e / D;
+    const int r = (int)(gr % R), g = (int)(gr / R);
+    const long long base = (long long)g * NG * R + r;   // (g, grp, r) at base + grp * R
+    float M = -INFINITY;
+    for (int c0 = 0; c0 < NG; c0 += B) {
+      float v[B];
+#pragma unroll
+      for (int q = 0; q < B; ++q) v[q] = c0 + q < NG ? P.pm[base + (long long)(c0 + q) * R] : -INFINITY;
+#pragma unroll
+      for (int q = 0; q < B; ++q) M = fmaxf(M, v[q]);
+    }
+    float S = 0.f, A = 0.f;
+    for (int c0 = 0; c0 < NG; c0 += B) {
+      float vm[B], vs[B], va[B];
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        const bool ok = c0 + q < NG;
+        const long long pi = base + (long long)(c0 + q) * R;
+        vm[q] = ok ? P.pm[pi] : -INFINITY;
+        vs[q] = ok ? P.ps[pi] : 0.f;
+        va[q] = ok ? P.pacc[pi * D + d] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        if (c0 + q < NG) {
+          const float f = vm[q] == -INFINITY ? 0.f : expf(vm[q] - M);
+          S += f * vs[q];
+          A += f * va[q];
+        }
+      }
+    }
+    const int j = r / P.G, h = g * P.G + r % P.G;
+    afrag_put(P.a_o, j, h * D + d, A / S);
+  }
+}
+
+// ------------------------------------------------------------ MoE routing
+// Every workgroup routes the block redundantly (same inputs, same order):
+// pi = softmax(r + b) over the experts, each row keeps its top_k experts by
+// probability (ties to the lower id), weights = those probabilities; the
+// union of the rows' experts in ascending id order becomes the slot list.
+// Workgroup 0 also writes the routing record for the combine phase.
+__device__ __forceinline__ void route_block(const PassP& P, const float* bias, unsigned char* smem, int layer) {
+  Ctl* C = ctl(smem, (size_t)P.lds_bytes);
+  int* used = reinterpret_cast<int*>(smem);            // [E] (scratch; A windows not live here)
+  int* sel = used + 256;                              // [16][top_k]
+  float* selw = reinterpret_cast<float*>(sel + 16 * 16);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < P.E; e += kThreads) used[e] = 0;
+  __syncthreads();
+  for (int row = wave; row < P.m; row += kWaves) {
+    constexpr int EPL = 4;
+    float z[EPL];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      z[i] = e < P.E ? P.rlog[row * P.ldr + e] + bias[e] : -INFINITY;
+      mx = fmaxf(mx, z[i]);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    float pr[EPL], sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      pr[i] = (lane + 64 * i < P.E) ? expf(z[i] - mx) : 0.f;
+      sum += pr[i];
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+    bool taken[EPL] = {false, false, false, false};
+    for (int r = 0; r < P.top_k; ++r) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        if (e < P.E && !taken[i] && (pr[i] > bv || (pr[i] == bv && e < bi))) { bv = pr[i]; bi = e; }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      if (bi >= P.E) bi = 0;   // only reachable with non-finite router logits
+      if ((bi & 63) == lane) taken[bi >> 6] = true;
+      if (lane == 0) {
+        sel[row * P.top_k + r] = bi;
+        selw[row * P.top_k + r] = bv / sum;
+        used[bi] = 1;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int cnt = 0;
+    for (int e = 0; e < P.E; ++e)
+      if (used[e]) C->ulist[cnt++] = e;
+    C->uc = cnt;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    int* rec = P.route;
+    const int E = P.E, K = P.top_k;
+    if (tid == 0) {
+      rec[0] = C->uc;
+      if (P.union_hist) P.union_hist[layer] = C->uc;
+    }
+    for (int e = tid; e < E; e += kThreads) {
+      rec[1 + e] = e < C->uc ? C->ulist[e] : -1;
+      int s = -1;
+      for (int q = 0; q < C->uc; ++q)
+        if (C->ulist[q] == e) s = q;
+      rec[1 + E + e] = s;
+    }
+    for (int i = tid; i < P.m * K; i += kThreads) {
+      rec[1 + 2 * E + i] = sel[i];
+      reinterpret_cast<float*>(rec)[1 + 2 * E + 16 * K + i] = selw[i];
+    }
+  }
+  __syncthreads();
+}
+
+// x_j += sum_r w_{j,r} y[slot(sel_{j,r})]_j + sum_s y[shared slot s]_j, in
+// rank order then shared; new sum-of-squares partials and next A operand.
+__device__ __forceinline__ void moe_combine_phase(const PassP& P, const float* next_gain, float* trace) {
+  const int n_tiles = (P.d + 15) / 16;
+  const int t = threadIdx.x;
+  const int row = t >> 4, cl = t & 15;
+  const int* rec = P.route;
+  const int E = P.E, K = P.top_k;
+  const int uc = rec[0];
+  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    if (t >= 256) continue;
+    const int col = tile * 16 + cl;
+    float v = 0.f;
+    if (row < P.m && col < P.d) {
+      float y = 0.f;
+      for (int r = 0; r < K; ++r) {
+        const int e = rec[1 + 2 * E + row * K + r];
+        const float w = reinterpret_cast<const float*>(rec)[1 + 2 * E + 16 * K + row * K + r];
+        const int s = rec[1 + E + e];
+        y += w * P.ey[(long long)s * P.ey_slot + (long long)row * P.ldy + col];
+      }
+      for (int s = 0; s < P.n_shared; ++s) y += P.ey[(long long)(uc + s) * P.ey_slot + (long long)row * P.ldy + col];
+      v = P.x[(long long)row * P.ldx + col] + y;
+      P.x[(long long)row * P.ldx + col] = v;
+      if (trace) trace[(long long)row * P.d + col] = v;
+    }
+    if (col < P.d) afrag_put(P.a_norm, row, col, v * next_gain[col]);
+    float sq = v * v;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o, 64);
+    if (cl == 0 && row < P.m) P.ss[row * P.n_ss + tile] = sq;
+  }
+}
+
+// ------------------------------------------------------------ the pass
+__device__ __forceinline__ void stamp(const PassP& P, int& k) {
+  if (P.stamps && blockIdx.x == 0 && threadIdx.x == 0) P.stamps[k] = wall_clock64();
+  ++k;
+}
+
+
+// The pass interprets a program of phases prepared by the host (one entry
+// per phase, a grid barrier between consecutive phases).  Each phase kind
+// is inlined once, and the weight ring lives in registers for the whole
+// pass.
+template <int WF>
+__global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  Ctl* C = ctl(smem, (size_t)P.lds_bytes);
+  GridBar gb{P.bar, P.bar_base, P.err, false};
+  Ring ring;
+  int sk = 0;
+  stamp(P, sk);
+  for (int ph = 0; ph < P.n_prog; ++ph) {
+    // local copy: loop-invariant phase fields stay in registers (the phase's
+    // own stores could otherwise alias the descriptor in memory)
+    const Phase dd = P.prog[ph];
+    const Phase* d = &dd;
+    const int kind = d->kind;
+    GemmIO io;
+    io.a = d->a; io.a_slot = d->a_slot;
+    io.out = d->out; io.ldo = d->ldo; io.out_slot = d->out_slot; io.scale = d->scale;
+    io.gain = d->gain; io.a_out = d->a_out; io.a_out_slot = d->a_out_slot;
+    io.trace = (d->trace && P.trace) ? P.trace + (long long)d->layer * P.m * P.d : nullptr;
+    const SlotMap dense{nullptr, 0, 0, 1};
+    const SlotMap slots{C->ulist, C->uc, P.E, C->uc + P.n_shared};
+    // Each phase but the first starts with a grid barrier.  A weight-
+    // streaming phase issues its first weight batch during that barrier;
+    // the ring is written right before every phase that reads it, so it is
+    // dead (and its registers free) in the other phases.
+    auto sync = [&](auto&& prefetch) {
+      if (ph > 0) {
+        grid_sync(gb, prefetch);
+        stamp(P, sk);
+      } else {
+        prefetch();
+      }
+    };
+    switch (kind) {
+      case PH_EMBED:
+        sync([] {});
+        embed_phase(P, WF == W_F32);
+        break;
+      case PH_STORE: {
+        const SlotMap sm = d->slot_mode ? slots : dense;
+        sync([&] { gemm_prefetch<WF, 1>(d->M, sm, d->slot_mode == 2, ring); });
+        gemm_phase<WF, EPI_STORE, 1>(P, d->M, io, sm, d->slot_mode == 2, ring, smem);
+        break;
+      }
+      case PH_RESID:
+        sync([&] { gemm_prefetch<WF, 1>(d->M, dense, false, ring); });
+        gemm_phase<WF, EPI_RESID, 1>(P, d->M, io, dense, false, ring, smem);
+        break;
+      case PH_ROUTE_SWIGLU:
+        sync([] {});
+      {
+        route_block(P, d->bias, smem, d->layer);
+        const SlotMap routed{C->ulist, C->uc, P.E, C->uc + P.n_shared};   // the union just built
+        gemm_prefetch<WF, 2>(d->M, routed, false, ring);
+        gemm_phase<WF, EPI_SWIGLU, 2>(P, d->M, io, routed, false, ring, smem);
+        break;
+      }
+      case PH_SWIGLU:
+        sync([&] { gemm_prefetch<WF, 2>(d->M, dense, false, ring); });
+        gemm_phase<WF, EPI_SWIGLU, 2>(P, d->M, io, dense, false, ring, smem);
+        break;
+      case PH_LOGITS:
+        sync([&] { gemm_prefetch<WF, 1>(d->M, dense, false, ring); });
+        gemm_phase<WF, EPI_LOGITS, 1>(P, d->M, io, dense, false, ring, smem);
+        break;
+      case PH_ATTN:
+        sync([] {});
+        attention_phase<WF == W_F32>(P, d->kv, smem);
+        break;
+      case PH_ATTN_MERGE:
+        sync([] {});
+        attn_merge_phase(P);
+        break;
+      case PH_COMBINE:
+        sync([] {});
+        moe_combine_phase(P, d->gain, io.trace);
+        break;
+      default:
+        sync([] {});
+        break;
+    }
+  }
+}
+
+size_t pass_lds_bytes(int wfmt, int max_rows_attn, int D) {
+  const size_t gemm = 2 * (size_t)kAWindowBytes;
+  const size_t attn = attn_lds_bytes((max_rows_attn + 15) / 16, D);
+  const size_t route = 4 * (256 + 16 * 16 * 2);
+  size_t b = gemm > attn ? gemm : attn;
+  if (route > b) b = route;
+  (void)wfmt;
+  return b + kCtlBytes;
+}
+
+static const void* pick(int wfmt) {
+  if (wfmt == W_F32) return reinterpret_cast<const void*>(&k_pass<W_F32>);
+  if (wfmt == W_BF16) return reinterpret_cast<const void*>(&k_pass<W_BF16>);
+  if (wfmt == W_INT4) return reinterpret_cast<const void*>(&k_pass<W_INT4>);
+  return nullptr;
+}
+
+hipError_t pass_occupancy(int wfmt, size_t lds, int* blocks_per_cu) {
+  const void* f = pick(wfmt);
+  if (!f) return hipErrorInvalidValue;
+  hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, kThreads, lds);
+}
+
+hipError_t launch_pass(int wfmt, const PassP& p, int n_wg, size_t lds, hipStream_t s) {
+  const void* f = pick(wfmt);
+  if (!f) return hipErrorInvalidValue;
+  PassP q = p;
+  void* args[] = {&q};
+  return hipLaunchCooperativeKernel(f, dim3(n_wg), dim3(kThreads), args, (unsigned)lds, s);
+}
+
+}  // namespace sv

@@ -1,6 +1,7 @@
 // Host runtime of the verification-step library: configuration checks,
-// weight upload and re-tiling, the paged KV cache, the launch sequence of
-// one verification pass, acceptance readback and KV commit / rollback.
+// weight upload into the streaming layout, the paged KV cache, the phase
+// program of one pass, the cooperative launch, acceptance readback and KV
+// commit / rollback.
 #include "../../include/spec_verify.h"
 
 #include <hip/hip_runtime.h>
@@ -15,6 +16,7 @@
 #include <vector>
 
 #include "sv_common.h"
+#include "stream_plan.h"
 
 using namespace sv;
 
@@ -23,25 +25,18 @@ namespace {
 inline int rup(int a, int b) { return ((a + b - 1) / b) * b; }
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-struct Mat {
-  void* w = nullptr;
-  void* w2 = nullptr;
-  int K = 0, N = 0, nkc = 0, n_tiles = 0;
-  long long w_stride = 0, w2_stride = 0;   // bytes per expert (stacked MoE matrices)
-  double alg_bytes = 0;                    // logical weight bytes per expert
+struct HostMat {
+  Mat m{};
+  int tpu = 1, n_stack = 1;
+  double alg_bytes = 0;   // logical weight bytes per expert
 };
 
-struct LayerW {
-  Mat qkv, o, gateup, down, router, ex_gateup, ex_down;
+struct HostLayer {
+  HostMat qkv, o, gateup, down, router, ex_gateup, ex_down;
   float* attn_norm = nullptr;
   float* ffn_norm = nullptr;
   float* router_bias = nullptr;
-};
-
-struct ProfRec {
-  int cls;
-  double bytes;
-  hipEvent_t a, b;
+  void* kv = nullptr;
 };
 
 }  // namespace
@@ -51,9 +46,12 @@ struct spec_verify {
   hipStream_t stream = nullptr;
   int device = 0;
   int wfmt = W_BF16;
-  std::vector<LayerW> layers;
+  int n_wg = 0;                 // workgroups of the pass (one per CU)
+  size_t lds = 0;
+  double wall_khz = 0;          // device wall clock rate (kHz)
+  std::vector<HostLayer> layers;
   void* embed = nullptr;
-  Mat lm_head;
+  HostMat lm_head;
   float* final_norm = nullptr;
   // KV cache
   void* kv = nullptr;
@@ -62,24 +60,30 @@ struct spec_verify {
   int* page_table = nullptr;
   float* rope_cs = nullptr;
   // activations / scratch
-  int ldx = 0, ldqkv = 0, ldo_attn = 0, ldact = 0, ldl = 0, n_ss = 0, n_stat = 0;
-  float *x = nullptr, *qkv = nullptr, *attn_o = nullptr, *act = nullptr, *ss = nullptr, *logits = nullptr;
+  int ldx = 0, ldqkv = 0, ldl = 0, n_ss = 0, n_stat = 0, ldr = 0;
+  float *x = nullptr, *qkv = nullptr, *ss = nullptr, *logits = nullptr;
+  uint4 *a_norm = nullptr, *a_o = nullptr, *a_act = nullptr;
+  long long a_act_slot = 0;
   float *st_max = nullptr, *st_sum = nullptr;
   int* st_idx = nullptr;
   float *pm = nullptr, *ps = nullptr, *pacc = nullptr;
+  float *rlog = nullptr, *ey = nullptr;
+  long long ey_slot = 0;
+  int* route = nullptr;
   float* ws = nullptr;
-  unsigned* counters = nullptr;
+  unsigned* tickets = nullptr;
+  unsigned long long* bar = nullptr;
+  unsigned long long bar_gen = 0;
   int* tokens_dev = nullptr;
   int* result_dev = nullptr;
   int* tokens_host = nullptr;   // pinned
   int* result_host = nullptr;   // pinned
-  // MoE
-  float* rlog = nullptr;
-  int *ucount = nullptr, *ulist = nullptr, *sel = nullptr, *slot_of = nullptr;
-  float* selw = nullptr;
-  float *ex_act = nullptr, *ex_y = nullptr;
-  int ld_exact = 0;
-  long long ex_act_stride = 0, ex_y_stride = 0;
+  // the pass program
+  Phase* prog = nullptr;
+  int n_prog = 0;
+  std::vector<int> prog_cls;    // profiling class of each phase
+  std::vector<int> prog_layer;  // layer of each phase (-1: none)
+  std::vector<double> prog_bytes_fixed;   // weight bytes of each phase (MoE experts: per expert)
   std::vector<void*> allocs;
   // state
   int kv_len = 0;
@@ -87,9 +91,10 @@ struct spec_verify {
   std::string err;
   // profiling
   bool profiling = false;
-  std::vector<ProfRec> prof_pending;
-  std::vector<hipEvent_t> ev_pool;
-  size_t ev_used = 0;
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+  unsigned long long* stamps_dev = nullptr;
+  std::vector<unsigned long long> stamps_host;
+  int* union_dev_prof = nullptr;
   int64_t prof_launches[SPEC_K_NCLASSES] = {};
   double prof_ms[SPEC_K_NCLASSES] = {};
   double prof_bytes[SPEC_K_NCLASSES] = {};
@@ -133,6 +138,20 @@ int dalloc_t(spec_verify* h, T** p, size_t count) {
   return rc;
 }
 
+// zero-filled allocation
+template <typename T>
+int dalloc_z(spec_verify* h, T** p, size_t count) {
+  int rc = dalloc_t(h, p, count);
+  if (rc) return rc;
+  hipError_t e = hipMemsetAsync(*p, 0, std::max<size_t>(count * sizeof(T), 16), h->stream);
+  if (e != hipSuccess) return fail(h, SPEC_EHIP, std::string("memset: ") + hipGetErrorString(e));
+  return SPEC_OK;
+}
+
+double elem_bytes(int dt) { return dt == SPEC_DT_F32 ? 4.0 : dt == SPEC_DT_BF16 ? 2.0 : 0.5; }
+
+int max_rows_attn(const spec_config* c) { return (c->max_k + 1) * (c->n_q_heads / c->n_kv_heads); }
+
 bool check_cfg(const spec_config* c, std::string& msg) {
   auto bad = [&](const char* m) {
     msg = m;
@@ -145,17 +164,19 @@ bool check_cfg(const spec_config* c, std::string& msg) {
   if (c->head_dim != 64 && c->head_dim != 128) return bad("head_dim must be 64 or 128");
   if (c->weight_dtype < SPEC_DT_F32 || c->weight_dtype > SPEC_DT_INT4G128) return bad("bad weight_dtype");
   if (c->kv_dtype != SPEC_DT_F32 && c->kv_dtype != SPEC_DT_BF16) return bad("kv_dtype must be F32 or BF16");
+  if ((c->weight_dtype == SPEC_DT_F32) != (c->kv_dtype == SPEC_DT_F32))
+    return bad("fp32 weights need an fp32 KV cache and bf16/int4 weights a bf16 cache");
   if (c->max_k < 0 || c->max_k > 15) return bad("max_k must be in [0, 15]");
   if (c->max_ctx < 1 || c->max_ctx > (1 << 22)) return bad("max_ctx out of range");
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return bad("rope_theta must be > 0 and rms_eps >= 0");
-  if (c->gemm_k_split < 0 || c->gemm_k_split % 128 != 0 || c->gemm_k_split > 2048)
-    return bad("gemm_k_split must be a multiple of 128 in [0, 2048]");
+  if (c->gemm_k_split < 0 || c->gemm_k_split % 128 != 0 || c->gemm_k_split > 1024)
+    return bad("gemm_k_split must be a multiple of 128 in [0, 1024]");
   for (int i = 0; i < 7; ++i)
     if (c->reserved[i] != 0) return bad("reserved fields must be zero");
   const bool moe = c->n_experts > 0;
   if (moe) {
     if (c->n_experts > 256) return bad("n_experts must be <= 256");
-    if (c->top_k < 1 || c->top_k > c->n_experts) return bad("top_k must be in [1, n_experts]");
+    if (c->top_k < 1 || c->top_k > c->n_experts || c->top_k > 16) return bad("top_k must be in [1, min(16, n_experts)]");
     if (c->n_shared < 0 || c->n_shared > 8) return bad("n_shared must be in [0, 8]");
     if (c->d_ff_expert < 1) return bad("d_ff_expert must be >= 1");
   } else {
@@ -167,15 +188,83 @@ bool check_cfg(const spec_config* c, std::string& msg) {
     if (c->d_model % 128 || (c->n_q_heads * c->head_dim) % 128 || F % 128)
       return bad("int4 weights need d_model, n_q_heads*head_dim and the FFN width divisible by 128");
   }
-  const int G = c->n_q_heads / c->n_kv_heads;
-  const long long R = (long long)(c->max_k + 1) * G;
-  const long long lds = 4LL * (R * c->head_dim + 2LL * kPage * (c->head_dim + 1) + R * kPage);
-  if (lds > 160 * 1024) return bad("(max_k+1) * (n_q_heads/n_kv_heads) too large for the attention kernel");
+  if (c->d_model % 16) return bad("d_model must be a multiple of 16");
+  if (max_rows_attn(c) > kMaxAttnRows)
+    return bad("(max_k+1) * (n_q_heads/n_kv_heads) must be at most 128 (attention rows per KV head)");
+  const size_t lds = pass_lds_bytes(W_BF16, max_rows_attn(c), c->head_dim);
+  if (lds > (size_t)kMaxLds) return bad("the pass does not fit in LDS for this configuration");
   return true;
 }
 
-double elem_bytes(int dt) { return dt == SPEC_DT_F32 ? 4.0 : dt == SPEC_DT_BF16 ? 2.0 : 0.5; }
+// ------------------------------------------------------------------ stream-K plan
+// Geometry of every weight-streaming phase, the split-K workspace and
+// ticket counts they need on a grid of G workgroups, and a host replay of
+// every workgroup's walk (check_gemm_walk) before anything is allocated.
+struct PassPlan {
+  GemmShape qkv{}, o{}, gateup{}, down{}, router{}, ex_gateup{}, ex_down{}, lm_head{};
+  std::vector<GemmShape*> used;
+  size_t ws_floats = 16, n_tickets = 16;
+  long long a_norm = 0, a_o = 0, a_act_slot = 0;   // A operand sizes (uint4)
+};
 
+bool build_plan(const spec_config& c, int wf, int G, PassPlan& P, std::string& err) {
+  const int d = c.d_model, Hq = c.n_q_heads, Hkv = c.n_kv_heads, D = c.head_dim, V = c.vocab;
+  const bool moe = c.n_experts > 0;
+  const int E = c.n_experts, S = c.n_shared, F = moe ? c.d_ff_expert : c.d_ff;
+  const int window_k = c.gemm_k_split > 0 ? c.gemm_k_split : 1024;
+  const int n_slots_max = moe ? E + S : 1;
+  P.a_norm = (long long)cdiv(d, 32) * 128;
+  P.a_o = (long long)cdiv(Hq * D, 32) * 128;
+  P.a_act_slot = (long long)cdiv(F, 32) * 128;
+  auto shape = [&](GemmShape& s, const char* name, int K, int N, int tpu, int n_stack, bool slot_major,
+                   long long a_slot, long long a_size) {
+    s.name = name;
+    mat_geometry(s.M, wf, K, N, cdiv(N, 16), tpu, window_k);
+    s.wf = wf;
+    s.tpu = tpu;
+    s.n_stack = n_stack;
+    s.n_experts = E;
+    s.n_shared = S;
+    s.max_slots = n_stack;
+    s.slot_major = slot_major;
+    s.a_slot = a_slot;
+    s.a_size = a_size;
+    P.used.push_back(&s);
+  };
+  shape(P.qkv, "qkv", d, (Hq + 2 * Hkv) * D, 1, 1, false, 0, P.a_norm);
+  shape(P.o, "o", Hq * D, d, 1, 1, false, 0, P.a_o);
+  if (!moe) {
+    shape(P.gateup, "gate/up", d, F, 2, 1, false, 0, P.a_norm);
+    shape(P.down, "down", F, d, 1, 1, false, 0, P.a_act_slot);
+  } else {
+    shape(P.router, "router", d, E, 1, 1, false, 0, P.a_norm);
+    shape(P.ex_gateup, "expert gate/up", d, F, 2, n_slots_max, false, 0, P.a_norm);
+    shape(P.ex_down, "expert down", F, d, 1, n_slots_max, true, P.a_act_slot, P.a_act_slot * n_slots_max);
+  }
+  shape(P.lm_head, "lm_head", d, V, 1, 1, false, 0, P.a_norm);
+  for (GemmShape* s : P.used) {
+    int ms = 1, mp = 0;
+    const int lo = s->max_slots > 1 ? std::max(1, S) : 1;
+    for (int ns = lo; ns <= s->max_slots; ++ns) {
+      int a = 0, b = 0;
+      seg_bounds(s->M, ns, s->slot_major, G, a, b);
+      ms = std::max(ms, a);
+      mp = std::max(mp, b);
+    }
+    if (mp > kMaxPending) {
+      err = std::string(s->name) + ": matrix too long for the split-K bookkeeping";
+      return false;
+    }
+    s->M.max_seg = ms;
+    P.ws_floats = std::max(P.ws_floats, (size_t)s->max_slots * s->M.n_sg * ms * kWaves * s->tpu * 256);
+    P.n_tickets = std::max(P.n_tickets, (size_t)s->max_slots * s->M.n_sg);
+  }
+  for (GemmShape* s : P.used)
+    if (!check_gemm_walk(*s, G, P.ws_floats, P.n_tickets, err)) return false;
+  return true;
+}
+
+// ------------------------------------------------------------------ weights
 using TKey = std::tuple<int, int, int, int>;
 
 struct Uploader {
@@ -192,47 +281,39 @@ struct Uploader {
       return nullptr;
     }
     if (it->second->bytes != bytes || it->second->data == nullptr) {
-      h->err = "tensor kind=" + std::to_string(kind) + " layer=" + std::to_string(layer) + " expert=" +
-               std::to_string(expert) + " part=" + std::to_string(part) + " has " +
+      h->err = "tensor kind=" + std::to_string(kind) + " layer=" + std::to_string(layer) + " has " +
                std::to_string(it->second->bytes) + " bytes, expected " + std::to_string(bytes);
       return nullptr;
     }
     return it->second;
   }
 
-  int stage(const void* src, size_t bytes) {
-    hipError_t e = hipMemcpyAsync(staging, src, bytes, hipMemcpyHostToDevice, h->stream);
-    if (e != hipSuccess) return fail(h, SPEC_EHIP, std::string("staging copy: ") + hipGetErrorString(e));
-    return SPEC_OK;
-  }
-
-  // allocate a (possibly stacked) fragment matrix
-  int alloc_mat(Mat& M, int K, int N_tiles, int n_stack) {
-    const int wf = h->wfmt;
-    M.K = K;
-    M.n_tiles = N_tiles;
-    M.nkc = (wf == W_INT4) ? (K / 128) * 4 : cdiv(K, 32);
-    if (wf == W_INT4) {
-      M.w_stride = (long long)N_tiles * (K / 128) * 1024;
-      M.w2_stride = (long long)N_tiles * (K / 128) * 32;
-    } else {
-      M.w_stride = (long long)N_tiles * M.nkc * 1024;
-      M.w2_stride = (wf == W_F32) ? M.w_stride : 0;
-    }
-    int rc = dalloc(h, &M.w, (size_t)M.w_stride * n_stack);
+  // allocate a (possibly stacked) matrix of the planned shape
+  int alloc_mat(HostMat& H, const GemmShape& s) {
+    Mat& M = H.m;
+    M = s.M;
+    H.tpu = s.tpu;
+    H.n_stack = s.n_stack;
+    void* w = nullptr;
+    int rc = dalloc_z(h, reinterpret_cast<char**>(&w), (size_t)M.w_stride * s.n_stack);
     if (rc) return rc;
+    M.w = w;
+    M.w2 = nullptr;
     if (M.w2_stride) {
-      rc = dalloc(h, &M.w2, (size_t)M.w2_stride * n_stack);
+      void* w2 = nullptr;
+      rc = dalloc_z(h, reinterpret_cast<char**>(&w2), (size_t)M.w2_stride * s.n_stack);
       if (rc) return rc;
+      M.w2 = w2;
     }
     return SPEC_OK;
   }
 
-  // upload one host matrix [K][N] into tiles tile_off + t*tile_stride of M (stack slot e)
-  int put(Mat& M, int kind, int layer, int expert, int K, int N, int tile_off, int tile_stride, int e) {
+  // upload host matrix [K][N] into tiles tile_off + t * tile_stride of stack slot e
+  int put(HostMat& H, int kind, int layer, int expert, int K, int N, int tile_off, int tile_stride, int e) {
     const int wf = h->wfmt;
-    char* wdst = static_cast<char*>(M.w) + (long long)e * M.w_stride;
-    char* w2dst = M.w2 ? static_cast<char*>(M.w2) + (long long)e * M.w2_stride : nullptr;
+    Mat& M = H.m;
+    char* wdst = const_cast<char*>(static_cast<const char*>(M.w)) + (long long)e * M.w_stride;
+    char* w2dst = M.w2 ? const_cast<char*>(static_cast<const char*>(M.w2)) + (long long)e * M.w2_stride : nullptr;
     hipError_t he;
     if (wf == W_INT4) {
       const spec_tensor* tq = get(kind, layer, expert, 0, (uint64_t)K / 2 * N);
@@ -240,30 +321,24 @@ struct Uploader {
       if (!tq || !ts) return SPEC_EINVAL;
       const size_t qb = (size_t)K / 2 * N;
       const size_t sb = (size_t)(K / 128) * N * 2;
-      if (stage(tq->data, qb)) return SPEC_EHIP;
       const size_t soff = (qb + 255) / 256 * 256;
-      he = hipMemcpyAsync(static_cast<char*>(staging) + soff, ts->data, sb, hipMemcpyHostToDevice, h->stream);
-      if (he != hipSuccess) return fail(h, SPEC_EHIP, std::string("scale copy: ") + hipGetErrorString(he));
-      he = launch_retile_int4(static_cast<const uint8_t*>(staging),
-                              reinterpret_cast<const uint16_t*>(static_cast<char*>(staging) + soff), K, N, wdst,
-                              w2dst, tile_off, tile_stride, M.n_tiles, h->stream);
-    } else if (wf == W_F32) {
-      const spec_tensor* t = get(kind, layer, expert, 0, (uint64_t)K * N * 4);
-      if (!t) return SPEC_EINVAL;
-      if (stage(t->data, (size_t)K * N * 4)) return SPEC_EHIP;
-      he = launch_retile_f32(static_cast<const float*>(staging), K, N, wdst, w2dst, M.nkc, tile_off, tile_stride,
-                             h->stream);
+      he = hipMemcpyAsync(staging, tq->data, qb, hipMemcpyHostToDevice, h->stream);
+      if (he == hipSuccess)
+        he = hipMemcpyAsync(static_cast<char*>(staging) + soff, ts->data, sb, hipMemcpyHostToDevice, h->stream);
+      if (he == hipSuccess)
+        he = launch_retile(wf, staging, static_cast<char*>(staging) + soff, K, N, wdst, w2dst, M.nkc, H.tpu,
+                           tile_off, tile_stride, h->stream);
     } else {
-      const spec_tensor* t = get(kind, layer, expert, 0, (uint64_t)K * N * 2);
+      const size_t eb = wf == W_F32 ? 4 : 2;
+      const spec_tensor* t = get(kind, layer, expert, 0, (uint64_t)K * N * eb);
       if (!t) return SPEC_EINVAL;
-      if (stage(t->data, (size_t)K * N * 2)) return SPEC_EHIP;
-      he = launch_retile_bf16(static_cast<const uint16_t*>(staging), K, N, wdst, M.nkc, tile_off, tile_stride,
-                              h->stream);
+      he = hipMemcpyAsync(staging, t->data, (size_t)K * N * eb, hipMemcpyHostToDevice, h->stream);
+      if (he == hipSuccess)
+        he = launch_retile(wf, staging, nullptr, K, N, wdst, w2dst, M.nkc, H.tpu, tile_off, tile_stride, h->stream);
     }
-    if (he != hipSuccess) return fail(h, SPEC_EHIP, std::string("retile: ") + hipGetErrorString(he));
-    he = hipStreamSynchronize(h->stream);
-    if (he != hipSuccess) return fail(h, SPEC_EHIP, std::string("retile sync: ") + hipGetErrorString(he));
-    M.alg_bytes += (double)K * N * elem_bytes(h->cfg.weight_dtype) +
+    if (he == hipSuccess) he = hipStreamSynchronize(h->stream);
+    if (he != hipSuccess) return fail(h, SPEC_EHIP, std::string("weight upload: ") + hipGetErrorString(he));
+    H.alg_bytes += (double)K * N * elem_bytes(h->cfg.weight_dtype) +
                    (wf == W_INT4 ? (double)(K / 128) * N * 2 : 0.0);
     return SPEC_OK;
   }
@@ -278,287 +353,6 @@ struct Uploader {
     return SPEC_OK;
   }
 };
-
-// ------------------------------------------------------------------ launches
-
-struct Launcher {
-  spec_verify* h;
-  int rc = SPEC_OK;
-
-  template <typename F>
-  void run(int cls, double bytes, F&& f) {
-    if (rc) return;
-    hipEvent_t a = nullptr, b = nullptr;
-    if (h->profiling) {
-      if (h->ev_used + 2 > h->ev_pool.size()) {
-        for (int i = 0; i < 64; ++i) {
-          hipEvent_t e;
-          if (hipEventCreate(&e) != hipSuccess) {
-            rc = fail(h, SPEC_EHIP, "hipEventCreate failed");
-            return;
-          }
-          h->ev_pool.push_back(e);
-        }
-      }
-      a = h->ev_pool[h->ev_used++];
-      b = h->ev_pool[h->ev_used++];
-      (void)hipEventRecord(a, h->stream);
-    }
-    hipError_t e = f();
-    if (e != hipSuccess) {
-      rc = fail(h, SPEC_EHIP, std::string("kernel launch (class ") + std::to_string(cls) + "): " +
-                                  hipGetErrorString(e));
-      return;
-    }
-    if (h->profiling) {
-      (void)hipEventRecord(b, h->stream);
-      h->prof_pending.push_back(ProfRec{cls, bytes, a, b});
-    }
-  }
-};
-
-GemmParams gemm_base(spec_verify* h, const Mat& M, int m, int N, const float* x, int ldx) {
-  GemmParams p{};
-  p.m = m;
-  p.K = M.K;
-  p.nkc = M.nkc;
-  p.N = N;
-  p.n_tiles = M.n_tiles;
-  int kcs = (h->cfg.gemm_k_split > 0 ? h->cfg.gemm_k_split : 1024) / 32;
-  kcs = std::min(kcs, M.nkc);
-  if (h->wfmt == W_INT4) kcs = std::max(4, (kcs / 4) * 4);
-  p.kcs = kcs;
-  p.splits = cdiv(M.nkc, kcs);
-  p.x = x;
-  p.ldx = ldx;
-  p.w = M.w;
-  p.w2 = M.w2;
-  p.w_stride = M.w_stride;
-  p.w2_stride = M.w2_stride;
-  p.ws = h->ws;
-  p.counters = h->counters;
-  p.eps = h->cfg.rms_eps;
-  p.inv_dnorm = 1.0f / (float)h->cfg.d_model;
-  return p;
-}
-
-size_t gemm_ws_floats(const Mat& M, int kcs_cfg, int wf, int n_slots) {
-  int kcs = std::min(kcs_cfg / 32, M.nkc);
-  if (wf == W_INT4) kcs = std::max(4, (kcs / 4) * 4);
-  const int splits = cdiv(M.nkc, kcs);
-  if (splits <= 1) return 0;
-  return (size_t)n_slots * splits * 16 * M.n_tiles * 16;
-}
-
-int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, const float* q_dev,
-              const float* u_dev, spec_step_result* out, float* logits_dev, float* trace_dev,
-              int32_t* union_dev) {
-  if (!h) return SPEC_EINVAL;
-  if (h->broken) return fail(h, SPEC_ESTATE, "handle unusable after an earlier GPU error");
-  const spec_config& c = h->cfg;
-  if (!tokens || !out) return fail(h, SPEC_EINVAL, "tokens and out must not be NULL");
-  if (k < 0 || k > c.max_k) return fail(h, SPEC_EINVAL, "k out of range [0, max_k]");
-  if (mode < SPEC_ACCEPT_GREEDY || mode > SPEC_ACCEPT_NONE) return fail(h, SPEC_EINVAL, "bad acceptance mode");
-  for (int i = 0; i <= k; ++i)
-    if (tokens[i] < 0 || tokens[i] >= c.vocab) return fail(h, SPEC_EINVAL, "token id out of range");
-  if (mode == SPEC_ACCEPT_STOCHASTIC && (!q_dev || !u_dev))
-    return fail(h, SPEC_EINVAL, "stochastic acceptance needs q_dev and u_dev");
-  const int m = k + 1;
-  const int L = h->kv_len;
-  if ((long long)L + m > c.max_ctx) return fail(h, SPEC_ECAPACITY, "block exceeds max_ctx");
-
-  const int d = c.d_model, Hq = c.n_q_heads, Hkv = c.n_kv_heads, D = c.head_dim, V = c.vocab;
-  const int G = Hq / Hkv;
-  const bool moe = c.n_experts > 0;
-  const double eb = elem_bytes(c.weight_dtype);
-  const double kvb = c.kv_dtype == SPEC_DT_F32 ? 4.0 : 2.0;
-  Launcher ln{h};
-
-  std::memcpy(h->tokens_host, tokens, sizeof(int32_t) * m);
-  hipError_t he = hipMemcpyAsync(h->tokens_dev, h->tokens_host, sizeof(int32_t) * m, hipMemcpyHostToDevice,
-                                 h->stream);
-  if (he != hipSuccess) {
-    h->broken = true;
-    return fail(h, SPEC_EHIP, std::string("token upload: ") + hipGetErrorString(he));
-  }
-  ln.run(SPEC_K_EMBED, (double)m * d * (eb == 4.0 ? 4 : 2) + (double)m * d * 4, [&] {
-    return launch_embed(c.weight_dtype == SPEC_DT_F32, h->embed, h->tokens_dev, m, d, h->x, h->ss, h->stream);
-  });
-  const int n_chunks = cdiv(L + m, kPage);
-  for (int l = 0; l < c.n_layers && !ln.rc; ++l) {
-    LayerW& Lw = h->layers[l];
-    char* kv_layer = static_cast<char*>(h->kv) + (long long)l * h->kv_layer_elems * (long long)kvb;
-    {
-      GemmParams p = gemm_base(h, Lw.qkv, m, (Hq + 2 * Hkv) * D, h->x, h->ldx);
-      p.ss = h->ss;
-      p.n_ss = h->n_ss;
-      p.gain = Lw.attn_norm;
-      p.out = h->qkv;
-      p.ldo = h->ldqkv;
-      ln.run(SPEC_K_QKV, Lw.qkv.alg_bytes + (double)m * d * 4 + (double)m * p.N * 4,
-             [&] { return launch_gemm(h->wfmt, EPI_STORE, p, 1, h->stream); });
-    }
-    {
-      AttnParams a{};
-      a.m = m; a.L = L; a.G = G; a.Hq = Hq; a.Hkv = Hkv; a.D = D;
-      a.n_chunks = n_chunks;
-      a.qkv = h->qkv; a.ldqkv = h->ldqkv;
-      a.rope_cs = h->rope_cs;
-      a.kv = kv_layer;
-      a.page_table = h->page_table;
-      a.pm = h->pm; a.ps = h->ps; a.pacc = h->pacc;
-      a.R = m * G;
-      a.scale = 1.0f / std::sqrt((float)D);
-      const double bytes = (double)L * Hkv * D * 2 * kvb + (double)m * Hkv * D * 2 * kvb +
-                           (double)m * (Hq + 2 * Hkv) * D * 4;
-      ln.run(SPEC_K_ATTN, bytes, [&] { return launch_attention(c.kv_dtype == SPEC_DT_F32, a, h->stream); });
-      CombineParams cp{};
-      cp.m = m; cp.G = G; cp.Hq = Hq; cp.D = D; cp.n_chunks = n_chunks; cp.R = m * G;
-      cp.pm = h->pm; cp.ps = h->ps; cp.pacc = h->pacc;
-      cp.o = h->attn_o; cp.ldo = h->ldo_attn;
-      ln.run(SPEC_K_ATTN_COMBINE, (double)m * Hq * D * 4 * (1 + n_chunks),
-             [&] { return launch_attn_combine(cp, h->stream); });
-    }
-    {
-      GemmParams p = gemm_base(h, Lw.o, m, d, h->attn_o, h->ldo_attn);
-      p.out = h->x;
-      p.ldo = h->ldx;
-      p.ss_out = h->ss;
-      p.n_ss_out = h->n_ss;
-      ln.run(SPEC_K_O, Lw.o.alg_bytes + (double)m * Hq * D * 4 + 2.0 * m * d * 4,
-             [&] { return launch_gemm(h->wfmt, EPI_RESID, p, 1, h->stream); });
-    }
-    if (!moe) {
-      GemmParams p = gemm_base(h, Lw.gateup, m, c.d_ff, h->x, h->ldx);
-      p.ss = h->ss;
-      p.n_ss = h->n_ss;
-      p.gain = Lw.ffn_norm;
-      p.out = h->act;
-      p.ldo = h->ldact;
-      ln.run(SPEC_K_GATEUP, Lw.gateup.alg_bytes + (double)m * d * 4 + (double)m * c.d_ff * 4,
-             [&] { return launch_gemm(h->wfmt, EPI_SWIGLU, p, 1, h->stream); });
-      GemmParams q = gemm_base(h, Lw.down, m, d, h->act, h->ldact);
-      q.out = h->x;
-      q.ldo = h->ldx;
-      q.ss_out = h->ss;
-      q.n_ss_out = h->n_ss;
-      ln.run(SPEC_K_DOWN, Lw.down.alg_bytes + (double)m * c.d_ff * 4 + 2.0 * m * d * 4,
-             [&] { return launch_gemm(h->wfmt, EPI_RESID, q, 1, h->stream); });
-    } else {
-      const int E = c.n_experts, S = c.n_shared, Fe = c.d_ff_expert;
-      GemmParams p = gemm_base(h, Lw.router, m, E, h->x, h->ldx);
-      p.ss = h->ss;
-      p.n_ss = h->n_ss;
-      p.gain = Lw.ffn_norm;
-      p.out = h->rlog;
-      p.ldo = rup(E, 32);
-      ln.run(SPEC_K_ROUTER, Lw.router.alg_bytes + (double)m * d * 4,
-             [&] { return launch_gemm(h->wfmt, EPI_STORE, p, 1, h->stream); });
-      RouteParams rp{};
-      rp.m = m; rp.E = E; rp.top_k = c.top_k;
-      rp.rlogits = h->rlog; rp.ldr = rup(E, 32);
-      rp.bias = Lw.router_bias;
-      rp.union_count = h->ucount; rp.union_list = h->ulist; rp.sel = h->sel; rp.selw = h->selw;
-      rp.slot_of = h->slot_of;
-      rp.union_hist = union_dev ? union_dev + l : nullptr;
-      ln.run(SPEC_K_ROUTE, (double)m * E * 4, [&] { return launch_route(rp, h->stream); });
-      // expert gate/up (+SwiGLU) over the union, then down, per slot
-      GemmParams g = gemm_base(h, Lw.ex_gateup, m, Fe, h->x, h->ldx);
-      g.ss = h->ss;
-      g.n_ss = h->n_ss;
-      g.gain = Lw.ffn_norm;
-      g.out = h->ex_act;
-      g.ldo = h->ld_exact;
-      g.out_stride = h->ex_act_stride;
-      g.union_count = h->ucount; g.union_list = h->ulist; g.n_experts = E; g.n_shared = S;
-      // bytes: accounted per pass from the union size (see spec_pass_bytes)
-      ln.run(SPEC_K_EXPERT_GATEUP, 0.0, [&] { return launch_gemm(h->wfmt, EPI_SWIGLU, g, E + S, h->stream); });
-      GemmParams dn = gemm_base(h, Lw.ex_down, m, d, h->ex_act, h->ld_exact);
-      dn.x_stride = h->ex_act_stride;
-      dn.out = h->ex_y;
-      dn.ldo = h->ldx;
-      dn.out_stride = h->ex_y_stride;
-      dn.union_count = h->ucount; dn.union_list = h->ulist; dn.n_experts = E; dn.n_shared = S;
-      ln.run(SPEC_K_EXPERT_DOWN, 0.0, [&] { return launch_gemm(h->wfmt, EPI_STORE, dn, E + S, h->stream); });
-      MoeCombineParams mc{};
-      mc.m = m; mc.d = d; mc.top_k = c.top_k; mc.n_shared = S; mc.n_ss = h->n_ss;
-      mc.union_count = h->ucount; mc.sel = h->sel; mc.selw = h->selw; mc.slot_of = h->slot_of;
-      mc.y = h->ex_y; mc.y_stride = h->ex_y_stride; mc.ldy = h->ldx;
-      mc.x = h->x; mc.ldx = h->ldx; mc.ss_out = h->ss;
-      ln.run(SPEC_K_MOE_COMBINE, (double)m * d * 4 * (2 + c.top_k + S),
-             [&] { return launch_moe_combine(mc, h->stream); });
-    }
-    if (trace_dev && !ln.rc) {
-      he = hipMemcpy2DAsync(trace_dev + (long long)l * m * d, (size_t)d * 4, h->x, (size_t)h->ldx * 4,
-                            (size_t)d * 4, m, hipMemcpyDeviceToDevice, h->stream);
-      if (he != hipSuccess) ln.rc = fail(h, SPEC_EHIP, std::string("trace copy: ") + hipGetErrorString(he));
-    }
-  }
-  {
-    GemmParams p = gemm_base(h, h->lm_head, m, V, h->x, h->ldx);
-    p.ss = h->ss;
-    p.n_ss = h->n_ss;
-    p.gain = h->final_norm;
-    p.out = h->logits;
-    p.ldo = h->ldl;
-    p.st_max = h->st_max; p.st_sum = h->st_sum; p.st_idx = h->st_idx; p.n_stat = h->n_stat;
-    ln.run(SPEC_K_LMHEAD, h->lm_head.alg_bytes + (double)m * d * 4 + (double)m * V * 4,
-           [&] { return launch_gemm(h->wfmt, EPI_LOGITS, p, 1, h->stream); });
-  }
-  {
-    AcceptParams a{};
-    a.k = k; a.V = V; a.L = L; a.mode = mode; a.n_stat = h->n_stat;
-    a.tokens = h->tokens_dev;
-    a.st_max = h->st_max; a.st_sum = h->st_sum; a.st_idx = h->st_idx;
-    a.logits = h->logits; a.ldl = h->ldl;
-    a.q = q_dev; a.u = u_dev;
-    a.result = h->result_dev;
-    const double bytes = (double)m * h->n_stat * 12 +
-                         (mode == SPEC_ACCEPT_STOCHASTIC ? (double)V * 8 + (double)k * 8 : 0.0);
-    ln.run(SPEC_K_ACCEPT, bytes, [&] { return launch_accept(a, h->stream); });
-  }
-  if (ln.rc) {
-    h->broken = true;
-    return ln.rc;
-  }
-  he = hipMemcpyAsync(h->result_host, h->result_dev, 3 * sizeof(int), hipMemcpyDeviceToHost, h->stream);
-  if (he == hipSuccess && logits_dev)
-    he = hipMemcpy2DAsync(logits_dev, (size_t)V * 4, h->logits, (size_t)h->ldl * 4, (size_t)V * 4, m,
-                          hipMemcpyDeviceToDevice, h->stream);
-  if (he == hipSuccess) he = hipStreamSynchronize(h->stream);
-  if (he != hipSuccess) {
-    h->broken = true;
-    return fail(h, SPEC_EHIP, std::string("step completion: ") + hipGetErrorString(he));
-  }
-  if (h->profiling) {
-    for (auto& r : h->prof_pending) {
-      float ms = 0.f;
-      if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
-        h->prof_launches[r.cls] += 1;
-        h->prof_ms[r.cls] += ms;
-        h->prof_bytes[r.cls] += r.bytes;
-      }
-    }
-    h->prof_pending.clear();
-    h->ev_used = 0;
-  }
-  out->n_accepted = h->result_host[0];
-  out->next_token = h->result_host[1];
-  out->kv_len = h->result_host[2];
-  h->kv_len = out->kv_len;
-  h->err.clear();
-  return SPEC_OK;
-}
-
-void free_all(spec_verify* h) {
-  if (h->stream) (void)hipStreamSynchronize(h->stream);
-  for (void* p : h->allocs) (void)hipFree(p);
-  h->allocs.clear();
-  if (h->tokens_host) (void)hipHostFree(h->tokens_host);
-  if (h->result_host) (void)hipHostFree(h->result_host);
-  for (auto e : h->ev_pool) (void)hipEventDestroy(e);
-  h->ev_pool.clear();
-}
 
 struct Req {
   int kind, layer, expert, part;
@@ -639,14 +433,40 @@ bool check_tensors(const spec_config& c, const spec_tensor* t, int n, std::strin
   return true;
 }
 
+Phase gemm_phase_desc(int kind, int layer, const HostMat& H) {
+  Phase p{};
+  p.kind = kind;
+  p.layer = layer;
+  p.M = H.m;
+  return p;
+}
+
 int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, const void* prompt_k,
                 const void* prompt_v, int32_t prompt_len) {
   const spec_config& c = h->cfg;
   const int d = c.d_model, Hq = c.n_q_heads, Hkv = c.n_kv_heads, D = c.head_dim, V = c.vocab;
   const bool moe = c.n_experts > 0;
+  const int E = c.n_experts, S = c.n_shared;
+  const int F = moe ? c.d_ff_expert : c.d_ff;
   h->wfmt = c.weight_dtype == SPEC_DT_F32 ? W_F32 : c.weight_dtype == SPEC_DT_BF16 ? W_BF16 : W_INT4;
   int rc;
   HIPCHK(hipGetDevice(&h->device));
+  HIPCHK(hipDeviceGetAttribute(&h->n_wg, hipDeviceAttributeMultiprocessorCount, h->device));
+  int coop = 0;
+  HIPCHK(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, h->device));
+  if (!coop) return fail(h, SPEC_EHIP, "device does not support cooperative launches");
+  int wclk = 0;
+  HIPCHK(hipDeviceGetAttribute(&wclk, hipDeviceAttributeWallClockRate, h->device));
+  h->wall_khz = wclk > 0 ? (double)wclk : 100000.0;
+  h->lds = pass_lds_bytes(h->wfmt, max_rows_attn(&c), D);
+  int per_cu = 0;
+  HIPCHK(pass_occupancy(h->wfmt, h->lds, &per_cu));
+  if (per_cu < 1) return fail(h, SPEC_EHIP, "the pass kernel does not fit on a compute unit");
+  PassPlan plan;
+  {
+    std::string err;
+    if (!build_plan(c, h->wfmt, h->n_wg, plan, err)) return fail(h, SPEC_EINVAL, "stream-K plan: " + err);
+  }
 
   Uploader up{h};
   size_t max_bytes = 0;
@@ -657,14 +477,12 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
     up.idx[key] = &t;
     max_bytes = std::max<size_t>(max_bytes, t.bytes);
   }
-  // int4 matrices stage packed nibbles and scales together
-  max_bytes = max_bytes * 2 + 256;
+  max_bytes = max_bytes * 2 + 256;   // int4: nibbles and scales staged together
   const size_t kv_elem = c.kv_dtype == SPEC_DT_F32 ? 4 : 2;
   max_bytes = std::max(max_bytes, (size_t)2 * Hkv * std::max(prompt_len, 1) * D * kv_elem);
   if ((rc = dalloc(h, &up.staging, max_bytes))) return rc;
   up.staging_bytes = max_bytes;
 
-  // embedding
   {
     const size_t eb = c.weight_dtype == SPEC_DT_F32 ? 4 : 2;
     const spec_tensor* t = up.get(SPEC_T_EMBED, -1, -1, 0, (uint64_t)V * d * eb);
@@ -674,49 +492,47 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   }
   if ((rc = up.put_vec(&h->final_norm, SPEC_T_FINAL_NORM, -1, d))) return rc;
   h->layers.resize(c.n_layers);
-  const int qkv_tiles = (Hq + 2 * Hkv) * D / 16;
   for (int l = 0; l < c.n_layers; ++l) {
-    LayerW& Lw = h->layers[l];
+    HostLayer& Lw = h->layers[l];
     if ((rc = up.put_vec(&Lw.attn_norm, SPEC_T_ATTN_NORM, l, d))) return rc;
     if ((rc = up.put_vec(&Lw.ffn_norm, SPEC_T_FFN_NORM, l, d))) return rc;
-    if ((rc = up.alloc_mat(Lw.qkv, d, qkv_tiles, 1))) return rc;
+    if ((rc = up.alloc_mat(Lw.qkv, plan.qkv))) return rc;
     if ((rc = up.put(Lw.qkv, SPEC_T_WQ, l, -1, d, Hq * D, 0, 1, 0))) return rc;
     if ((rc = up.put(Lw.qkv, SPEC_T_WK, l, -1, d, Hkv * D, Hq * D / 16, 1, 0))) return rc;
     if ((rc = up.put(Lw.qkv, SPEC_T_WV, l, -1, d, Hkv * D, (Hq + Hkv) * D / 16, 1, 0))) return rc;
-    if ((rc = up.alloc_mat(Lw.o, Hq * D, cdiv(d, 16), 1))) return rc;
+    if ((rc = up.alloc_mat(Lw.o, plan.o))) return rc;
     if ((rc = up.put(Lw.o, SPEC_T_WO, l, -1, Hq * D, d, 0, 1, 0))) return rc;
     if (!moe) {
-      const int F = c.d_ff;
-      if ((rc = up.alloc_mat(Lw.gateup, d, 2 * cdiv(F, 16), 1))) return rc;
+      if ((rc = up.alloc_mat(Lw.gateup, plan.gateup))) return rc;
       if ((rc = up.put(Lw.gateup, SPEC_T_W_GATE, l, -1, d, F, 0, 2, 0))) return rc;
       if ((rc = up.put(Lw.gateup, SPEC_T_W_UP, l, -1, d, F, 1, 2, 0))) return rc;
-      if ((rc = up.alloc_mat(Lw.down, F, cdiv(d, 16), 1))) return rc;
+      if ((rc = up.alloc_mat(Lw.down, plan.down))) return rc;
       if ((rc = up.put(Lw.down, SPEC_T_W_DOWN, l, -1, F, d, 0, 1, 0))) return rc;
     } else {
-      const int E = c.n_experts, S = c.n_shared, F = c.d_ff_expert;
-      if ((rc = up.alloc_mat(Lw.router, d, cdiv(E, 16), 1))) return rc;
+      if ((rc = up.alloc_mat(Lw.router, plan.router))) return rc;
       if ((rc = up.put(Lw.router, SPEC_T_ROUTER, l, -1, d, E, 0, 1, 0))) return rc;
       if ((rc = up.put_vec(&Lw.router_bias, SPEC_T_ROUTER_BIAS, l, E))) return rc;
-      if ((rc = up.alloc_mat(Lw.ex_gateup, d, 2 * cdiv(F, 16), E + S))) return rc;
-      if ((rc = up.alloc_mat(Lw.ex_down, F, cdiv(d, 16), E + S))) return rc;
+      if ((rc = up.alloc_mat(Lw.ex_gateup, plan.ex_gateup))) return rc;
+      if ((rc = up.alloc_mat(Lw.ex_down, plan.ex_down))) return rc;
       for (int e = 0; e < E + S; ++e) {
         if ((rc = up.put(Lw.ex_gateup, SPEC_T_W_GATE, l, e, d, F, 0, 2, e))) return rc;
         if ((rc = up.put(Lw.ex_gateup, SPEC_T_W_UP, l, e, d, F, 1, 2, e))) return rc;
         if ((rc = up.put(Lw.ex_down, SPEC_T_W_DOWN, l, e, F, d, 0, 1, e))) return rc;
       }
-      // per-expert logical bytes (the stack accumulated E+S experts)
       Lw.ex_gateup.alg_bytes /= (E + S);
       Lw.ex_down.alg_bytes /= (E + S);
     }
   }
-  if ((rc = up.alloc_mat(h->lm_head, d, cdiv(V, 16), 1))) return rc;
+  if ((rc = up.alloc_mat(h->lm_head, plan.lm_head))) return rc;
   if ((rc = up.put(h->lm_head, SPEC_T_LM_HEAD, -1, -1, d, V, 0, 1, 0))) return rc;
 
   // KV cache pages + identity page table
   h->n_pages = cdiv(c.max_ctx, kPage);
   h->kv_layer_elems = (long long)h->n_pages * Hkv * 2 * kPage * D;
-  if ((rc = dalloc(h, &h->kv, (size_t)h->kv_layer_elems * c.n_layers * kv_elem))) return rc;
-  HIPCHK(hipMemsetAsync(h->kv, 0, (size_t)h->kv_layer_elems * c.n_layers * kv_elem, h->stream));
+  if ((rc = dalloc_z(h, reinterpret_cast<char**>(&h->kv), (size_t)h->kv_layer_elems * c.n_layers * kv_elem)))
+    return rc;
+  for (int l = 0; l < c.n_layers; ++l)
+    h->layers[l].kv = static_cast<char*>(h->kv) + (long long)l * h->kv_layer_elems * (long long)kv_elem;
   {
     std::vector<int> pt(h->n_pages);
     for (int i = 0; i < h->n_pages; ++i) pt[i] = i;
@@ -730,9 +546,8 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
                             h->stream));
       HIPCHK(hipMemcpyAsync(static_cast<char*>(up.staging) + lb, static_cast<const char*>(prompt_v) + l * lb, lb,
                             hipMemcpyHostToDevice, h->stream));
-      char* base = static_cast<char*>(h->kv) + (long long)l * h->kv_layer_elems * (long long)kv_elem;
-      HIPCHK(launch_kv_import(c.kv_dtype == SPEC_DT_F32, up.staging, prompt_len, Hkv, D, base, h->page_table,
-                              h->stream));
+      HIPCHK(launch_kv_import(c.kv_dtype == SPEC_DT_F32, up.staging, prompt_len, Hkv, D, h->layers[l].kv,
+                              h->page_table, h->stream));
       HIPCHK(hipStreamSynchronize(h->stream));
     }
   }
@@ -750,70 +565,117 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
     if ((rc = dalloc_t(h, &h->rope_cs, cs.size()))) return rc;
     HIPCHK(hipMemcpy(h->rope_cs, cs.data(), cs.size() * 4, hipMemcpyHostToDevice));
   }
-  // activations and scratch
+  // activations and scratch (zero-filled)
   h->ldx = rup(d, 32);
   h->ldqkv = rup((Hq + 2 * Hkv) * D, 32);
-  h->ldo_attn = rup(Hq * D, 32);
-  h->ldact = rup(moe ? 32 : c.d_ff, 32);
   h->ldl = rup(V, 32);
-  h->n_ss = cdiv(d, 64);
-  h->n_stat = cdiv(cdiv(V, 16), 4);
-  if ((rc = dalloc_t(h, &h->x, 16 * h->ldx))) return rc;
-  if ((rc = dalloc_t(h, &h->qkv, 16 * h->ldqkv))) return rc;
-  if ((rc = dalloc_t(h, &h->attn_o, 16 * h->ldo_attn))) return rc;
-  if ((rc = dalloc_t(h, &h->act, 16 * h->ldact))) return rc;
-  if ((rc = dalloc_t(h, &h->ss, 16 * h->n_ss))) return rc;
-  if ((rc = dalloc_t(h, &h->logits, 16 * (size_t)h->ldl))) return rc;
-  if ((rc = dalloc_t(h, &h->st_max, 16 * h->n_stat))) return rc;
-  if ((rc = dalloc_t(h, &h->st_sum, 16 * h->n_stat))) return rc;
-  if ((rc = dalloc_t(h, &h->st_idx, 16 * h->n_stat))) return rc;
-  const int G = Hq / Hkv;
-  const size_t Rmax = (size_t)(c.max_k + 1) * G;
-  const size_t max_chunks = cdiv(c.max_ctx, kPage);
-  if ((rc = dalloc_t(h, &h->pm, Hkv * max_chunks * Rmax))) return rc;
-  if ((rc = dalloc_t(h, &h->ps, Hkv * max_chunks * Rmax))) return rc;
-  if ((rc = dalloc_t(h, &h->pacc, Hkv * max_chunks * Rmax * D))) return rc;
-  // split-K scratch and tickets
-  const int ksplit = c.gemm_k_split > 0 ? c.gemm_k_split : 1024;
-  size_t ws = 0, ctr = 0;
-  auto acc_mat = [&](const Mat& M, int n_slots) {
-    ws = std::max(ws, gemm_ws_floats(M, ksplit, h->wfmt, n_slots));
-    ctr = std::max(ctr, (size_t)n_slots * cdiv(M.n_tiles, 4));
-  };
-  for (auto& Lw : h->layers) {
-    acc_mat(Lw.qkv, 1);
-    acc_mat(Lw.o, 1);
-    if (!moe) {
-      acc_mat(Lw.gateup, 1);
-      acc_mat(Lw.down, 1);
-    } else {
-      acc_mat(Lw.router, 1);
-      acc_mat(Lw.ex_gateup, c.n_experts + c.n_shared);
-      acc_mat(Lw.ex_down, c.n_experts + c.n_shared);
-    }
+  h->n_ss = cdiv(d, 16);
+  h->n_stat = cdiv(V, 16);
+  h->ldr = rup(std::max(E, 1), 32);
+  const int n_slots_max = moe ? E + S : 1;
+  if ((rc = dalloc_z(h, &h->x, 16 * (size_t)h->ldx))) return rc;
+  if ((rc = dalloc_z(h, &h->qkv, 16 * (size_t)h->ldqkv))) return rc;
+  if ((rc = dalloc_z(h, &h->ss, 16 * (size_t)h->n_ss))) return rc;
+  if ((rc = dalloc_z(h, &h->logits, 16 * (size_t)h->ldl))) return rc;
+  if ((rc = dalloc_z(h, &h->a_norm, (size_t)plan.a_norm))) return rc;
+  if ((rc = dalloc_z(h, &h->a_o, (size_t)plan.a_o))) return rc;
+  h->a_act_slot = plan.a_act_slot;
+  if ((rc = dalloc_z(h, &h->a_act, (size_t)h->a_act_slot * n_slots_max))) return rc;
+  if ((rc = dalloc_z(h, &h->st_max, 16 * (size_t)h->n_stat))) return rc;
+  if ((rc = dalloc_z(h, &h->st_sum, 16 * (size_t)h->n_stat))) return rc;
+  if ((rc = dalloc_z(h, &h->st_idx, 16 * (size_t)h->n_stat))) return rc;
+  const size_t Rmax = (size_t)max_rows_attn(&c);
+  const size_t max_groups = cdiv(c.max_ctx, kGroupPos);
+  if ((rc = dalloc_z(h, &h->pm, Hkv * max_groups * Rmax))) return rc;
+  if ((rc = dalloc_z(h, &h->ps, Hkv * max_groups * Rmax))) return rc;
+  if ((rc = dalloc_z(h, &h->pacc, Hkv * max_groups * Rmax * D))) return rc;
+  if ((rc = dalloc_z(h, &h->ws, plan.ws_floats))) return rc;
+  if ((rc = dalloc_z(h, &h->tickets, plan.n_tickets))) return rc;
+  if ((rc = dalloc_z(h, &h->bar, 512))) return rc;
+  if ((rc = dalloc_z(h, &h->tokens_dev, 16))) return rc;
+  if ((rc = dalloc_z(h, &h->result_dev, 4))) return rc;
+  if (moe) {
+    if ((rc = dalloc_z(h, &h->rlog, 16 * (size_t)h->ldr))) return rc;
+    h->ey_slot = 16LL * h->ldx;
+    if ((rc = dalloc_z(h, &h->ey, (size_t)h->ey_slot * n_slots_max))) return rc;
+    if ((rc = dalloc_z(h, &h->route, (size_t)route_words(E, c.top_k)))) return rc;
   }
-  acc_mat(h->lm_head, 1);
-  if ((rc = dalloc_t(h, &h->ws, std::max<size_t>(ws, 16)))) return rc;
-  if ((rc = dalloc_t(h, &h->counters, std::max<size_t>(ctr, 16)))) return rc;
-  HIPCHK(hipMemsetAsync(h->counters, 0, std::max<size_t>(ctr, 16) * sizeof(unsigned), h->stream));
-  if ((rc = dalloc_t(h, &h->tokens_dev, 16))) return rc;
-  if ((rc = dalloc_t(h, &h->result_dev, 4))) return rc;
   HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->tokens_host), 16 * sizeof(int), hipHostMallocDefault));
   HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->result_host), 4 * sizeof(int), hipHostMallocDefault));
-  if (moe) {
-    const int E = c.n_experts, S = c.n_shared, F = c.d_ff_expert;
-    if ((rc = dalloc_t(h, &h->rlog, 16 * rup(E, 32)))) return rc;
-    if ((rc = dalloc_t(h, &h->ucount, 4))) return rc;
-    if ((rc = dalloc_t(h, &h->ulist, E + 4))) return rc;
-    if ((rc = dalloc_t(h, &h->sel, 16 * c.top_k))) return rc;
-    if ((rc = dalloc_t(h, &h->selw, 16 * c.top_k))) return rc;
-    if ((rc = dalloc_t(h, &h->slot_of, E + 4))) return rc;
-    h->ld_exact = rup(F, 32);
-    h->ex_act_stride = 16LL * h->ld_exact;
-    h->ex_y_stride = 16LL * h->ldx;
-    if ((rc = dalloc_t(h, &h->ex_act, (size_t)(E + S) * h->ex_act_stride))) return rc;
-    if ((rc = dalloc_t(h, &h->ex_y, (size_t)(E + S) * h->ex_y_stride))) return rc;
+
+  // ---- the pass program
+  std::vector<Phase> prog;
+  std::vector<int> cls;
+  std::vector<double> wbytes;
+  auto add = [&](const Phase& p, int k, double b) {
+    prog.push_back(p);
+    cls.push_back(k);
+    wbytes.push_back(b);
+  };
+  {
+    Phase p{};
+    p.kind = PH_EMBED;
+    add(p, SPEC_K_EMBED, 0);
   }
+  for (int l = 0; l < c.n_layers; ++l) {
+    HostLayer& Lw = h->layers[l];
+    const float* next_gain = l + 1 < c.n_layers ? h->layers[l + 1].attn_norm : h->final_norm;
+    Phase q = gemm_phase_desc(PH_STORE, l, Lw.qkv);
+    q.a = h->a_norm; q.out = h->qkv; q.ldo = h->ldqkv; q.scale = 1;
+    add(q, SPEC_K_QKV, Lw.qkv.alg_bytes);
+    Phase at{};
+    at.kind = PH_ATTN; at.layer = l; at.kv = Lw.kv;
+    add(at, SPEC_K_ATTN, 0);
+    Phase mg{};
+    mg.kind = PH_ATTN_MERGE; mg.layer = l;
+    add(mg, SPEC_K_ATTN_COMBINE, 0);
+    Phase o = gemm_phase_desc(PH_RESID, l, Lw.o);
+    o.a = h->a_o; o.gain = Lw.ffn_norm; o.a_out = h->a_norm;
+    add(o, SPEC_K_O, Lw.o.alg_bytes);
+    if (!moe) {
+      Phase g = gemm_phase_desc(PH_SWIGLU, l, Lw.gateup);
+      g.a = h->a_norm; g.a_out = h->a_act;
+      add(g, SPEC_K_GATEUP, Lw.gateup.alg_bytes);
+      Phase dn = gemm_phase_desc(PH_RESID, l, Lw.down);
+      dn.a = h->a_act; dn.gain = next_gain; dn.a_out = h->a_norm; dn.trace = 1;
+      add(dn, SPEC_K_DOWN, Lw.down.alg_bytes);
+    } else {
+      Phase r = gemm_phase_desc(PH_STORE, l, Lw.router);
+      r.a = h->a_norm; r.out = h->rlog; r.ldo = h->ldr; r.scale = 1;
+      add(r, SPEC_K_ROUTER, Lw.router.alg_bytes);
+      Phase g = gemm_phase_desc(PH_ROUTE_SWIGLU, l, Lw.ex_gateup);
+      g.slot_mode = 1; g.a = h->a_norm; g.a_out = h->a_act; g.a_out_slot = h->a_act_slot; g.bias = Lw.router_bias;
+      add(g, SPEC_K_EXPERT_GATEUP, Lw.ex_gateup.alg_bytes);
+      Phase dn = gemm_phase_desc(PH_STORE, l, Lw.ex_down);
+      dn.slot_mode = 2; dn.a = h->a_act; dn.a_slot = h->a_act_slot; dn.out = h->ey; dn.ldo = h->ldx;
+      dn.out_slot = h->ey_slot; dn.scale = 0;
+      add(dn, SPEC_K_EXPERT_DOWN, Lw.ex_down.alg_bytes);
+      Phase cb{};
+      cb.kind = PH_COMBINE; cb.layer = l; cb.gain = next_gain; cb.trace = 1;
+      add(cb, SPEC_K_MOE_COMBINE, 0);
+    }
+  }
+  {
+    Phase lm = gemm_phase_desc(PH_LOGITS, -1, h->lm_head);
+    lm.a = h->a_norm; lm.out = h->logits; lm.ldo = h->ldl;
+    add(lm, SPEC_K_LMHEAD, h->lm_head.alg_bytes);
+  }
+  h->n_prog = (int)prog.size();
+  for (int i = h->n_prog - 1, nx = h->n_prog; i >= 0; --i) {
+    prog[i].next_gemm = nx;
+    const int kd = prog[i].kind;
+    if (kd == PH_STORE || kd == PH_RESID || kd == PH_SWIGLU || kd == PH_LOGITS || kd == PH_ROUTE_SWIGLU) nx = i;
+  }
+  h->prog_layer.clear();
+  for (const Phase& q : prog) h->prog_layer.push_back(q.layer);
+  h->prog_cls = cls;
+  h->prog_bytes_fixed = wbytes;
+  if ((rc = dalloc_t(h, &h->prog, prog.size()))) return rc;
+  HIPCHK(hipMemcpy(h->prog, prog.data(), prog.size() * sizeof(Phase), hipMemcpyHostToDevice));
+  if ((rc = dalloc_z(h, &h->stamps_dev, (size_t)h->n_prog + 4))) return rc;
+  h->stamps_host.assign((size_t)h->n_prog + 4, 0);
+  for (auto& e : h->ev) HIPCHK(hipEventCreate(&e));
+
   // the staging buffer is no longer needed
   HIPCHK(hipStreamSynchronize(h->stream));
   auto it = std::find(h->allocs.begin(), h->allocs.end(), up.staging);
@@ -821,6 +683,173 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
     (void)hipFree(up.staging);
     h->allocs.erase(it);
   }
+  return SPEC_OK;
+}
+
+void free_all(spec_verify* h) {
+  if (h->stream) (void)hipStreamSynchronize(h->stream);
+  for (void* p : h->allocs) (void)hipFree(p);
+  h->allocs.clear();
+  if (h->tokens_host) (void)hipHostFree(h->tokens_host);
+  if (h->result_host) (void)hipHostFree(h->result_host);
+  for (auto& e : h->ev)
+    if (e) (void)hipEventDestroy(e);
+}
+
+// algorithmic bytes of one phase of the program (profiling)
+double phase_bytes(const spec_verify* h, int i, int m, int L, int experts_loaded_layer) {
+  const spec_config& c = h->cfg;
+  const double kvb = c.kv_dtype == SPEC_DT_F32 ? 4.0 : 2.0;
+  const int d = c.d_model, Hq = c.n_q_heads, Hkv = c.n_kv_heads, D = c.head_dim;
+  const double w = h->prog_bytes_fixed[i];
+  switch (h->prog_cls[i]) {
+    case SPEC_K_EMBED: return (double)m * d * (c.weight_dtype == SPEC_DT_F32 ? 4 : 2) + (double)m * d * 4;
+    case SPEC_K_QKV: return w + (double)m * d * 4 + (double)m * (Hq + 2 * Hkv) * D * 4;
+    case SPEC_K_ATTN:
+      return (double)L * Hkv * D * 2 * kvb + (double)m * Hkv * D * 2 * kvb + (double)m * (Hq + 2 * Hkv) * D * 4;
+    case SPEC_K_O: return w + (double)m * Hq * D * 4 + 2.0 * m * d * 4;
+    case SPEC_K_GATEUP: return w + (double)m * d * 4 + (double)m * c.d_ff * 4;
+    case SPEC_K_DOWN: return w + (double)m * c.d_ff * 4 + 2.0 * m * d * 4;
+    case SPEC_K_ROUTER: return w + (double)m * d * 4;
+    case SPEC_K_EXPERT_GATEUP: return w * (experts_loaded_layer + c.n_shared);
+    case SPEC_K_EXPERT_DOWN: return w * (experts_loaded_layer + c.n_shared);
+    case SPEC_K_MOE_COMBINE: return (double)m * d * 4 * (2 + c.top_k + c.n_shared);
+    case SPEC_K_LMHEAD: return w + (double)m * d * 4 + (double)m * c.vocab * 4;
+    default: return 0;
+  }
+}
+
+int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, const float* q_dev,
+              const float* u_dev, spec_step_result* out, float* logits_dev, float* trace_dev,
+              int32_t* union_dev) {
+  if (!h) return SPEC_EINVAL;
+  if (h->broken) return fail(h, SPEC_ESTATE, "handle unusable after an earlier GPU error");
+  const spec_config& c = h->cfg;
+  if (!tokens || !out) return fail(h, SPEC_EINVAL, "tokens and out must not be NULL");
+  if (k < 0 || k > c.max_k) return fail(h, SPEC_EINVAL, "k out of range [0, max_k]");
+  if (mode < SPEC_ACCEPT_GREEDY || mode > SPEC_ACCEPT_NONE) return fail(h, SPEC_EINVAL, "bad acceptance mode");
+  for (int i = 0; i <= k; ++i)
+    if (tokens[i] < 0 || tokens[i] >= c.vocab) return fail(h, SPEC_EINVAL, "token id out of range");
+  if (mode == SPEC_ACCEPT_STOCHASTIC && (!q_dev || !u_dev))
+    return fail(h, SPEC_EINVAL, "stochastic acceptance needs q_dev and u_dev");
+  const int m = k + 1;
+  const int L = h->kv_len;
+  if ((long long)L + m > c.max_ctx) return fail(h, SPEC_ECAPACITY, "block exceeds max_ctx");
+  const bool moe = c.n_experts > 0;
+  int* union_rec = union_dev;
+  if (!union_rec && h->profiling && moe) {
+    if (!h->union_dev_prof) {
+      void* p = nullptr;
+      if (hipMalloc(&p, sizeof(int) * c.n_layers) != hipSuccess) return fail(h, SPEC_ENOMEM, "profiling buffer");
+      h->allocs.push_back(p);
+      h->union_dev_prof = static_cast<int*>(p);
+    }
+    union_rec = h->union_dev_prof;
+  }
+
+  std::memcpy(h->tokens_host, tokens, sizeof(int32_t) * m);
+  hipError_t he = hipMemcpyAsync(h->tokens_dev, h->tokens_host, sizeof(int32_t) * m, hipMemcpyHostToDevice,
+                                 h->stream);
+  PassP p{};
+  p.m = m; p.L = L; p.n_layers = c.n_layers; p.d = c.d_model; p.Hq = c.n_q_heads; p.Hkv = c.n_kv_heads;
+  p.D = c.head_dim; p.V = c.vocab; p.G = c.n_q_heads / c.n_kv_heads; p.E = c.n_experts; p.top_k = c.top_k;
+  p.n_shared = c.n_shared; p.F = moe ? c.d_ff_expert : c.d_ff;
+  p.n_groups = cdiv(L + m, kGroupPos);
+  p.n_ss = h->n_ss;
+  p.lds_bytes = (int)h->lds;
+  p.eps = c.rms_eps;
+  p.inv_d = 1.0f / (float)c.d_model;
+  p.attn_scale = 1.0f / std::sqrt((float)c.head_dim);
+  p.prog = h->prog; p.n_prog = h->n_prog;
+  p.embed = h->embed; p.gain0 = h->layers[0].attn_norm;
+  p.tokens = h->tokens_dev; p.page_table = h->page_table; p.rope_cs = h->rope_cs;
+  p.x = h->x; p.ldx = h->ldx; p.ss = h->ss;
+  p.a_norm = h->a_norm; p.a_o = h->a_o; p.a_act = h->a_act; p.a_act_slot = h->a_act_slot;
+  p.qkv = h->qkv; p.ldqkv = h->ldqkv; p.logits = h->logits; p.ldl = h->ldl;
+  p.st_max = h->st_max; p.st_sum = h->st_sum; p.st_idx = h->st_idx; p.n_stat = h->n_stat;
+  p.pm = h->pm; p.ps = h->ps; p.pacc = h->pacc;
+  p.rlog = h->rlog; p.ldr = h->ldr; p.ey = h->ey; p.ey_slot = h->ey_slot; p.ldy = h->ldx;
+  p.route = h->route;
+  p.ws = h->ws; p.tickets = h->tickets;
+  p.bar = h->bar; p.bar_base = h->bar_gen; p.err = h->result_dev + 3;
+  p.trace = trace_dev; p.union_hist = union_rec;
+  p.stamps = h->profiling ? h->stamps_dev : nullptr;
+
+  if (he == hipSuccess && h->profiling) he = hipEventRecord(h->ev[0], h->stream);
+  if (he == hipSuccess) he = launch_pass(h->wfmt, p, h->n_wg, h->lds, h->stream);
+  if (he != hipSuccess) {
+    h->broken = true;
+    return fail(h, SPEC_EHIP, std::string("pass launch: ") + hipGetErrorString(he));
+  }
+  h->bar_gen += (unsigned long long)(h->n_prog - 1);
+  if (h->profiling) he = hipEventRecord(h->ev[1], h->stream);
+  AcceptParams a{};
+  a.k = k; a.V = c.vocab; a.L = L; a.mode = mode; a.n_stat = h->n_stat;
+  a.tokens = h->tokens_dev;
+  a.st_max = h->st_max; a.st_sum = h->st_sum; a.st_idx = h->st_idx;
+  a.logits = h->logits; a.ldl = h->ldl;
+  a.q = q_dev; a.u = u_dev;
+  a.result = h->result_dev;
+  if (he == hipSuccess) he = launch_accept(a, h->stream);
+  if (he == hipSuccess && h->profiling) he = hipEventRecord(h->ev[2], h->stream);
+  if (he == hipSuccess)
+    he = hipMemcpyAsync(h->result_host, h->result_dev, 4 * sizeof(int), hipMemcpyDeviceToHost, h->stream);
+  if (he == hipSuccess && logits_dev)
+    he = hipMemcpy2DAsync(logits_dev, (size_t)c.vocab * 4, h->logits, (size_t)h->ldl * 4, (size_t)c.vocab * 4, m,
+                          hipMemcpyDeviceToDevice, h->stream);
+  if (he == hipSuccess && h->profiling)
+    he = hipMemcpyAsync(h->stamps_host.data(), h->stamps_dev, sizeof(unsigned long long) * h->n_prog,
+                        hipMemcpyDeviceToHost, h->stream);
+  std::vector<int> uh;
+  if (he == hipSuccess && h->profiling && moe) {
+    uh.resize(c.n_layers);
+    he = hipMemcpyAsync(uh.data(), union_rec, sizeof(int) * c.n_layers, hipMemcpyDeviceToHost, h->stream);
+  }
+  if (he == hipSuccess) he = hipStreamSynchronize(h->stream);
+  if (he != hipSuccess) {
+    h->broken = true;
+    return fail(h, SPEC_EHIP, std::string("step completion: ") + hipGetErrorString(he));
+  }
+  if (h->result_host[3] != 0) {
+    h->broken = true;
+    return fail(h, SPEC_EHIP, "grid barrier wait timed out inside the pass");
+  }
+  if (h->profiling) {
+    float pass_ms = 0.f, acc_ms = 0.f;
+    (void)hipEventElapsedTime(&pass_ms, h->ev[0], h->ev[1]);
+    (void)hipEventElapsedTime(&acc_ms, h->ev[1], h->ev[2]);
+    double total_bytes = 0;
+    const double tick_ms = 1.0 / h->wall_khz;
+    double stamped = 0;
+    for (int i = 0; i < h->n_prog; ++i) {
+      double ms;
+      if (i + 1 < h->n_prog) {
+        ms = (double)(h->stamps_host[i + 1] - h->stamps_host[i]) * tick_ms;
+        stamped += ms;
+      } else {
+        ms = std::max(0.0, (double)pass_ms - stamped);
+      }
+      const int layer = std::max(0, h->prog_layer[i]);
+      const double b = phase_bytes(h, i, m, L, moe ? uh[layer] : 0);
+      const int k2 = h->prog_cls[i];
+      h->prof_launches[k2] += 1;
+      h->prof_ms[k2] += ms;
+      h->prof_bytes[k2] += b;
+      total_bytes += b;
+    }
+    h->prof_launches[SPEC_K_PASS] += 1;
+    h->prof_ms[SPEC_K_PASS] += pass_ms;
+    h->prof_bytes[SPEC_K_PASS] += total_bytes;
+    h->prof_launches[SPEC_K_ACCEPT] += 1;
+    h->prof_ms[SPEC_K_ACCEPT] += acc_ms;
+    h->prof_bytes[SPEC_K_ACCEPT] +=
+        (double)m * h->n_stat * 12 + (mode == SPEC_ACCEPT_STOCHASTIC ? (double)c.vocab * 8 + (double)k * 8 : 0.0);
+  }
+  out->n_accepted = h->result_host[0];
+  out->next_token = h->result_host[1];
+  out->kv_len = h->result_host[2];
+  h->kv_len = out->kv_len;
+  h->err.clear();
   return SPEC_OK;
 }
 
@@ -833,9 +862,21 @@ extern "C" {
 int spec_config_check(const spec_config* cfg, char* msg, int32_t msg_len) {
   std::string m;
   const bool ok = check_cfg(cfg, m);
-  if (msg && msg_len > 0) {
-    std::snprintf(msg, (size_t)msg_len, "%s", ok ? "" : m.c_str());
+  if (msg && msg_len > 0) std::snprintf(msg, (size_t)msg_len, "%s", ok ? "" : m.c_str());
+  return ok ? SPEC_OK : SPEC_EINVAL;
+}
+
+int spec_plan_check(const spec_config* cfg, int32_t n_wg, char* msg, int32_t msg_len) {
+  std::string m;
+  bool ok = n_wg >= 1 && n_wg <= 4096;
+  if (!ok) m = "n_wg must be in [1, 4096]";
+  if (ok) ok = check_cfg(cfg, m);
+  if (ok) {
+    PassPlan plan;
+    const int wf = cfg->weight_dtype == SPEC_DT_F32 ? W_F32 : cfg->weight_dtype == SPEC_DT_BF16 ? W_BF16 : W_INT4;
+    ok = build_plan(*cfg, wf, n_wg, plan, m);
   }
+  if (msg && msg_len > 0) std::snprintf(msg, (size_t)msg_len, "%s", ok ? "" : m.c_str());
   return ok ? SPEC_OK : SPEC_EINVAL;
 }
 
@@ -907,8 +948,6 @@ int spec_profile_enable(spec_verify_t* h, int32_t on) {
     h->prof_ms[i] = 0;
     h->prof_bytes[i] = 0;
   }
-  h->prof_pending.clear();
-  h->ev_used = 0;
   return SPEC_OK;
 }
 

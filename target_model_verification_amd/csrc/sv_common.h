@@ -1,4 +1,4 @@
-// Shared declarations of the HIP kernels' parameter blocks and launchers.
+// Shared declarations of the HIP device code and the host runtime.
 // Device code targets gfx950 (CDNA4, wave64) only.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -7,68 +7,115 @@
 
 namespace sv {
 
-// ---------------------------------------------------------------- tiling
-// A weight "fragment" is the B operand of one v_mfma_f32_16x16x32_bf16:
-// 16 output columns x 32 k.  Lane l holds 8 consecutive k of column l%16:
-// k = 8*(l/16) + e, e = 0..7 (16 bytes, bf16).  Fragments of one 16-column
-// tile ("n-tile") are contiguous along k, so a wave streams a tile's K
-// extent as consecutive 1 KB blocks.
-constexpr int kWave = 64;
-constexpr int kTileN = 16;
-constexpr int kChunkK = 32;
-constexpr int kGroupK = 128;          // int4 scale group along K
-constexpr int kWavesPerWG = 4;
-constexpr int kColsPerWG = kWavesPerWG * kTileN;   // 64 output columns / WG
+// ---------------------------------------------------------------- geometry
+// The verification pass runs as one persistent cooperative kernel: one
+// workgroup of kWaves waves per compute unit (one per SIMD, so a wave may
+// hold up to 512 registers), each wave streaming its weights in batches of
+// kRing 1 KB fragments (128 KB in flight per CU).  Work of every weight-
+// streaming phase is split over the workgroups in equal runs of
+// (supergroup, K chunk) units ("stream-K"); a supergroup is kWaves output
+// units, one per wave, so the kWaves waves of a workgroup read one
+// contiguous block of kWaves x 1 KB fragments per K chunk.
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTileN = 16;            // output columns per MFMA tile
+constexpr int kChunkK = 32;           // k per bf16 / fp32 fragment
+constexpr int kGroupK = 128;          // int4: k per fragment (= scale group)
 constexpr int kMaxRows = 16;          // block rows (k+1) per pass
-constexpr int kPage = 64;             // KV page = attention chunk (positions)
+constexpr int kPage = 64;             // KV page (positions); attention sub-chunk
+constexpr int kGroupPages = 4;        // pages per attention work item (fixed grid)
+constexpr int kGroupPos = kPage * kGroupPages;
+constexpr int kMaxAttnRows = 128;     // (k+1) * (n_q_heads / n_kv_heads) per KV head
+constexpr int kRing = 32;             // weight fragments per prefetch batch (per wave)
+constexpr int kAWindowBytes = 64 * 1024;   // LDS bytes of one staged A window (two are resident)
+constexpr int kMaxLds = 160 * 1024;
 
 enum WFmt : int { W_BF16 = 0, W_INT4 = 1, W_F32 = 2 };
-enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
 
-struct GemmParams {
-  int m;              // live rows (<= 16)
-  int K;              // logical K
-  int nkc;            // K chunks of 32 in the fragment layout (padded)
-  int N;              // logical output columns (SWIGLU: act columns)
-  int n_tiles;        // weight n-tiles (SWIGLU: 2 per act tile, interleaved gate/up)
-  int kcs;            // chunks per split-K slice
-  int splits;         // number of K slices
-  // activations
-  const float* x; int ldx; long long x_stride;   // x_stride: per expert slot (MoE down)
-  const float* ss; int n_ss; float inv_dnorm; float eps;   // RMSNorm prologue (ss == nullptr: none)
-  const float* gain;                                      // per-k gain (nullptr: 1)
-  // weights
-  const void* w;            // fragments (bf16 / int4) or hi fragments (f32)
-  const void* w2;           // lo fragments (f32) or fp16 scales (int4)
-  long long w_stride;       // bytes between experts (MoE)
-  long long w2_stride;
-  // split-K scratch
-  float* ws; unsigned* counters;
-  // outputs
-  float* out; int ldo; long long out_stride;   // per expert slot (MoE)
-  float* ss_out; int n_ss_out;                 // RESID: sum-of-squares partials of new x
-  float* st_max; float* st_sum; int* st_idx; int n_stat;   // LOGITS partials (per 64 cols)
-  // MoE expert dispatch (nullptr: dense)
-  const int* union_count; const int* union_list; int n_experts; int n_shared;
+// One weight matrix, or a stack of expert matrices of one shape, in the
+// streaming layout: fragment (expert, supergroup, chunk, wave, half) at
+// ((((e * n_sg + sg) * nkc + c) * kWaves + w) * tpu + half) KB, where the
+// output unit of (sg, w) is sg * kWaves + w and a unit is one 16-column
+// tile (tpu = 1) or a gate tile and its up tile (tpu = 2).
+struct Mat {
+  const void* w;          // fragments (bf16, int4, or the bf16 "hi" part of fp32)
+  const void* w2;         // fp32: "lo" fragments; int4: fp16 scales [..][16]; else null
+  long long w_stride;     // bytes per expert (w)
+  long long w2_stride;    // bytes per expert (w2)
+  int n_units;            // units per expert
+  int n_sg;               // supergroups per expert = ceil(n_units / kWaves)
+  int nkc;                // fragments along K (32 k each; 128 k for int4)
+  int win;                // chunks per staged A window
+  int n_win;              // ceil(nkc / win)
+  int K, N;               // logical shape (N: output columns; SwiGLU: activation columns)
+  int max_seg;            // workspace slots per unit block (split-K partials)
 };
 
-struct AttnParams {
-  int m, L, G;           // block rows, committed length, query heads per KV head
-  int Hq, Hkv, D;
-  int n_chunks;
-  const float* qkv; int ldqkv;     // [m][(Hq+2Hkv)*D]
-  const float* rope_cs;            // [max_ctx][D/2][2] (cos, sin)
-  void* kv;                        // layer base: pages [page][Hkv][2][kPage][D]
+// One phase of the pass program (a grid barrier separates consecutive
+// phases).  GEMM phases stream M; the other fields are what the phase kind
+// reads or writes.
+enum PhKind : int {
+  PH_EMBED = 0,        // embedding gather + first norm's A operand
+  PH_STORE = 1,        // Y = (A W) [* row scale] -> out (QKV, router, expert down)
+  PH_RESID = 2,        // x += A W -> next A operand (x * gain), sum-of-squares
+  PH_SWIGLU = 3,       // silu(s * A Wg) * (s * A Wu) -> next A operand
+  PH_LOGITS = 4,       // logits = s * A W and per-tile (max, argmax, sum-exp)
+  PH_ATTN = 5,         // causal attention over the paged cache -> per-group partials
+  PH_ROUTE_SWIGLU = 6, // MoE routing of the block, then SWIGLU over the union
+  PH_COMBINE = 7,      // MoE weighted combine -> x, next A operand
+  PH_ATTN_MERGE = 8    // merge of the attention partials -> A operand of O
+};
+
+struct Phase {
+  int kind, layer;
+  int slot_mode;          // 0 dense; 1 MoE slots sharing A; 2 MoE slot-major (A per slot)
+  int trace;              // RESID / COMBINE: this phase finishes the layer's residual
+  Mat M;
+  const uint4* a; long long a_slot;
+  float* out; int ldo; long long out_slot; int scale;
+  const float* gain;      // RESID / COMBINE: gain of the next norm
+  uint4* a_out; long long a_out_slot;
+  const float* bias;      // ROUTE: router bias
+  void* kv;               // ATTN: the layer's KV pages
+  int next_gemm;          // index of the next weight-streaming phase (n_prog if none)
+};
+
+// Everything one pass needs; passed by value to the pass kernel.
+struct PassP {
+  int m, L, n_layers, d, Hq, Hkv, D, V, G, E, top_k, n_shared, F;
+  int n_groups;              // attention position groups covering [0, L+m)
+  int n_ss;                  // d / 16: sum-of-squares partials per row
+  int lds_bytes;             // dynamic LDS of the launch (control area at its end)
+  float eps, inv_d, attn_scale;
+  const Phase* prog; int n_prog;   // device array: the phases of one pass
+  const void* embed;         // [V][d] bf16 bits (fp32 for fp32 models)
+  const float* gain0;        // attention-norm gain of layer 0
+  const int* tokens;         // [m]
   const int* page_table;
-  float* pm; float* ps; float* pacc;   // partials [Hkv][n_chunks][R] / [..][R][D]
-  int R;                           // m*G
-  float scale;                     // 1/sqrt(D)
-};
-
-struct CombineParams {
-  int m, G, Hq, D, n_chunks, R;
-  const float* pm; const float* ps; const float* pacc;
-  float* o; int ldo;
+  const float* rope_cs;      // [max_ctx][D/2][2]
+  // activations
+  float* x; int ldx;         // residual stream [16][ldx]
+  float* ss;                 // [16][n_ss]
+  uint4* a_norm;             // A operand of norm-fed GEMMs: x * gain, hi/lo fragments
+  uint4* a_o;                // attention output, hi/lo fragments
+  uint4* a_act;              // SwiGLU output [slot][..], hi/lo fragments
+  long long a_act_slot;      // uint4 per slot
+  float* qkv; int ldqkv;     // [16][ldqkv]
+  float* logits; int ldl;    // [16][ldl]
+  float* st_max; float* st_sum; int* st_idx; int n_stat;   // per 16-column tile of the LM head
+  float* pm; float* ps; float* pacc;                      // attention partials
+  float* rlog; int ldr;      // MoE router logits [16][ldr]
+  float* ey; long long ey_slot; int ldy;                  // expert outputs [slot][16][ldy]
+  int* route;                // MoE routing record (route_words)
+  // split-K workspace and tickets
+  float* ws; unsigned* tickets;
+  // grid barrier
+  unsigned long long* bar; unsigned long long bar_base;
+  int* err;                  // set to 1 by a grid-barrier wait that ran out
+  // debug / profiling (nullable)
+  float* trace;              // [n_layers][m][d]
+  int* union_hist;           // [n_layers]
+  unsigned long long* stamps;   // [n_phases + 1] wall clock at phase ends (workgroup 0)
 };
 
 struct AcceptParams {
@@ -80,37 +127,24 @@ struct AcceptParams {
   int* result;          // [3]
 };
 
-struct RouteParams {
-  int m, E, top_k;
-  const float* rlogits; int ldr;   // [m][E] router logits (without bias)
-  const float* bias;
-  int* union_count; int* union_list; int* sel; float* selw; int* slot_of;
-  int* union_hist;       // nullable: per-layer |U| record
-};
-
-struct MoeCombineParams {
-  int m, d, top_k, n_shared, n_ss;
-  const int* union_count; const int* sel; const float* selw; const int* slot_of;
-  const float* y; long long y_stride; int ldy;   // [slot][m][d]
-  float* x; int ldx; float* ss_out;
-};
+// MoE routing record in global memory (int32 words):
+//   [0] union size U; [1 .. E] union list (ascending expert id);
+//   [1+E .. 2E] slot of each expert (-1 if unused);
+//   [1+2E ..) sel [16][top_k] expert ids; then selw [16][top_k] fp32 bits.
+__host__ __device__ inline int route_words(int E, int top_k) { return 1 + 2 * E + 2 * 16 * top_k; }
 
 // ---------------------------------------------------------------- launchers
-hipError_t launch_gemm(int wfmt, int epi, const GemmParams& p, int n_slots, hipStream_t s);
-hipError_t launch_attention(int kv_f32, const AttnParams& p, hipStream_t s);
-hipError_t launch_attn_combine(const CombineParams& p, hipStream_t s);
-hipError_t launch_embed(int emb_f32, const void* table, const int* tokens, int m, int d,
-                        float* x, float* ss_out, hipStream_t s);
-hipError_t launch_route(const RouteParams& p, hipStream_t s);
-hipError_t launch_moe_combine(const MoeCombineParams& p, hipStream_t s);
+// One pass executes n_prog - 1 grid barriers (the host advances the barrier
+// generation by that much per launch).  fp32 weights imply an fp32 KV cache;
+// bf16 / int4 weights a bf16 cache.
+hipError_t launch_pass(int wfmt, const PassP& p, int n_wg, size_t lds, hipStream_t s);
+size_t pass_lds_bytes(int wfmt, int max_rows_attn, int D);
+hipError_t pass_occupancy(int wfmt, size_t lds, int* blocks_per_cu);
+// split units one workgroup may flush per phase (control-area capacity)
+constexpr int kMaxPending = 512;
 hipError_t launch_accept(const AcceptParams& p, hipStream_t s);
-hipError_t launch_retile_bf16(const uint16_t* src, int K, int N, void* dst, int nkc,
-                              int tile_off, int tile_stride, hipStream_t s);
-hipError_t launch_retile_f32(const float* src, int K, int N, void* dst_hi, void* dst_lo, int nkc,
-                             int tile_off, int tile_stride, hipStream_t s);
-hipError_t launch_retile_int4(const uint8_t* src_q, const uint16_t* src_s, int K, int N, void* dst,
-                              void* dst_s, int tile_off, int tile_stride, int n_tiles_total,
-                              hipStream_t s);
+hipError_t launch_retile(int wfmt, const void* src, const void* src_scales, int K, int N, void* dst,
+                         void* dst2, int nkc, int tpu, int tile_off, int tile_stride, hipStream_t s);
 hipError_t launch_kv_import(int kv_f32, const void* src, int P, int Hkv, int D, void* layer_base,
                             const int* page_table, hipStream_t s);
 
