@@ -130,6 +130,7 @@ class Session:
         dt = time.perf_counter() - t0
         prof = h.profile_read() if profile else None
         if profile:
+            self.detail = h.profile_detail()
             h.profile(False)
         return out, s, pending, dt, prof
 
@@ -257,10 +258,17 @@ def main():
                 f"{r['verified_tok_s']:.1f} verified tok/s, mean accepted+1 {r['mean_accept']:.3f}, "
                 f"{r['pass_gb']:.3f} GB/pass, wall {r['wall_gbs']:.0f} GB/s "
                 f"({r['wall_gbs'] / HBM_PEAK_GBS:.1%} of 8 TB/s)")
+            det = getattr(sess, "detail", {})
             for c, (n, ms, by) in r["prof"].items():
                 if n:
-                    log(f"[bench]   {c:14s} {n:6d} launches {ms / n * 1e3:9.1f} us/launch "
-                        f"{by / n / 1e6:9.2f} MB/launch {by / ms / 1e6 if ms else 0:8.0f} GB/s")
+                    line = (f"[bench]   {c:14s} {n:6d} launches {ms / n * 1e3:9.1f} us/launch "
+                            f"{by / n / 1e6:9.2f} MB/launch {by / ms / 1e6 if ms else 0:8.0f} GB/s")
+                    if c in det and c not in ("pass", "accept"):
+                        mean, mx = ([v / n * 1e3 for v in t] for t in det[c])
+                        line += (" | workgroup mean/max us: stage %.1f/%.1f stream %.1f/%.1f flush %.1f/%.1f "
+                                 "work %.1f/%.1f, barrier %.1f" % (mean[0], mx[0], mean[1], mx[1], mean[2], mx[2],
+                                                                   mean[3], mx[3], ms / n * 1e3 - mx[3]))
+                    log(line)
     r = results[k]
     name, n, ms, by = dominant(r["prof"])
     per_launch_bytes = by / n

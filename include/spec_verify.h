@@ -80,7 +80,7 @@ typedef struct {
   int32_t max_ctx;       /* KV capacity in positions */
   int32_t max_k;         /* largest k per step, 0..15 */
   int32_t gemm_k_split;  /* K elements per staged activation window of the weight-streaming
-                            phases (multiple of 128, at most 1024); 0 = 1024.  Smaller windows
+                            phases (multiple of 128, at most 2048); 0 = 2048.  Smaller windows
                             split every output over more partial sums (a test knob). */
   int32_t reserved[7];   /* must be zero */
 } spec_config;
@@ -215,6 +215,18 @@ int spec_profile_enable(spec_verify_t* h, int32_t on);
  * launches / ms / bytes: host arrays of SPEC_K_NCLASSES entries (any may
  * be NULL). */
 int spec_profile_read(const spec_verify_t* h, int64_t* launches, double* ms, double* bytes);
+
+/* Per-workgroup split of each class's phases while profiling is on (device
+ * wall-clock stamps taken by every workgroup), summed over launches, in ms.
+ * For class c, out[8*c + j] is the mean over workgroups and out[8*c + 4 + j]
+ * the maximum of: j = 0 activation staging, 1 weight stream, 2 flush
+ * (split-K tickets, reductions, epilogues), 3 the whole work.  Attention:
+ * j = 0 operand loads and query set-up, 1 the position walk, 2 partials
+ * and merges (of a workgroup's last item).  Other phases that stream no
+ * weights: their whole work in j = 2.  A phase's time
+ * (spec_profile_read) minus the maximum whole work is its grid-barrier
+ * wait.  out: host array of 8 * SPEC_K_NCLASSES doubles. */
+int spec_profile_detail(const spec_verify_t* h, double* out);
 
 /* Like spec_verify_step, and additionally copies the residual stream after
  * every layer into trace_dev (device fp32 [n_layers][k+1][d_model], may be

@@ -73,6 +73,7 @@ def _load():
         "spec_verify_destroy": (None, [P]),
         "spec_profile_enable": (I, [P, I]),
         "spec_profile_read": (I, [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(D), ctypes.POINTER(D)]),
+        "spec_profile_detail": (I, [P, ctypes.POINTER(D)]),
         "spec_pass_bytes": (D, [P, I, I, I, ctypes.c_int64]),
     }
     for name, (res, args) in sig.items():
@@ -96,6 +97,7 @@ spec_last_error = lib.spec_last_error
 spec_verify_destroy = lib.spec_verify_destroy
 spec_profile_enable = lib.spec_profile_enable
 spec_profile_read = lib.spec_profile_read
+spec_profile_detail = lib.spec_profile_detail
 spec_pass_bytes = lib.spec_pass_bytes
 
 
@@ -220,6 +222,15 @@ class Verifier:
         by = (ctypes.c_double * SPEC_K_NCLASSES)()
         spec_profile_read(self.h, n, ms, by)
         return {KERNEL_CLASSES[i]: (int(n[i]), float(ms[i]), float(by[i])) for i in range(SPEC_K_NCLASSES)}
+
+    def profile_detail(self):
+        """Per class: ((stage, stream, flush, work) means, (...) maxima) over
+        workgroups, ms summed over launches."""
+        out = (ctypes.c_double * (8 * SPEC_K_NCLASSES))()
+        spec_profile_detail(self.h, out)
+        return {KERNEL_CLASSES[i]: (tuple(float(out[8 * i + j]) for j in range(4)),
+                                    tuple(float(out[8 * i + 4 + j]) for j in range(4)))
+                for i in range(SPEC_K_NCLASSES)}
 
     def pass_bytes(self, L: int, k: int, mode: int = SPEC_ACCEPT_GREEDY, experts_loaded: int = 0) -> float:
         return spec_pass_bytes(self.h, L, k, mode, experts_loaded)

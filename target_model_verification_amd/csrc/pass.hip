@@ -71,6 +71,39 @@ __device__ __forceinline__ u4 nib8_to_bf16(uint32_t d) {
   return u4{o[0], o[1], o[2], o[3]};
 }
 
+// Data one workgroup writes and another reads later in the same pass is
+// stored through to the device-coherent level (agent-scope relaxed atomic
+// stores, "sc1"): a signal then needs no L2 write-back, only each wave's
+// wait on its own stores.  Reads that follow a grid barrier are plain (the
+// barrier's acquire drops stale cache lines); reads that follow a ticket
+// instead of a barrier use agent-scope loads.
+__device__ __forceinline__ void cst(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void cst(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void cst16(uint16_t* p, uint16_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void cst4(float* p, f32x4 v) {   // p 16-byte aligned
+  unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
+  const unsigned long long a = (unsigned long long)__float_as_uint(v[0]) | (unsigned long long)__float_as_uint(v[1]) << 32;
+  const unsigned long long b = (unsigned long long)__float_as_uint(v[2]) | (unsigned long long)__float_as_uint(v[3]) << 32;
+  __hip_atomic_store(q, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float cld(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 cld4(const float* p) {   // p 16-byte aligned
+  unsigned long long* q = reinterpret_cast<unsigned long long*>(const_cast<float*>(p));
+  const unsigned long long a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x4{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)), __uint_as_float((uint32_t)b),
+               __uint_as_float((uint32_t)(b >> 32))};
+}
+
 // Element (row, col) of an A operand in hi/lo fragment layout: 32-k chunk
 // col/32 holds 128 uint4 (hi[64], lo[64]); lane l of a fragment holds 8
 // consecutive k of row l%16 starting at 8*(l/16).
@@ -80,8 +113,8 @@ __device__ __forceinline__ void afrag_put(uint4* a, int row, int col, float v) {
   const int ch = col >> 5, kk = col & 31;
   const int ln = row + 16 * (kk >> 3), e = kk & 7;
   uint16_t* base = reinterpret_cast<uint16_t*>(a + (long long)ch * 128);
-  base[ln * 8 + e] = (uint16_t)h;
-  base[(64 + ln) * 8 + e] = (uint16_t)l;
+  cst16(base + ln * 8 + e, (uint16_t)h);
+  cst16(base + (64 + ln) * 8 + e, (uint16_t)l);
 }
 
 // raw workgroup barrier: execution only; the compiler may not move memory
@@ -90,6 +123,12 @@ __device__ __forceinline__ void raw_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Per-workgroup stamp i (0 start, 1 after A staging, 2 after the weight
+// stream, 3 end of work) of the current phase; ws is null when off.
+__device__ __forceinline__ void wstamp(unsigned long long* ws, int i) {
+  if (ws && threadIdx.x == 0) ws[i] = wall_clock64();
 }
 
 // ------------------------------------------------------------ grid barrier
@@ -133,7 +172,8 @@ __device__ __forceinline__ void grid_sync(GridBar& gb, PF&& prefetch) {
     const unsigned g = blockIdx.x & 7u;
     const unsigned long long ng = (gridDim.x - g + 7u) / 8u;
     const unsigned long long ngr = gridDim.x < 8 ? gridDim.x : 8;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // (no release fence: the phase's shared data was stored through, and
+    // every wave waited for its stores before the workgroup barrier)
     const unsigned long long old =
         __hip_atomic_fetch_add(gb.bar + 16 * g, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == gb.gen * ng - 1) {
@@ -165,7 +205,7 @@ __device__ __forceinline__ void grid_sync(GridBar& gb, PF&& prefetch) {
 }
 
 // ------------------------------------------------------------ LDS plan
-// [0, 2*kAWindowBytes): two staged A windows (GEMM phases) / attention
+// [0, kAWindowBytes): the staged A window (GEMM phases) / attention
 // working set; then a small control area.
 constexpr int kCtlBytes = 4096;
 struct Ctl {
@@ -280,7 +320,7 @@ __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const Gem
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * rg + i;
-      if (row < P.m && col < M.N) out[(long long)row * io.ldo + col] = io.scale ? rs[row] * acc[0][i] : acc[0][i];
+      if (row < P.m && col < M.N) cst(out + (long long)row * io.ldo + col, io.scale ? rs[row] * acc[0][i] : acc[0][i]);
     }
   } else if constexpr (EPI == EPI_RESID) {
     const int col = unit * kTileN + cl;
@@ -291,7 +331,7 @@ __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const Gem
       float v = 0.f;
       if (row < P.m && col < M.N) {
         v = P.x[(long long)row * P.ldx + col] + acc[0][i];
-        P.x[(long long)row * P.ldx + col] = v;
+        cst(P.x + (long long)row * P.ldx + col, v);
         if (io.trace) io.trace[(long long)row * P.d + col] = v;
       }
       sq[i] = v * v;
@@ -306,7 +346,7 @@ __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const Gem
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 4 * rg + i;
-        if (row < P.m) P.ss[row * P.n_ss + unit] = sq[i];
+        if (row < P.m) cst(P.ss + row * P.n_ss + unit, sq[i]);
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
@@ -380,13 +420,12 @@ __device__ __forceinline__ void row_scales(const PassP& P, float* rs) {
 
 // Stages the A window of block (slot, win) into LDS window slot `ws`.
 template <int WF>
-__device__ __forceinline__ void stage_window(const Lin& L, const GemmIO& io, int slot, int win, unsigned char* smem,
-                                             int ws) {
+__device__ __forceinline__ void stage_window(const Lin& L, const GemmIO& io, int slot, int win, unsigned char* smem) {
   constexpr int ACH = (WF == W_INT4) ? 4 : 1;
-  constexpr int B = 8;   // loads in flight per thread
+  constexpr int B = 16;   // loads in flight per thread
   const int n16 = L.wlen(win) * ACH * 128;    // uint4 to copy
   const gu4* src = (const gu4*)(io.a + (long long)slot * io.a_slot + (long long)win * L.W * ACH * 128);
-  u4* dst = reinterpret_cast<u4*>(smem + ws * kAWindowBytes);
+  u4* dst = reinterpret_cast<u4*>(smem);
   for (int i0 = threadIdx.x; i0 < n16; i0 += kThreads * B) {
     u4 v[B];
 #pragma unroll
@@ -405,7 +444,7 @@ __device__ __forceinline__ void stage_window(const Lin& L, const GemmIO& io, int
 // One weight-streaming phase over `sm.n_slots` slots (experts) of M.
 template <int WF, int EPI, int TPU>
 __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const GemmIO io, const SlotMap sm,
-                                        bool slot_major, Ring& ring, unsigned char* smem) {
+                                        bool slot_major, Ring& ring, unsigned char* smem, unsigned long long* wst) {
   using F = Fmt<WF, TPU>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -417,29 +456,21 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
   if (threadIdx.x == 0) C->pend_n = 0;
   if (EPI == EPI_SWIGLU || EPI == EPI_LOGITS || (EPI == EPI_STORE && io.scale)) row_scales(P, C->rs);
 
-  // A windows touched by [u0, u1), staged in order into LDS slots 0 and 1
-  // (key, win) of the blocks in LDS window slots 0 and 1
-  int sk0 = -1, sw0 = -1, sk1 = -1, sw1 = -1;
+  // the A window of the range's first block; a range that crosses into
+  // another (key, window) restages (a few workgroups per phase)
+  int sk = -1, sw = -1;
   if (u0 < u1) {
-    const Cur a = cur_at(L, u0), b = cur_at(L, u1 - 1);
-    const int ka = slot_major ? a.slot : 0, kb = slot_major ? b.slot : 0;
-    sk0 = ka;
-    sw0 = a.win;
-    stage_window<WF>(L, io, ka, a.win, smem, 0);
-    if (ka != kb || a.win != b.win) {
-      int ns = ka, nw = a.win;
-      if (slot_major) {
-        if (++nw == L.n_win) { nw = 0; ++ns; }
-      } else {
-        ++nw;
-      }
-      sk1 = ns;
-      sw1 = nw;
-      stage_window<WF>(L, io, ns, nw, smem, 1);
-    }
+    const Cur a = cur_at(L, u0);
+    sk = slot_major ? a.slot : 0;
+    sw = a.win;
+    stage_window<WF>(L, io, sk, sw, smem);
   }
   __syncthreads();
-  if (u0 >= u1) return;
+  wstamp(wst, 1);
+  if (u0 >= u1) {
+    wstamp(wst, 2);
+    return;
+  }
 
   // the caller issued the first batch (gemm_prefetch); advance the load
   // cursor past it
@@ -451,13 +482,12 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
   }
 
   Cur cc = cur_at(L, u0);
-  int wi = 0;   // LDS window slot in use
   f32x4 acc[TPU];
 
   // one batch of n chunks starting at window chunk c0
   auto compute = [&](int c0, int n, bool live) {
     if (!live) return;
-    const uint4* aw = reinterpret_cast<const uint4*>(smem + (wi & 1) * kAWindowBytes) + (long long)c0 * F::ACH * 128;
+    const uint4* aw = reinterpret_cast<const uint4*>(smem) + (long long)c0 * F::ACH * 128;
     const u4 z4 = u4{0u, 0u, 0u, 0u};
     // branch-free over the batch: slots past n use zero weights and a valid
     // (finite) A chunk, so they add exact zeros
@@ -528,7 +558,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
       } else {
         float* p = P.ws + ((((long long)cc.slot * M.n_sg + cc.sg) * M.max_seg + idx) * kWaves + wave) * TPU * 256;
 #pragma unroll
-        for (int t = 0; t < TPU; ++t) *reinterpret_cast<f32x4*>(p + t * 256 + lane * 4) = acc[t];
+        for (int t = 0; t < TPU; ++t) cst4(p + t * 256 + lane * 4, acc[t]);
       }
     }
     if (nseg > 1 && threadIdx.x == 0) {
@@ -539,27 +569,23 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     if (cc.u >= u1) break;
     seg_advance(L, cc);
     const int key = slot_major ? cc.slot : 0;
-    const bool same = (wi & 1) ? (key == sk1 && cc.win == sw1) : (key == sk0 && cc.win == sw0);
-    if (!same) {
-      ++wi;
-      if (wi >= 2) {   // a third window: restage (rare)
-        __syncthreads();
-        if (wi & 1) { sk1 = key; sw1 = cc.win; } else { sk0 = key; sw0 = cc.win; }
-        stage_window<WF>(L, io, key, cc.win, smem, wi & 1);
-        __syncthreads();
-      }
+    if (key != sk || cc.win != sw) {
+      __syncthreads();   // every wave is done with the staged window
+      sk = key;
+      sw = cc.win;
+      stage_window<WF>(L, io, sk, sw, smem);
+      __syncthreads();
     }
   }
 
+  wstamp(wst, 2);
   // ---- split units: tickets, then the last arriver sums partials in K order
   release_all_waves();
   __syncthreads();
   const int np = C->pend_n;
   if (np == 0) return;
-  // one lane per split block: the tickets go out together, after one
-  // agent-scope release per signalling wave (every partial of this
-  // workgroup is complete in the L2 by now)
-  if (threadIdx.x < np) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // one lane per split block: the tickets go out together (every partial of
+  // this workgroup is stored through and complete by now)
   for (int k = threadIdx.x; k < np; k += kThreads) {
     const int s = C->pend[k] >> 20, sg = C->pend[k] & 0xfffff;
     int idx, n;
@@ -567,14 +593,11 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     unsigned* t = P.tickets + (long long)s * M.n_sg + sg;
     const unsigned old = __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = old == (unsigned)(n - 1);
-    if (last) {
-      __hip_atomic_store(t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
-    C->last[k] = last ? 1 : 0;
+    if (last) __hip_atomic_store(t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    C->last[k] = last ? 1 : 0;   // the partials are then read with agent-scope loads
   }
   __syncthreads();
-  constexpr int RB = 4;   // partial loads in flight per lane
+  constexpr int RB = TPU == 1 ? 16 : 8;   // partial loads in flight per lane (a block's usual count)
   for (int k = 0; k < np; ++k) {
     if (!C->last[k]) continue;
     const int s = C->pend[k] >> 20, sg = C->pend[k] & 0xfffff;
@@ -592,7 +615,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
       for (int q = 0; q < RB; ++q) {
 #pragma unroll
         for (int t = 0; t < TPU; ++t)
-          v[q][t] = j0 + q < n ? *reinterpret_cast<const f32x4*>(p + (long long)(j0 + q) * kWaves * TPU * 256 + t * 256)
+          v[q][t] = j0 + q < n ? cld4(p + (long long)(j0 + q) * kWaves * TPU * 256 + t * 256)
                                : f32x4{0.f, 0.f, 0.f, 0.f};
       }
       // partials are added in K order
@@ -644,13 +667,13 @@ __device__ __forceinline__ void embed_phase(const PassP& P, bool emb_f32) {
       const long long tok = P.tokens[row];
       v = emb_f32 ? static_cast<const float*>(P.embed)[tok * P.d + col]
                   : bf2f(static_cast<const uint16_t*>(P.embed)[tok * P.d + col]);
-      P.x[(long long)row * P.ldx + col] = v;
+      cst(P.x + (long long)row * P.ldx + col, v);
     }
     if (col < P.d) afrag_put(P.a_norm, row, col, v * P.gain0[col]);
     float sq = v * v;
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o, 64);
-    if (cl == 0 && row < P.m) P.ss[row * P.n_ss + tile] = sq;
+    if (cl == 0 && row < P.m) cst(P.ss + row * P.n_ss + tile, sq);
   }
 }
 
@@ -668,21 +691,10 @@ __device__ __forceinline__ void embed_phase(const PassP& P, bool emb_f32) {
 // exact zeros, so a row's result does not depend on the block size or on
 // positions after it.
 template <bool KVF32>
-__device__ __forceinline__ float kv_ld(const void* base, long long i) {
-  if constexpr (KVF32) return static_cast<const float*>(base)[i];
-  else return bf2f(static_cast<const uint16_t*>(base)[i]);
-}
-template <bool KVF32>
 __device__ __forceinline__ void kv_st(void* base, long long i, float v) {
   if constexpr (KVF32) static_cast<float*>(base)[i] = v;
   else static_cast<uint16_t*>(base)[i] = (uint16_t)f2bf(v);
 }
-template <bool KVF32>
-__device__ __forceinline__ float kv_round(float v) {
-  if constexpr (KVF32) return v;
-  else return bf2f(f2bf(v));
-}
-
 // 8 fp32 -> bf16 hi and lo parts (hi + lo carries ~16 significant bits)
 __device__ __forceinline__ void split8(const float (&v)[8], u4& hi, u4& lo) {
   uint32_t h[8], l[8];
@@ -695,52 +707,6 @@ __device__ __forceinline__ void split8(const float (&v)[8], u4& hi, u4& lo) {
   lo = u4{l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16, l[6] | l[7] << 16};
 }
 
-// 8 consecutive cache elements at element index i as MFMA operand(s)
-// (bf16: the raw word; fp32: hi and lo parts); lanes with keep == false
-// contribute zeros.
-template <bool KVF32>
-__device__ __forceinline__ void kv_operand(const void* kv, long long i, bool keep, u4& hi, u4& lo) {
-  if constexpr (KVF32) {
-    const gu4* p = (const gu4*)(static_cast<const float*>(kv) + i);
-    const u4 a = p[0], b = p[1];
-    float v[8] = {__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3]),
-                  __uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3])};
-    if (!keep)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    split8(v, hi, lo);
-  } else {
-    const u4 z{0u, 0u, 0u, 0u};
-    hi = keep ? *(const gu4*)(static_cast<const uint16_t*>(kv) + i) : z;
-    lo = z;
-  }
-}
-
-// value operand: 8 consecutive positions of one d from a transposed value
-// page; positions at or past nvalid are zeroed (they may hold any bits)
-template <bool KVF32>
-__device__ __forceinline__ void v_operand(const void* kv, long long i, int p0, int nvalid, u4& hi, u4& lo) {
-  if constexpr (KVF32) {
-    const gu4* p = (const gu4*)(static_cast<const float*>(kv) + i);
-    const u4 a = p[0], b = p[1];
-    float v[8] = {__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3]),
-                  __uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3])};
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (p0 + e >= nvalid) v[e] = 0.f;
-    split8(v, hi, lo);
-  } else {
-    u4 w = *(const gu4*)(static_cast<const uint16_t*>(kv) + i);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (p0 + 2 * q >= nvalid) w[q] &= 0xFFFF0000u;
-      if (p0 + 2 * q + 1 >= nvalid) w[q] &= 0x0000FFFFu;
-    }
-    hi = w;
-    lo = u4{0u, 0u, 0u, 0u};
-  }
-}
-
 constexpr int kAttnRT = kMaxAttnRows / 16;   // row tiles at most
 constexpr int kPsStride = kPage + 4;         // floats per score row in LDS
 
@@ -750,10 +716,123 @@ __host__ __device__ constexpr size_t attn_lds_bytes(int rt, int D) {
   return (size_t)rt * (D / 32) * 2 * 1024 + (size_t)rt * 16 * kPsStride * 4 + (size_t)3 * rt * 16 * 4;
 }
 
-template <bool KVF32>
-__device__ __forceinline__ void attention_phase(const PassP& P, void* kv, unsigned char* smem) {
+// One output element (row r, dim d) of KV head g: the groups' partials
+// combined in ascending group order.
+__device__ __forceinline__ float attn_merge_one(const PassP& P, int g, int r, int d) {
+  const int D = P.D, R = P.m * P.G, NG = P.n_groups;
+  const long long base = (long long)g * NG * R + r;   // (g, grp, r) at base + grp * R
+  constexpr int B = 8;                                // groups in flight
+  float M = -INFINITY;
+  for (int c0 = 0; c0 < NG; c0 += B) {
+    float v[B];
+#pragma unroll
+    for (int q = 0; q < B; ++q) v[q] = c0 + q < NG ? P.pm[base + (long long)(c0 + q) * R] : -INFINITY;
+#pragma unroll
+    for (int q = 0; q < B; ++q) M = fmaxf(M, v[q]);
+  }
+  float S = 0.f, A = 0.f;
+  for (int c0 = 0; c0 < NG; c0 += B) {
+    float vm[B], vs[B], va[B];
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      const bool ok = c0 + q < NG;
+      const long long pi = base + (long long)(c0 + q) * R;
+      vm[q] = ok ? P.pm[pi] : -INFINITY;
+      vs[q] = ok ? P.ps[pi] : 0.f;
+      va[q] = ok ? P.pacc[pi * D + d] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      if (c0 + q < NG) {
+        const float f = vm[q] == -INFINITY ? 0.f : expf(vm[q] - M);
+        S += f * vs[q];
+        A += f * va[q];
+      }
+    }
+  }
+  return A / S;
+}
+
+__device__ __forceinline__ void attn_merge_store(const PassP& P, int g, int r, int d) {
+  const int j = r / P.G, h = g * P.G + r % P.G;
+  afrag_put(P.a_o, j, h * P.D + d, attn_merge_one(P, g, r, d));
+}
+
+// The whole merge of KV head g by one workgroup (its last attention item):
+// per-row group factors once in LDS, then each thread's outputs with their
+// partial loads in flight together.  Same arithmetic as attn_merge_one.
+__device__ __forceinline__ void attn_merge_head(const PassP& P, int g, unsigned char* smem) {
+  const int D = P.D, R = P.m * P.G, NG = P.n_groups;
+  const int tid = threadIdx.x;
+  float* fv = reinterpret_cast<float*>(smem);   // [NG][R]: pm, then the factors
+  float* sv = fv + NG * R;                      // [NG][R]: ps
+  float* Sr = sv + NG * R;                      // [R]
+  const long long gb = (long long)g * NG * R;
+  for (int i = tid; i < NG * R; i += kThreads) {
+    fv[i] = cld(P.pm + gb + i);
+    sv[i] = cld(P.ps + gb + i);
+  }
+  __syncthreads();
+  for (int r = tid; r < R; r += kThreads) {
+    float M = -INFINITY;
+    for (int c = 0; c < NG; ++c) M = fmaxf(M, fv[c * R + r]);
+    float S = 0.f;
+    for (int c = 0; c < NG; ++c) {
+      const float m = fv[c * R + r];
+      const float f = m == -INFINITY ? 0.f : expf(m - M);
+      S += f * sv[c * R + r];
+      fv[c * R + r] = f;
+    }
+    Sr[r] = S;
+  }
+  __syncthreads();
+  constexpr int KB = 8;   // outputs per thread per round
+  constexpr int GB = 4;   // groups per round
+  for (int e0 = tid; e0 < R * D; e0 += kThreads * KB) {
+    float A[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) A[k] = 0.f;
+    for (int c0 = 0; c0 < NG; c0 += GB) {
+      float v[KB][GB];
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int e = e0 + k * kThreads;
+#pragma unroll
+        for (int q = 0; q < GB; ++q)
+          v[k][q] = (e < R * D && c0 + q < NG) ? cld(P.pacc + (gb + (long long)(c0 + q) * R) * D + e) : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int e = e0 + k * kThreads;
+        if (e < R * D) {
+          const int r = e / D;
+#pragma unroll
+          for (int q = 0; q < GB; ++q)
+            if (c0 + q < NG) A[k] += fv[(c0 + q) * R + r] * v[k][q];
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int e = e0 + k * kThreads;
+      if (e < R * D) {
+        const int r = e / D, d = e % D;
+        const int j = r / P.G, h = g * P.G + r % P.G;
+        afrag_put(P.a_o, j, h * D + d, A[k] / Sr[r]);
+      }
+    }
+  }
+}
+
+template <bool KVF32, int MAXRT>
+__device__ __forceinline__ void attention_phase(const PassP& P, void* kv, unsigned char* smem,
+                                                unsigned long long* wst) {
+  constexpr int W = KVF32 ? 2 : 1;          // 16-byte words per 8 cache elements
+  // sub-chunks whose operands are loaded together (bounded by registers)
+  constexpr int NPF = KVF32 ? (MAXRT == 1 ? 2 : 1) : (MAXRT == 1 ? 4 : 2);
   const int D = P.D, H = D / 2, KDC = D / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  Ctl* C = ctl(smem, (size_t)P.lds_bytes);
   const int R = P.m * P.G;
   const int RT = (R + 15) >> 4;
   const int T = P.L + P.m;
@@ -764,181 +843,273 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, unsign
   float* alpha = lrun + RT * 16;
   const int n_items = P.Hkv * P.n_groups;
   const int DTW = D / 16 / kWaves;   // value tiles (16 d) per wave: 1 or 2
+  const int key = 16 * wave + (lane & 15);   // this lane's key within a sub-chunk (scores)
+  const int kq = 8 * (lane >> 4);            // first of this lane's 8 k in a 32-k chunk
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int g = item / P.n_groups, grp = item % P.n_groups;
     const int gt0 = grp * kGroupPos;
-    // ---- Q fragments (rotated, scaled, hi/lo); padding rows are zero
-    for (int i = tid; i < RT * 16 * (D / 8); i += kThreads) {
-      const int r = i / (D / 8), dg = i % (D / 8);
-      const int d0 = dg * 8;
-      float v[8];
-      if (r < R) {
-        const int j = r / P.G, h = g * P.G + r % P.G;
-        const float* qrow = P.qkv + (long long)j * P.ldqkv + h * D;
-        const int pos = P.L + j;
-        const int i0 = d0 < H ? d0 : d0 - H;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float cs = P.rope_cs[((long long)pos * H + i0 + e) * 2 + 0];
-          const float sn = P.rope_cs[((long long)pos * H + i0 + e) * 2 + 1];
-          const float a = qrow[i0 + e], b = qrow[i0 + e + H];
-          v[e] = (d0 < H ? (a * cs - b * sn) : (b * cs + a * sn)) * P.attn_scale;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.f;
-      }
-      u4 hi, lo;
-      split8(v, hi, lo);
-      const int rt = r >> 4, kc = d0 >> 5, ln = (r & 15) + 16 * ((d0 & 31) >> 3);
-      Qf[((rt * KDC + kc) * 2 + 0) * 64 + ln] = hi;
-      Qf[((rt * KDC + kc) * 2 + 1) * 64 + ln] = lo;
-    }
-    for (int r = tid; r < RT * 16; r += kThreads) {
-      mrun[r] = -INFINITY;
-      lrun[r] = 0.f;
-    }
     // ---- new positions of the block inside this group -> cache
     const int n0 = max(P.L, gt0), n1 = min(T, gt0 + kGroupPos);
     if (n0 < n1) {
-      for (int i = tid; i < (n1 - n0) * D; i += kThreads) {
-        const int t = n0 + i / D, d = i % D;
-        const int j = t - P.L;
-        const int phys = P.page_table[t / kPage];
-        const long long kb = (((long long)phys * P.Hkv + g) * 2 + 0) * kPage * D;
-        const long long vb = kb + (long long)kPage * D;
-        const float* krow = P.qkv + (long long)j * P.ldqkv + (P.Hq + g) * D;
-        const float* vrow = P.qkv + (long long)j * P.ldqkv + (P.Hq + P.Hkv + g) * D;
-        const int ii = d < H ? d : d - H;
-        const float cs = P.rope_cs[((long long)t * H + ii) * 2 + 0];
-        const float sn = P.rope_cs[((long long)t * H + ii) * 2 + 1];
-        const float a = krow[ii], b = krow[ii + H];
-        kv_st<KVF32>(kv, kb + (long long)(t % kPage) * D + d, d < H ? (a * cs - b * sn) : (b * cs + a * sn));
-        kv_st<KVF32>(kv, vb + (long long)d * kPage + (t % kPage), vrow[d]);
+      // inputs of every element this thread writes are loaded first (the
+      // cache stores could otherwise alias the next element's loads)
+      constexpr int NE = (kMaxRows * 128 + kThreads - 1) / kThreads;   // elements per thread at most
+      float kv_k[NE], kv_v[NE];
+#pragma unroll
+      for (int q = 0; q < NE; ++q) {
+        const int i = tid + q * kThreads;
+        kv_k[q] = kv_v[q] = 0.f;
+        if (i < (n1 - n0) * D) {
+          const int t = n0 + i / D, d = i % D;
+          const int j = t - P.L;
+          const float* krow = P.qkv + (long long)j * P.ldqkv + (P.Hq + g) * D;
+          const int ii = d < H ? d : d - H;
+          const float cs = P.rope_cs[((long long)t * H + ii) * 2 + 0];
+          const float sn = P.rope_cs[((long long)t * H + ii) * 2 + 1];
+          const float a = krow[ii], b = krow[ii + H];
+          kv_k[q] = d < H ? (a * cs - b * sn) : (b * cs + a * sn);
+          kv_v[q] = P.qkv[(long long)j * P.ldqkv + (P.Hq + P.Hkv + g) * D + d];
+        }
       }
-      // the writes must be visible to this workgroup's operand loads below
+#pragma unroll
+      for (int q = 0; q < NE; ++q) {
+        const int i = tid + q * kThreads;
+        if (i < (n1 - n0) * D) {
+          const int t = n0 + i / D, d = i % D;
+          const int phys = P.page_table[t / kPage];
+          const long long kb = (((long long)phys * P.Hkv + g) * 2 + 0) * kPage * D;
+          const long long vb = kb + (long long)kPage * D;
+          kv_st<KVF32>(kv, kb + (long long)(t % kPage) * D + d, kv_k[q]);
+          kv_st<KVF32>(kv, vb + (long long)d * kPage + (t % kPage), kv_v[q]);
+        }
+      }
+      // the writes must be complete before this workgroup's operand loads
+      // below (same L2; no cache here holds these lines yet in this pass)
       release_all_waves();
       __syncthreads();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
-    __syncthreads();
-
-    f32x4 acc[kAttnRT][2];
+    f32x4 acc[MAXRT][2];
 #pragma unroll
-    for (int rt = 0; rt < kAttnRT; ++rt)
+    for (int rt = 0; rt < MAXRT; ++rt)
 #pragma unroll
       for (int q = 0; q < 2; ++q) acc[rt][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int sc = 0; sc < kGroupPages; ++sc) {
-      const int t0 = gt0 + sc * kPage;
-      if (t0 >= T) break;
-      const int nkeys = min(kPage, T - t0);
-      const int phys = P.page_table[t0 / kPage];
-      const long long kb = (((long long)phys * P.Hkv + g) * 2 + 0) * kPage * D;
-      const long long vb = kb + (long long)kPage * D;
-      // operands of this wave: keys 16*wave .. +15 (scores), values of its
-      // d tiles (output)
-      const int key = 16 * wave + (lane & 15);
-      const int kq = 8 * (lane >> 4);
-      u4 kh[4], kl[4], vh[2][2], vl[2][2];
+    bool first = true;
+    for (int sc0 = 0; sc0 < kGroupPages; sc0 += NPF) {
+      if (gt0 + sc0 * kPage >= T) break;
+      // ---- operand words of NPF sub-chunks, loaded together: keys
+      // 16*wave.. of this lane (scores) and values of this wave's d tiles
+      u4 kr[NPF][4 * W], vr[NPF][2][2 * W];
+      int phys[NPF];
 #pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-        if (kc < KDC) kv_operand<KVF32>(kv, kb + (long long)key * D + kc * 32 + kq, key < nkeys, kh[kc], kl[kc]);
+      for (int s = 0; s < NPF; ++s) {
+        const int t0 = gt0 + (sc0 + s) * kPage;
+        phys[s] = t0 < T ? P.page_table[t0 / kPage] : 0;
+      }
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-        if (q < DTW) {
-          const int d = (wave * DTW + q) * 16 + (lane & 15);
-#pragma unroll
-          for (int kc = 0; kc < 2; ++kc)
-            v_operand<KVF32>(kv, vb + (long long)d * kPage + kc * 32 + kq, kc * 32 + kq, nkeys, vh[q][kc], vl[q][kc]);
-        }
-      // ---- scores of this wave's 16 keys for every row tile
-#pragma unroll
-      for (int rt = 0; rt < kAttnRT; ++rt) {
-        if (rt >= RT) break;
-        f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < NPF; ++s) {
+        const int t0 = gt0 + (sc0 + s) * kPage;
+        if (t0 >= T) continue;
+        const long long kb = (((long long)phys[s] * P.Hkv + g) * 2 + 0) * kPage * D;
+        const long long vb = kb + (long long)kPage * D;
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
           if (kc >= KDC) break;
-          const u4 qh = Qf[((rt * KDC + kc) * 2 + 0) * 64 + lane];
-          const u4 ql = Qf[((rt * KDC + kc) * 2 + 1) * 64 + lane];
-          s4 = mfma(qh, kh[kc], s4);
-          s4 = mfma(ql, kh[kc], s4);
-          if constexpr (KVF32) {
-            s4 = mfma(qh, kl[kc], s4);
-            s4 = mfma(ql, kl[kc], s4);
-          }
+          const gu4* src = (const gu4*)(static_cast<const char*>(kv) + (kb + (long long)key * D + kc * 32 + kq) * (KVF32 ? 4 : 2));
+#pragma unroll
+          for (int w = 0; w < W; ++w) kr[s][kc * W + w] = src[w];
         }
-        const int tk = t0 + key;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = rt * 16 + 4 * (lane >> 4) + i;
-          const bool vis = r < R && key < nkeys && tk <= P.L + r / P.G;
-          Ps[r * kPsStride + key] = vis ? s4[i] : -INFINITY;
-        }
-      }
-      __syncthreads();
-      // ---- running softmax per row (a wave per row, a lane per key)
-      for (int r = wave; r < RT * 16; r += kWaves) {
-        const float s = Ps[r * kPsStride + lane];
-        float mc = s;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) mc = fmaxf(mc, __shfl_xor(mc, o, 64));
-        const float mo = mrun[r];
-        const float mn = fmaxf(mo, mc);
-        const float p = (mn == -INFINITY || s == -INFINITY) ? 0.f : expf(s - mn);
-        float sum = p;
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
-        Ps[r * kPsStride + lane] = p;
-        if (lane == 0) {
-          const float al = (mn == -INFINITY) ? 1.f : expf(mo - mn);
-          alpha[r] = al;
-          lrun[r] = lrun[r] * al + sum;
-          mrun[r] = mn;
-        }
-      }
-      __syncthreads();
-      // ---- O = O * alpha + P V for this wave's d tiles
-#pragma unroll
-      for (int rt = 0; rt < kAttnRT; ++rt) {
-        if (rt >= RT) break;
-        u4 ph[2], pl[2];
-#pragma unroll
-        for (int kc = 0; kc < 2; ++kc) {
-          const float* pr = Ps + (rt * 16 + (lane & 15)) * kPsStride + kc * 32 + kq;
-          float v[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = pr[e];
-          split8(v, ph[kc], pl[kc]);
-        }
-        float al[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = alpha[rt * 16 + 4 * (lane >> 4) + i];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           if (q >= DTW) break;
-          f32x4 a4 = acc[rt][q];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) a4[i] *= al[i];
+          const int d = (wave * DTW + q) * 16 + (lane & 15);
 #pragma unroll
           for (int kc = 0; kc < 2; ++kc) {
-            a4 = mfma(ph[kc], vh[q][kc], a4);
-            a4 = mfma(pl[kc], vh[q][kc], a4);
-            if constexpr (KVF32) {
-              a4 = mfma(ph[kc], vl[q][kc], a4);
-              a4 = mfma(pl[kc], vl[q][kc], a4);
-            }
+            const gu4* src = (const gu4*)(static_cast<const char*>(kv) + (vb + (long long)d * kPage + kc * 32 + kq) * (KVF32 ? 4 : 2));
+#pragma unroll
+            for (int w = 0; w < W; ++w) vr[s][q][kc * W + w] = src[w];
           }
-          acc[rt][q] = a4;
         }
       }
-      __syncthreads();
+      if (first) {
+        // ---- Q fragments (rotated, scaled, hi/lo); padding rows are zero
+        for (int i = tid; i < RT * 16 * (D / 8); i += kThreads) {
+          const int r = i / (D / 8), dg = i % (D / 8);
+          const int d0 = dg * 8;
+          float v[8];
+          if (r < R) {
+            const int j = r / P.G, h = g * P.G + r % P.G;
+            const float* qrow = P.qkv + (long long)j * P.ldqkv + h * D;
+            const int pos = P.L + j;
+            const int i0 = d0 < H ? d0 : d0 - H;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float cs = P.rope_cs[((long long)pos * H + i0 + e) * 2 + 0];
+              const float sn = P.rope_cs[((long long)pos * H + i0 + e) * 2 + 1];
+              const float a = qrow[i0 + e], b = qrow[i0 + e + H];
+              v[e] = (d0 < H ? (a * cs - b * sn) : (b * cs + a * sn)) * P.attn_scale;
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.f;
+          }
+          u4 hi, lo;
+          split8(v, hi, lo);
+          const int rt = r >> 4, kc = d0 >> 5, ln = (r & 15) + 16 * ((d0 & 31) >> 3);
+          Qf[((rt * KDC + kc) * 2 + 0) * 64 + ln] = hi;
+          Qf[((rt * KDC + kc) * 2 + 1) * 64 + ln] = lo;
+        }
+        for (int r = tid; r < RT * 16; r += kThreads) {
+          mrun[r] = -INFINITY;
+          lrun[r] = 0.f;
+        }
+        __syncthreads();
+        first = false;
+        wstamp(wst, 1);
+      }
+#pragma unroll
+      for (int s = 0; s < NPF; ++s) {
+        const int t0 = gt0 + (sc0 + s) * kPage;
+        if (t0 >= T) break;
+        const int nkeys = min(kPage, T - t0);
+        // ---- scores of this wave's 16 keys for every row tile
+        u4 kh[4], kl[4];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          if (kc >= KDC) break;
+          if constexpr (KVF32) {
+            const u4 a = kr[s][kc * 2], b = kr[s][kc * 2 + 1];
+            float v[8] = {__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3]),
+                          __uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3])};
+            if (key >= nkeys)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v[e] = 0.f;
+            split8(v, kh[kc], kl[kc]);
+          } else {
+            kh[kc] = key < nkeys ? kr[s][kc] : u4{0u, 0u, 0u, 0u};
+          }
+        }
+#pragma unroll
+        for (int rt = 0; rt < MAXRT; ++rt) {
+          if (rt >= RT) break;
+          f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < 4; ++kc) {
+            if (kc >= KDC) break;
+            const u4 qh = Qf[((rt * KDC + kc) * 2 + 0) * 64 + lane];
+            const u4 ql = Qf[((rt * KDC + kc) * 2 + 1) * 64 + lane];
+            s4 = mfma(qh, kh[kc], s4);
+            s4 = mfma(ql, kh[kc], s4);
+            if constexpr (KVF32) {
+              s4 = mfma(qh, kl[kc], s4);
+              s4 = mfma(ql, kl[kc], s4);
+            }
+          }
+          const int tk = t0 + key;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = rt * 16 + 4 * (lane >> 4) + i;
+            const bool vis = r < R && key < nkeys && tk <= P.L + r / P.G;
+            Ps[r * kPsStride + key] = vis ? s4[i] : -INFINITY;
+          }
+        }
+        __syncthreads();
+        // ---- running softmax per row: 16 threads per row, 4 keys each
+        // (the summation order is the same for any number of rows)
+        for (int r = tid >> 4; r < RT * 16; r += kThreads / 16) {
+          const int k0 = (tid & 15) * 4;
+          float sv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sv[e] = Ps[r * kPsStride + k0 + e];
+          float mc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) mc = fmaxf(mc, __shfl_xor(mc, o, 64));
+          const float mo = mrun[r];
+          const float mn = fmaxf(mo, mc);
+          float sum = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p = (mn == -INFINITY || sv[e] == -INFINITY) ? 0.f : expf(sv[e] - mn);
+            Ps[r * kPsStride + k0 + e] = p;
+            sum += p;
+          }
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
+          if ((tid & 15) == 0) {
+            const float al = (mn == -INFINITY) ? 1.f : expf(mo - mn);
+            alpha[r] = al;
+            lrun[r] = lrun[r] * al + sum;
+            mrun[r] = mn;
+          }
+        }
+        __syncthreads();
+        // ---- O = O * alpha + P V for this wave's d tiles
+        u4 vh[2][2], vl[2][2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          if (q >= DTW) break;
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc) {
+            const int p0 = kc * 32 + kq;   // first position of this lane's 8
+            if constexpr (KVF32) {
+              const u4 a = vr[s][q][kc * 2], b = vr[s][q][kc * 2 + 1];
+              float v[8] = {__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3]),
+                            __uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3])};
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (p0 + e >= nkeys) v[e] = 0.f;
+              split8(v, vh[q][kc], vl[q][kc]);
+            } else {
+              u4 w = vr[s][q][kc];
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                if (p0 + 2 * c >= nkeys) w[c] &= 0xFFFF0000u;
+                if (p0 + 2 * c + 1 >= nkeys) w[c] &= 0x0000FFFFu;
+              }
+              vh[q][kc] = w;
+            }
+          }
+        }
+#pragma unroll
+        for (int rt = 0; rt < MAXRT; ++rt) {
+          if (rt >= RT) break;
+          u4 ph[2], pl[2];
+#pragma unroll
+          for (int kc = 0; kc < 2; ++kc) {
+            const float* pr = Ps + (rt * 16 + (lane & 15)) * kPsStride + kc * 32 + kq;
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = pr[e];
+            split8(v, ph[kc], pl[kc]);
+          }
+          float al[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) al[i] = alpha[rt * 16 + 4 * (lane >> 4) + i];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            if (q >= DTW) break;
+            f32x4 a4 = acc[rt][q];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a4[i] *= al[i];
+#pragma unroll
+            for (int kc = 0; kc < 2; ++kc) {
+              a4 = mfma(ph[kc], vh[q][kc], a4);
+              a4 = mfma(pl[kc], vh[q][kc], a4);
+              if constexpr (KVF32) {
+                a4 = mfma(ph[kc], vl[q][kc], a4);
+                a4 = mfma(pl[kc], vl[q][kc], a4);
+              }
+            }
+            acc[rt][q] = a4;
+          }
+        }
+        __syncthreads();
+      }
     }
+    wstamp(wst, 2);
     // ---- per-row partials of this group
     const long long ib = ((long long)g * P.n_groups + grp) * R;
 #pragma unroll
-    for (int rt = 0; rt < kAttnRT; ++rt) {
+    for (int rt = 0; rt < MAXRT; ++rt) {
       if (rt >= RT) break;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
@@ -947,60 +1118,40 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, unsign
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = rt * 16 + 4 * (lane >> 4) + i;
-          if (r < R) P.pacc[(ib + r) * D + d] = acc[rt][q][i];
+          if (r < R) cst(P.pacc + (ib + r) * D + d, acc[rt][q][i]);
         }
       }
     }
     for (int r = tid; r < R; r += kThreads) {
-      P.pm[ib + r] = mrun[r];
-      P.ps[ib + r] = lrun[r];
+      cst(P.pm + ib + r, mrun[r]);
+      cst(P.ps + ib + r, lrun[r]);
+    }
+    if (P.attn_inline) {
+      // the last group of head g to finish merges the head's groups
+      release_all_waves();
+      __syncthreads();
+      if (tid == 0) {
+        const unsigned old = __hip_atomic_fetch_add(P.attn_tickets + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old == (unsigned)(P.n_groups - 1);
+        if (last) __hip_atomic_store(P.attn_tickets + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        C->misc[0] = last ? 1 : 0;   // the partials are then read with agent-scope loads
+      }
+      __syncthreads();
+      if (C->misc[0]) attn_merge_head(P, g, smem);
     }
     __syncthreads();
   }
 }
 
-// o[r][d] = sum_grp f_grp acc_grp / sum_grp f_grp l_grp with
-// f_grp = exp(m_grp - max m), groups in ascending order; one output element
-// per thread, written into the O projection's A operand.
+// The merge as a phase of its own (heads with many groups or rows): one
+// output element per thread over the whole grid.
 __device__ __forceinline__ void attn_merge_phase(const PassP& P) {
-  const int D = P.D, R = P.m * P.G, NG = P.n_groups;
+  const int D = P.D, R = P.m * P.G;
   const long long total = (long long)P.Hkv * R * D;
-  constexpr int B = 8;   // groups in flight per thread
   for (long long e = (long long)blockIdx.x * kThreads + threadIdx.x; e < total; e += (long long)gridDim.x * kThreads) {
     const int d = (int)(e % D);
     const long long gr = e / D;
-    const int r = (int)(gr % R), g = (int)(gr / R);
-    const long long base = (long long)g * NG * R + r;   // (g, grp, r) at base + grp * R
-    float M = -INFINITY;
-    for (int c0 = 0; c0 < NG; c0 += B) {
-      float v[B];
-#pragma unroll
-      for (int q = 0; q < B; ++q) v[q] = c0 + q < NG ? P.pm[base + (long long)(c0 + q) * R] : -INFINITY;
-#pragma unroll
-      for (int q = 0; q < B; ++q) M = fmaxf(M, v[q]);
-    }
-    float S = 0.f, A = 0.f;
-    for (int c0 = 0; c0 < NG; c0 += B) {
-      float vm[B], vs[B], va[B];
-#pragma unroll
-      for (int q = 0; q < B; ++q) {
-        const bool ok = c0 + q < NG;
-        const long long pi = base + (long long)(c0 + q) * R;
-        vm[q] = ok ? P.pm[pi] : -INFINITY;
-        vs[q] = ok ? P.ps[pi] : 0.f;
-        va[q] = ok ? P.pacc[pi * D + d] : 0.f;
-      }
-#pragma unroll
-      for (int q = 0; q < B; ++q) {
-        if (c0 + q < NG) {
-          const float f = vm[q] == -INFINITY ? 0.f : expf(vm[q] - M);
-          S += f * vs[q];
-          A += f * va[q];
-        }
-      }
-    }
-    const int j = r / P.G, h = g * P.G + r % P.G;
-    afrag_put(P.a_o, j, h * D + d, A / S);
+    attn_merge_store(P, (int)(gr / R), (int)(gr % R), d);
   }
 }
 
@@ -1074,19 +1225,19 @@ __device__ __forceinline__ void route_block(const PassP& P, const float* bias, u
     int* rec = P.route;
     const int E = P.E, K = P.top_k;
     if (tid == 0) {
-      rec[0] = C->uc;
+      cst(rec, C->uc);
       if (P.union_hist) P.union_hist[layer] = C->uc;
     }
     for (int e = tid; e < E; e += kThreads) {
-      rec[1 + e] = e < C->uc ? C->ulist[e] : -1;
+      cst(rec + 1 + e, e < C->uc ? C->ulist[e] : -1);
       int s = -1;
       for (int q = 0; q < C->uc; ++q)
         if (C->ulist[q] == e) s = q;
-      rec[1 + E + e] = s;
+      cst(rec + 1 + E + e, s);
     }
     for (int i = tid; i < P.m * K; i += kThreads) {
-      rec[1 + 2 * E + i] = sel[i];
-      reinterpret_cast<float*>(rec)[1 + 2 * E + 16 * K + i] = selw[i];
+      cst(rec + 1 + 2 * E + i, sel[i]);
+      cst(reinterpret_cast<float*>(rec) + 1 + 2 * E + 16 * K + i, selw[i]);
     }
   }
   __syncthreads();
@@ -1115,21 +1266,21 @@ __device__ __forceinline__ void moe_combine_phase(const PassP& P, const float* n
       }
       for (int s = 0; s < P.n_shared; ++s) y += P.ey[(long long)(uc + s) * P.ey_slot + (long long)row * P.ldy + col];
       v = P.x[(long long)row * P.ldx + col] + y;
-      P.x[(long long)row * P.ldx + col] = v;
+      cst(P.x + (long long)row * P.ldx + col, v);
       if (trace) trace[(long long)row * P.d + col] = v;
     }
     if (col < P.d) afrag_put(P.a_norm, row, col, v * next_gain[col]);
     float sq = v * v;
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o, 64);
-    if (cl == 0 && row < P.m) P.ss[row * P.n_ss + tile] = sq;
+    if (cl == 0 && row < P.m) cst(P.ss + row * P.n_ss + tile, sq);
   }
 }
 
 // ------------------------------------------------------------ the pass
-__device__ __forceinline__ void stamp(const PassP& P, int& k) {
-  if (P.stamps && blockIdx.x == 0 && threadIdx.x == 0) P.stamps[k] = wall_clock64();
-  ++k;
+// start of phase ph (after its barrier), taken by workgroup 0
+__device__ __forceinline__ void stamp(const PassP& P, int ph) {
+  if (P.stamps && blockIdx.x == 0 && threadIdx.x == 0) P.stamps[ph] = wall_clock64();
 }
 
 
@@ -1143,8 +1294,6 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
   Ctl* C = ctl(smem, (size_t)P.lds_bytes);
   GridBar gb{P.bar, P.bar_base, P.err, false};
   Ring ring;
-  int sk = 0;
-  stamp(P, sk);
   for (int ph = 0; ph < P.n_prog; ++ph) {
     // local copy: loop-invariant phase fields stay in registers (the phase's
     // own stores could otherwise alias the descriptor in memory)
@@ -1162,13 +1311,16 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
     // streaming phase issues its first weight batch during that barrier;
     // the ring is written right before every phase that reads it, so it is
     // dead (and its registers free) in the other phases.
+    unsigned long long* wst = P.wstamps ? P.wstamps + ((long long)ph * gridDim.x + blockIdx.x) * 4 : nullptr;
     auto sync = [&](auto&& prefetch) {
       if (ph > 0) {
+        wstamp(wst ? wst - (long long)gridDim.x * 4 : nullptr, 3);   // end of the previous phase's work
         grid_sync(gb, prefetch);
-        stamp(P, sk);
       } else {
         prefetch();
       }
+      stamp(P, ph);
+      wstamp(wst, 0);
     };
     switch (kind) {
       case PH_EMBED:
@@ -1178,12 +1330,12 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
       case PH_STORE: {
         const SlotMap sm = d->slot_mode ? slots : dense;
         sync([&] { gemm_prefetch<WF, 1>(d->M, sm, d->slot_mode == 2, ring); });
-        gemm_phase<WF, EPI_STORE, 1>(P, d->M, io, sm, d->slot_mode == 2, ring, smem);
+        gemm_phase<WF, EPI_STORE, 1>(P, d->M, io, sm, d->slot_mode == 2, ring, smem, wst);
         break;
       }
       case PH_RESID:
         sync([&] { gemm_prefetch<WF, 1>(d->M, dense, false, ring); });
-        gemm_phase<WF, EPI_RESID, 1>(P, d->M, io, dense, false, ring, smem);
+        gemm_phase<WF, EPI_RESID, 1>(P, d->M, io, dense, false, ring, smem, wst);
         break;
       case PH_ROUTE_SWIGLU:
         sync([] {});
@@ -1191,22 +1343,34 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
         route_block(P, d->bias, smem, d->layer);
         const SlotMap routed{C->ulist, C->uc, P.E, C->uc + P.n_shared};   // the union just built
         gemm_prefetch<WF, 2>(d->M, routed, false, ring);
-        gemm_phase<WF, EPI_SWIGLU, 2>(P, d->M, io, routed, false, ring, smem);
+        gemm_phase<WF, EPI_SWIGLU, 2>(P, d->M, io, routed, false, ring, smem, wst);
         break;
       }
       case PH_SWIGLU:
         sync([&] { gemm_prefetch<WF, 2>(d->M, dense, false, ring); });
-        gemm_phase<WF, EPI_SWIGLU, 2>(P, d->M, io, dense, false, ring, smem);
+        gemm_phase<WF, EPI_SWIGLU, 2>(P, d->M, io, dense, false, ring, smem, wst);
         break;
       case PH_LOGITS:
         sync([&] { gemm_prefetch<WF, 1>(d->M, dense, false, ring); });
-        gemm_phase<WF, EPI_LOGITS, 1>(P, d->M, io, dense, false, ring, smem);
+        gemm_phase<WF, EPI_LOGITS, 1>(P, d->M, io, dense, false, ring, smem, wst);
         break;
       case PH_ATTN:
         sync([] {});
-        attention_phase<WF == W_F32>(P, d->kv, smem);
+        wstamp(wst, 1);
+        wstamp(wst, 2);
+        if (P.m * P.G <= 16) attention_phase<WF == W_F32, 1>(P, d->kv, smem, wst);
+        else attention_phase<WF == W_F32, kAttnRT>(P, d->kv, smem, wst);
         break;
       case PH_ATTN_MERGE:
+        if (P.attn_inline) {
+          // merged by attention's last arrivers: no barrier, an empty phase
+          stamp(P, ph);
+          if (wst) {
+            wstamp(wst - (long long)gridDim.x * 4, 3);   // end of the attention's work
+            for (int i = 0; i < 3; ++i) wstamp(wst, i);  // (its end comes with the next phase)
+          }
+          break;
+        }
         sync([] {});
         attn_merge_phase(P);
         break;
@@ -1219,10 +1383,11 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
         break;
     }
   }
+  if (P.wstamps) wstamp(P.wstamps + ((long long)(P.n_prog - 1) * gridDim.x + blockIdx.x) * 4, 3);
 }
 
 size_t pass_lds_bytes(int wfmt, int max_rows_attn, int D) {
-  const size_t gemm = 2 * (size_t)kAWindowBytes;
+  const size_t gemm = (size_t)kAWindowBytes;
   const size_t attn = attn_lds_bytes((max_rows_attn + 15) / 16, D);
   const size_t route = 4 * (256 + 16 * 16 * 2);
   size_t b = gemm > attn ? gemm : attn;

@@ -71,24 +71,12 @@ bool check_gemm_walk(const GemmShape& s, int G, size_t ws_floats, size_t n_ticke
         const long long src = (long long)key * s.a_slot + (long long)win * L.W * ACH * 128;
         return n16 * 16 <= kAWindowBytes && src >= 0 && src + n16 <= s.a_size;
       };
-      int sk0 = -1, sw0 = -1, sk1 = -1, sw1 = -1;
+      int sk = -1, sw = -1;   // the staged (key, window)
       {
-        const Cur a = cur_at(L, u0), b = cur_at(L, u1 - 1);
-        const int ka = s.slot_major ? a.slot : 0, kb = s.slot_major ? b.slot : 0;
-        sk0 = ka;
-        sw0 = a.win;
-        if (!stage_ok(ka, a.win)) return fail("first A window out of bounds");
-        if (ka != kb || a.win != b.win) {
-          int ns = ka, nw = a.win;
-          if (s.slot_major) {
-            if (++nw == L.n_win) { nw = 0; ++ns; }
-          } else {
-            ++nw;
-          }
-          sk1 = ns;
-          sw1 = nw;
-          if (!stage_ok(ns, nw)) return fail("second A window out of bounds");
-        }
+        const Cur a = cur_at(L, u0);
+        sk = s.slot_major ? a.slot : 0;
+        sw = a.win;
+        if (!stage_ok(sk, sw)) return fail("first A window out of bounds");
       }
       // ---- load cursor (the first batch is issued before the phase)
       std::vector<Batch> loads;
@@ -117,14 +105,13 @@ bool check_gemm_walk(const GemmShape& s, int G, size_t ws_floats, size_t n_ticke
       if (!load()) return fail("first weight batch out of bounds");
       // ---- compute cursor
       Cur cc = cur_at(L, u0);
-      int wi = 0, pend = 0;
+      int pend = 0;
       size_t next = 0;
       for (;;) {
         const int nch = seg_left(cc, u1);
         if (nch < 1) return fail("empty segment");
         const int key = s.slot_major ? cc.slot : 0;
-        const bool in_slot = (wi & 1) ? (key == sk1 && cc.win == sw1) : (key == sk0 && cc.win == sw0);
-        if (!in_slot) return fail("segment computed against a different A window");
+        if (key != sk || cc.win != sw) return fail("segment computed against a different A window");
         for (int c0 = 0; c0 < nch; c0 += U) {
           const int n = std::min(U, nch - c0);
           if ((cc.c + c0 + n) > L.wlen(cc.win)) return fail("A chunk past the staged window");
@@ -156,13 +143,10 @@ bool check_gemm_walk(const GemmShape& s, int G, size_t ws_floats, size_t n_ticke
         if (cc.u >= u1) break;
         seg_advance(L, cc);
         const int nkey = s.slot_major ? cc.slot : 0;
-        const bool same = (wi & 1) ? (nkey == sk1 && cc.win == sw1) : (nkey == sk0 && cc.win == sw0);
-        if (!same) {
-          ++wi;
-          if (wi >= 2) {
-            if (wi & 1) { sk1 = nkey; sw1 = cc.win; } else { sk0 = nkey; sw0 = cc.win; }
-            if (!stage_ok(nkey, cc.win)) return fail("restaged A window out of bounds");
-          }
+        if (nkey != sk || cc.win != sw) {   // restage
+          sk = nkey;
+          sw = cc.win;
+          if (!stage_ok(sk, sw)) return fail("restaged A window out of bounds");
         }
       }
       if (next != loads.size() || !ldone) return fail("loads left over at the end of the range");

@@ -72,6 +72,7 @@ struct spec_verify {
   int* route = nullptr;
   float* ws = nullptr;
   unsigned* tickets = nullptr;
+  unsigned* attn_tickets = nullptr;
   unsigned long long* bar = nullptr;
   unsigned long long bar_gen = 0;
   int* tokens_dev = nullptr;
@@ -83,6 +84,7 @@ struct spec_verify {
   int n_prog = 0;
   std::vector<int> prog_cls;    // profiling class of each phase
   std::vector<int> prog_layer;  // layer of each phase (-1: none)
+  std::vector<int> prog_kind;   // PhKind of each phase
   std::vector<double> prog_bytes_fixed;   // weight bytes of each phase (MoE experts: per expert)
   std::vector<void*> allocs;
   // state
@@ -94,6 +96,9 @@ struct spec_verify {
   hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
   unsigned long long* stamps_dev = nullptr;
   std::vector<unsigned long long> stamps_host;
+  unsigned long long* wstamps_dev = nullptr;    // [n_prog][n_wg][4]
+  std::vector<unsigned long long> wstamps_host;
+  double prof_detail[SPEC_K_NCLASSES][8] = {};
   int* union_dev_prof = nullptr;
   int64_t prof_launches[SPEC_K_NCLASSES] = {};
   double prof_ms[SPEC_K_NCLASSES] = {};
@@ -169,8 +174,8 @@ bool check_cfg(const spec_config* c, std::string& msg) {
   if (c->max_k < 0 || c->max_k > 15) return bad("max_k must be in [0, 15]");
   if (c->max_ctx < 1 || c->max_ctx > (1 << 22)) return bad("max_ctx out of range");
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return bad("rope_theta must be > 0 and rms_eps >= 0");
-  if (c->gemm_k_split < 0 || c->gemm_k_split % 128 != 0 || c->gemm_k_split > 1024)
-    return bad("gemm_k_split must be a multiple of 128 in [0, 1024]");
+  if (c->gemm_k_split < 0 || c->gemm_k_split % 128 != 0 || c->gemm_k_split > 2048)
+    return bad("gemm_k_split must be a multiple of 128 in [0, 2048]");
   for (int i = 0; i < 7; ++i)
     if (c->reserved[i] != 0) return bad("reserved fields must be zero");
   const bool moe = c->n_experts > 0;
@@ -211,7 +216,7 @@ bool build_plan(const spec_config& c, int wf, int G, PassPlan& P, std::string& e
   const int d = c.d_model, Hq = c.n_q_heads, Hkv = c.n_kv_heads, D = c.head_dim, V = c.vocab;
   const bool moe = c.n_experts > 0;
   const int E = c.n_experts, S = c.n_shared, F = moe ? c.d_ff_expert : c.d_ff;
-  const int window_k = c.gemm_k_split > 0 ? c.gemm_k_split : 1024;
+  const int window_k = c.gemm_k_split > 0 ? c.gemm_k_split : 2048;
   const int n_slots_max = moe ? E + S : 1;
   P.a_norm = (long long)cdiv(d, 32) * 128;
   P.a_o = (long long)cdiv(Hq * D, 32) * 128;
@@ -433,6 +438,10 @@ bool check_tensors(const spec_config& c, const spec_tensor* t, int n, std::strin
   return true;
 }
 
+bool prog_kind_is_gemm(int kind) {
+  return kind == PH_STORE || kind == PH_RESID || kind == PH_SWIGLU || kind == PH_LOGITS || kind == PH_ROUTE_SWIGLU;
+}
+
 Phase gemm_phase_desc(int kind, int layer, const HostMat& H) {
   Phase p{};
   p.kind = kind;
@@ -591,6 +600,7 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   if ((rc = dalloc_z(h, &h->pacc, Hkv * max_groups * Rmax * D))) return rc;
   if ((rc = dalloc_z(h, &h->ws, plan.ws_floats))) return rc;
   if ((rc = dalloc_z(h, &h->tickets, plan.n_tickets))) return rc;
+  if ((rc = dalloc_z(h, &h->attn_tickets, (size_t)Hkv + 16))) return rc;
   if ((rc = dalloc_z(h, &h->bar, 512))) return rc;
   if ((rc = dalloc_z(h, &h->tokens_dev, 16))) return rc;
   if ((rc = dalloc_z(h, &h->result_dev, 4))) return rc;
@@ -663,17 +673,22 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   h->n_prog = (int)prog.size();
   for (int i = h->n_prog - 1, nx = h->n_prog; i >= 0; --i) {
     prog[i].next_gemm = nx;
-    const int kd = prog[i].kind;
-    if (kd == PH_STORE || kd == PH_RESID || kd == PH_SWIGLU || kd == PH_LOGITS || kd == PH_ROUTE_SWIGLU) nx = i;
+    if (prog_kind_is_gemm(prog[i].kind)) nx = i;
   }
   h->prog_layer.clear();
-  for (const Phase& q : prog) h->prog_layer.push_back(q.layer);
+  h->prog_kind.clear();
+  for (const Phase& q : prog) {
+    h->prog_layer.push_back(q.layer);
+    h->prog_kind.push_back(q.kind);
+  }
   h->prog_cls = cls;
   h->prog_bytes_fixed = wbytes;
   if ((rc = dalloc_t(h, &h->prog, prog.size()))) return rc;
   HIPCHK(hipMemcpy(h->prog, prog.data(), prog.size() * sizeof(Phase), hipMemcpyHostToDevice));
   if ((rc = dalloc_z(h, &h->stamps_dev, (size_t)h->n_prog + 4))) return rc;
   h->stamps_host.assign((size_t)h->n_prog + 4, 0);
+  if ((rc = dalloc_z(h, &h->wstamps_dev, (size_t)h->n_prog * h->n_wg * 4))) return rc;
+  h->wstamps_host.assign((size_t)h->n_prog * h->n_wg * 4, 0);
   for (auto& e : h->ev) HIPCHK(hipEventCreate(&e));
 
   // the staging buffer is no longer needed
@@ -755,6 +770,10 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   p.D = c.head_dim; p.V = c.vocab; p.G = c.n_q_heads / c.n_kv_heads; p.E = c.n_experts; p.top_k = c.top_k;
   p.n_shared = c.n_shared; p.F = moe ? c.d_ff_expert : c.d_ff;
   p.n_groups = cdiv(L + m, kGroupPos);
+  // heads whose merge is small are merged by their last attention item;
+  // the merge phases (one per layer) then run without a barrier
+  p.attn_inline = (long long)m * p.G * c.head_dim * p.n_groups <= kInlineMergeElems ? 1 : 0;
+  p.attn_tickets = h->attn_tickets;
   p.n_ss = h->n_ss;
   p.lds_bytes = (int)h->lds;
   p.eps = c.rms_eps;
@@ -774,6 +793,7 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   p.bar = h->bar; p.bar_base = h->bar_gen; p.err = h->result_dev + 3;
   p.trace = trace_dev; p.union_hist = union_rec;
   p.stamps = h->profiling ? h->stamps_dev : nullptr;
+  p.wstamps = h->profiling ? h->wstamps_dev : nullptr;
 
   if (he == hipSuccess && h->profiling) he = hipEventRecord(h->ev[0], h->stream);
   if (he == hipSuccess) he = launch_pass(h->wfmt, p, h->n_wg, h->lds, h->stream);
@@ -781,7 +801,7 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
     h->broken = true;
     return fail(h, SPEC_EHIP, std::string("pass launch: ") + hipGetErrorString(he));
   }
-  h->bar_gen += (unsigned long long)(h->n_prog - 1);
+  h->bar_gen += (unsigned long long)(h->n_prog - 1 - (p.attn_inline ? c.n_layers : 0));
   if (h->profiling) he = hipEventRecord(h->ev[1], h->stream);
   AcceptParams a{};
   a.k = k; a.V = c.vocab; a.L = L; a.mode = mode; a.n_stat = h->n_stat;
@@ -799,6 +819,9 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
                           hipMemcpyDeviceToDevice, h->stream);
   if (he == hipSuccess && h->profiling)
     he = hipMemcpyAsync(h->stamps_host.data(), h->stamps_dev, sizeof(unsigned long long) * h->n_prog,
+                        hipMemcpyDeviceToHost, h->stream);
+  if (he == hipSuccess && h->profiling)
+    he = hipMemcpyAsync(h->wstamps_host.data(), h->wstamps_dev, sizeof(unsigned long long) * h->wstamps_host.size(),
                         hipMemcpyDeviceToHost, h->stream);
   std::vector<int> uh;
   if (he == hipSuccess && h->profiling && moe) {
@@ -832,6 +855,30 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
       const int layer = std::max(0, h->prog_layer[i]);
       const double b = phase_bytes(h, i, m, L, moe ? uh[layer] : 0);
       const int k2 = h->prog_cls[i];
+      {
+        // per-workgroup split of the phase: A staging, weight stream and
+        // flush (GEMM phases; other phases: all in the third) and the whole
+        // work, each as mean and max over workgroups
+        const unsigned long long* w = h->wstamps_host.data() + (size_t)i * h->n_wg * 4;
+        const bool gemm = prog_kind_is_gemm(h->prog_kind[i]) || h->prog_kind[i] == PH_ATTN;
+        double sum[4] = {0, 0, 0, 0}, mx[4] = {0, 0, 0, 0};
+        for (int g = 0; g < h->n_wg; ++g) {
+          const unsigned long long* q = w + (size_t)g * 4;
+          double v[4];
+          v[0] = gemm ? (double)(q[1] - q[0]) * tick_ms : 0.0;
+          v[1] = gemm ? (double)(q[2] - q[1]) * tick_ms : 0.0;
+          v[2] = gemm ? (double)(q[3] - q[2]) * tick_ms : (double)(q[3] - q[0]) * tick_ms;
+          v[3] = (double)(q[3] - q[0]) * tick_ms;
+          for (int j = 0; j < 4; ++j) {
+            sum[j] += v[j];
+            mx[j] = std::max(mx[j], v[j]);
+          }
+        }
+        for (int j = 0; j < 4; ++j) {
+          h->prof_detail[k2][j] += sum[j] / h->n_wg;
+          h->prof_detail[k2][4 + j] += mx[j];
+        }
+      }
       h->prof_launches[k2] += 1;
       h->prof_ms[k2] += ms;
       h->prof_bytes[k2] += b;
@@ -947,7 +994,15 @@ int spec_profile_enable(spec_verify_t* h, int32_t on) {
     h->prof_launches[i] = 0;
     h->prof_ms[i] = 0;
     h->prof_bytes[i] = 0;
+    for (int j = 0; j < 8; ++j) h->prof_detail[i][j] = 0;
   }
+  return SPEC_OK;
+}
+
+int spec_profile_detail(const spec_verify_t* h, double* out) {
+  if (!h || !out) return SPEC_EINVAL;
+  for (int i = 0; i < SPEC_K_NCLASSES; ++i)
+    for (int j = 0; j < 8; ++j) out[i * 8 + j] = h->prof_detail[i][j];
   return SPEC_OK;
 }
 

@@ -26,8 +26,9 @@ constexpr int kPage = 64;             // KV page (positions); attention sub-chun
 constexpr int kGroupPages = 4;        // pages per attention work item (fixed grid)
 constexpr int kGroupPos = kPage * kGroupPages;
 constexpr int kMaxAttnRows = 128;     // (k+1) * (n_q_heads / n_kv_heads) per KV head
+constexpr long long kInlineMergeElems = 16384;   // rows * head_dim * groups merged by one workgroup
 constexpr int kRing = 32;             // weight fragments per prefetch batch (per wave)
-constexpr int kAWindowBytes = 64 * 1024;   // LDS bytes of one staged A window (two are resident)
+constexpr int kAWindowBytes = 128 * 1024;  // LDS bytes of the staged A window (2048 k of hi/lo rows)
 constexpr int kMaxLds = 160 * 1024;
 
 enum WFmt : int { W_BF16 = 0, W_INT4 = 1, W_F32 = 2 };
@@ -109,6 +110,8 @@ struct PassP {
   int* route;                // MoE routing record (route_words)
   // split-K workspace and tickets
   float* ws; unsigned* tickets;
+  unsigned* attn_tickets;     // [Hkv] groups finished per KV head (inline merge)
+  int attn_inline;           // 1: attention's last arrivers merge, the merge phase is skipped
   // grid barrier
   unsigned long long* bar; unsigned long long bar_base;
   int* err;                  // set to 1 by a grid-barrier wait that ran out
@@ -116,6 +119,7 @@ struct PassP {
   float* trace;              // [n_layers][m][d]
   int* union_hist;           // [n_layers]
   unsigned long long* stamps;   // [n_phases + 1] wall clock at phase ends (workgroup 0)
+  unsigned long long* wstamps;  // [n_phases][n_wg][4] per-workgroup phase stamps (nullable)
 };
 
 struct AcceptParams {

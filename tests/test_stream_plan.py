@@ -39,7 +39,7 @@ def _plan(spec, n_wg, max_k=15, k_split=0, max_ctx=4096):
 
 
 @pytest.mark.parametrize("name", list(synth.ALL_WORKLOADS))
-@pytest.mark.parametrize("k_split", (0, 256))
+@pytest.mark.parametrize("k_split", (0, 256, 1024))
 def test_plan_walk_in_bounds(name, k_split):
     spec = synth.ALL_WORKLOADS[name].spec
     for g in GRIDS:
