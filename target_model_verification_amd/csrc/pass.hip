@@ -212,7 +212,6 @@ struct Ctl {
   float rs[16];                 // RMSNorm row scales of the current phase
   int pend_n;                   // split units this workgroup flushed in the phase
   int pend[kMaxPending];        // split unit blocks flushed: slot << 20 | sg
-  unsigned char last[kMaxPending];   // 1 if this workgroup is the last arriver
   int uc;                       // MoE: union size
   int ulist[256];               // MoE: union (expert ids, ascending)
   int misc[8];
@@ -579,32 +578,39 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
   }
 
   wstamp(wst, 2);
-  // ---- split units: tickets, then the last arriver sums partials in K order
+  // ---- split blocks: every workgroup announces its segments (no waiting),
+  // then reduces the blocks assigned to it (an even share of all blocks),
+  // summing their partials in K order once every segment is in
   release_all_waves();
   __syncthreads();
   const int np = C->pend_n;
-  if (np == 0) return;
-  // one lane per split block: the tickets go out together (every partial of
-  // this workgroup is stored through and complete by now)
   for (int k = threadIdx.x; k < np; k += kThreads) {
     const int s = C->pend[k] >> 20, sg = C->pend[k] & 0xfffff;
+    __hip_atomic_fetch_add(P.tickets + (long long)s * M.n_sg + sg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  const int nb = L.n_slots * M.n_sg;
+  const int b0 = range_begin(nb, g, G), b1 = range_begin(nb, g + 1, G);
+  constexpr int RB = TPU == 1 ? 16 : 8;   // partial loads in flight per lane (a block's usual count)
+  for (int b = b0; b < b1; ++b) {
+    const int s = b / M.n_sg, sg = b - s * M.n_sg;
     int idx, n;
     seg_info(L, s, sg, 0, g, G, idx, n);
-    unsigned* t = P.tickets + (long long)s * M.n_sg + sg;
-    const unsigned old = __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = old == (unsigned)(n - 1);
-    if (last) __hip_atomic_store(t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    C->last[k] = last ? 1 : 0;   // the partials are then read with agent-scope loads
-  }
-  __syncthreads();
-  constexpr int RB = TPU == 1 ? 16 : 8;   // partial loads in flight per lane (a block's usual count)
-  for (int k = 0; k < np; ++k) {
-    if (!C->last[k]) continue;
-    const int s = C->pend[k] >> 20, sg = C->pend[k] & 0xfffff;
+    if (n == 1) continue;   // finished inside the stream
+    if (threadIdx.x == 0) {
+      unsigned* t = P.tickets + b;
+      unsigned spins = 0;
+      while (__hip_atomic_load(t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)n) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins == kSpinLimit) {
+          __hip_atomic_store(P.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+      __hip_atomic_store(t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();   // the partials are read with agent-scope loads
     const int unit = sg * kWaves + wave;
     if (unit >= M.n_units) continue;
-    int idx, n;
-    seg_info(L, s, sg, 0, g, G, idx, n);
     f32x4 sum[TPU];
 #pragma unroll
     for (int t = 0; t < TPU; ++t) sum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -618,7 +624,6 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
           v[q][t] = j0 + q < n ? cld4(p + (long long)(j0 + q) * kWaves * TPU * 256 + t * 256)
                                : f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      // partials are added in K order
 #pragma unroll
       for (int q = 0; q < RB; ++q) {
         if (j0 + q < n) {
