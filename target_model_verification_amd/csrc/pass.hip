@@ -43,8 +43,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u4 gu4;
 typedef __attribute__((address_space(1))) const uint16_t gu16;
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
 
-enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3 };
+enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_QKV = 4 };
 
 // ------------------------------------------------------------ small helpers
 __device__ __forceinline__ uint32_t f2bf(float f) {
@@ -305,10 +307,33 @@ struct GemmIO {
   const float* gain;         // RESID: gain of the next norm
   uint4* a_out; long long a_out_slot;        // RESID / SWIGLU: next A operand
   float* trace;              // RESID: residual copy for this layer (nullable)
+  void* kv;                  // QKV: the layer's cache pages
 };
 
+// Query element (block row j, query head h, dim d), already rotated and
+// scaled, into the attention's MFMA A fragments: per KV head g = h / G,
+// row r = j * G + h % G of row tile r / 16, 32-dim chunk d / 32, hi and lo
+// bf16 parts; lane (r % 16) + 16 * ((d % 32) / 8) holds 8 consecutive dims.
+__device__ __forceinline__ void qfrag_put(const PassP& P, int h, int j, int d, float v) {
+  const int g = h / P.G, r = j * P.G + (h - g * P.G);
+  const int KDC = P.D >> 5;
+  const long long f = (((long long)g * kAttnRT + (r >> 4)) * KDC + (d >> 5)) * 2;   // hi fragment
+  const int ln = (r & 15) + 16 * ((d & 31) >> 3), e = d & 7;
+  uint16_t* q = reinterpret_cast<uint16_t*>(P.qf);
+  const uint32_t hb = f2bf(v);
+  cst16(q + (f * 64 + ln) * 8 + e, (uint16_t)hb);
+  cst16(q + ((f + 1) * 64 + ln) * 8 + e, (uint16_t)f2bf(v - bf2f(hb)));
+}
+
+// one cache element, rounded to the cache dtype
+template <bool KVF32>
+__device__ __forceinline__ void kv_put(void* kv, long long i, float v) {
+  if constexpr (KVF32) cst(static_cast<float*>(kv) + i, v);
+  else cst16(static_cast<uint16_t*>(kv) + i, (uint16_t)f2bf(v));
+}
+
 // Epilogue of one finished unit (one wave, acc[t] = tile t of the unit).
-template <int EPI, int TPU>
+template <int WF, int EPI, int TPU>
 __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const GemmIO& io, const float* rs, int slot,
                                          int unit, f32x4 (&acc)[TPU]) {
   const int lane = threadIdx.x & 63;
@@ -323,18 +348,26 @@ __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const Gem
     }
   } else if constexpr (EPI == EPI_RESID) {
     const int col = unit * kTileN + cl;
+    // every load first (the stores below could alias later loads)
+    float xv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * rg + i;
+      xv[i] = (row < P.m && col < M.N) ? P.x[(long long)row * P.ldx + col] : 0.f;
+    }
+    const float gn = col < M.N ? io.gain[col] : 0.f;
     float sq[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * rg + i;
       float v = 0.f;
       if (row < P.m && col < M.N) {
-        v = P.x[(long long)row * P.ldx + col] + acc[0][i];
+        v = xv[i] + acc[0][i];
         cst(P.x + (long long)row * P.ldx + col, v);
         if (io.trace) io.trace[(long long)row * P.d + col] = v;
       }
       sq[i] = v * v;
-      if (col < M.N) afrag_put(io.a_out, row, col, v * io.gain[col]);
+      if (col < M.N) afrag_put(io.a_out, row, col, v * gn);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -346,6 +379,46 @@ __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const Gem
       for (int i = 0; i < 4; ++i) {
         const int row = 4 * rg + i;
         if (row < P.m) cst(P.ss + row * P.n_ss + unit, sq[i]);
+      }
+    }
+  } else if constexpr (EPI == EPI_QKV) {
+    // RMSNorm row scale, then the rotary embedding of query and key columns
+    // (pairs side by side: the partner is the neighbouring lane); queries,
+    // scaled by 1/sqrt(D), go to the attention's fragments, keys and values
+    // (rounded to the cache dtype) to the cache at positions L .. L+m-1
+    const int col = unit * kTileN + cl;
+    const int D = P.D, H = D >> 1;
+    const int qc = P.Hq * D, kc = P.Hkv * D;
+    const bool rot_col = col < qc + kc;
+    const int c2 = col < qc ? col : (rot_col ? col - qc : col - qc - kc);
+    const int head = c2 / D, p = c2 - head * D, ii = p >> 1, odd = p & 1;
+    // every load first (the stores below could alias later loads)
+    float v[4], pv[4], cs[4], sn[4];
+    long long pg[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * rg + i;
+      v[i] = rs[row] * acc[0][i];
+      pv[i] = __shfl_xor(v[i], 1, 64);
+      const int t = P.L + min(row, P.m - 1);
+      pg[i] = (long long)P.page_table[t / kPage] * P.Hkv;
+      cs[i] = rot_col ? P.rope_cs[((long long)t * H + ii) * 2 + 0] : 0.f;
+      sn[i] = rot_col ? P.rope_cs[((long long)t * H + ii) * 2 + 1] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * rg + i;
+      if (row < P.m && col < M.N) {
+        const int t = P.L + row;
+        if (rot_col) {
+          const float a = odd ? pv[i] : v[i], b = odd ? v[i] : pv[i];   // x[ii], x[ii + H]
+          const float rot = odd ? (b * cs[i] + a * sn[i]) : (a * cs[i] - b * sn[i]);
+          const int dd = ii + odd * H;
+          if (col < qc) qfrag_put(P, head, row, dd, rot * P.attn_scale);
+          else kv_put<WF == W_F32>(io.kv, ((pg[i] + head) * 2 + 0) * kPage * D + (long long)(t % kPage) * D + dd, rot);
+        } else {
+          kv_put<WF == W_F32>(io.kv, ((pg[i] + head) * 2 + 1) * kPage * D + (long long)p * kPage + (t % kPage), v[i]);
+        }
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
@@ -418,26 +491,20 @@ __device__ __forceinline__ void row_scales(const PassP& P, float* rs) {
 }
 
 // Stages the A window of block (slot, win) into LDS window slot `ws`.
+// Stages the A window of block (slot, win) into LDS with direct
+// global-to-LDS loads (lane l of a wave writes its 16 bytes at base + 16 l):
+// every load is in flight at once and no registers are used.  The caller
+// waits (s_waitcnt) and synchronises before reading the window.  The
+// window holds a multiple of 128 words, so each wave's 64-word block lies
+// wholly inside it.
 template <int WF>
 __device__ __forceinline__ void stage_window(const Lin& L, const GemmIO& io, int slot, int win, unsigned char* smem) {
   constexpr int ACH = (WF == W_INT4) ? 4 : 1;
-  constexpr int B = 16;   // loads in flight per thread
-  const int n16 = L.wlen(win) * ACH * 128;    // uint4 to copy
-  const gu4* src = (const gu4*)(io.a + (long long)slot * io.a_slot + (long long)win * L.W * ACH * 128);
-  u4* dst = reinterpret_cast<u4*>(smem);
-  for (int i0 = threadIdx.x; i0 < n16; i0 += kThreads * B) {
-    u4 v[B];
-#pragma unroll
-    for (int q = 0; q < B; ++q) {
-      const int i = i0 + q * kThreads;
-      if (i < n16) v[q] = src[i];
-    }
-#pragma unroll
-    for (int q = 0; q < B; ++q) {
-      const int i = i0 + q * kThreads;
-      if (i < n16) dst[i] = v[q];
-    }
-  }
+  const int n16 = L.wlen(win) * ACH * 128;    // 16-byte words to copy
+  const uint4* src = io.a + (long long)slot * io.a_slot + (long long)win * L.W * ACH * 128;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i0 = wave * 64; i0 < n16; i0 += kThreads)
+    __builtin_amdgcn_global_load_lds((gvoid*)(src + i0 + lane), (lvoid*)(smem + (size_t)i0 * 16), 16, 0, 0);
 }
 
 // One weight-streaming phase over `sm.n_slots` slots (experts) of M.
@@ -453,10 +520,9 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
   const int u0 = range_begin(L.total, g, G), u1 = range_begin(L.total, g + 1, G);
 
   if (threadIdx.x == 0) C->pend_n = 0;
-  if (EPI == EPI_SWIGLU || EPI == EPI_LOGITS || (EPI == EPI_STORE && io.scale)) row_scales(P, C->rs);
-
-  // the A window of the range's first block; a range that crosses into
-  // another (key, window) restages (a few workgroups per phase)
+  // the A window of the range's first block (a range that crosses into
+  // another (key, window) restages: a few workgroups per phase), with the
+  // row scales' loads in flight at the same time
   int sk = -1, sw = -1;
   if (u0 < u1) {
     const Cur a = cur_at(L, u0);
@@ -464,6 +530,8 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     sw = a.win;
     stage_window<WF>(L, io, sk, sw, smem);
   }
+  if (EPI == EPI_SWIGLU || EPI == EPI_LOGITS || EPI == EPI_QKV || (EPI == EPI_STORE && io.scale)) row_scales(P, C->rs);
+  __builtin_amdgcn_s_waitcnt(0);   // the window's direct loads
   __syncthreads();
   wstamp(wst, 1);
   if (u0 >= u1) {
@@ -553,7 +621,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     seg_info(L, cc.slot, cc.sg, cc.win, g, G, idx, nseg);
     if (live) {
       if (nseg == 1) {
-        epilogue<EPI, TPU>(P, M, io, C->rs, cc.slot, cc.sg * kWaves + wave, acc);
+        epilogue<WF, EPI, TPU>(P, M, io, C->rs, cc.slot, cc.sg * kWaves + wave, acc);
       } else {
         float* p = P.ws + ((((long long)cc.slot * M.n_sg + cc.sg) * M.max_seg + idx) * kWaves + wave) * TPU * 256;
 #pragma unroll
@@ -573,6 +641,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
       sk = key;
       sw = cc.win;
       stage_window<WF>(L, io, sk, sw, smem);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
   }
@@ -632,7 +701,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
         }
       }
     }
-    epilogue<EPI, TPU>(P, M, io, C->rs, s, unit, sum);
+    epilogue<WF, EPI, TPU>(P, M, io, C->rs, s, unit, sum);
   }
 }
 
@@ -712,13 +781,14 @@ __device__ __forceinline__ void split8(const float (&v)[8], u4& hi, u4& lo) {
   lo = u4{l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16, l[6] | l[7] << 16};
 }
 
-constexpr int kAttnRT = kMaxAttnRows / 16;   // row tiles at most
 constexpr int kPsStride = kPage + 4;         // floats per score row in LDS
 
 // LDS of the attention phase: Q fragments [RT][D/32][hi|lo][64 lanes],
 // scores / probabilities [RT*16][kPsStride], running max / sum / rescale.
+// (two-pass path; the one-row-tile path needs 16 rows of kGroupPos + 4)
 __host__ __device__ constexpr size_t attn_lds_bytes(int rt, int D) {
-  return (size_t)rt * (D / 32) * 2 * 1024 + (size_t)rt * 16 * kPsStride * 4 + (size_t)3 * rt * 16 * 4;
+  return (size_t)rt * (D / 32) * 2 * 1024 + (size_t)rt * 16 * kPsStride * 4 + (size_t)3 * rt * 16 * 4 +
+         (size_t)16 * (kGroupPos + 4) * 4;
 }
 
 // One output element (row r, dim d) of KV head g: the groups' partials
@@ -829,284 +899,310 @@ __device__ __forceinline__ void attn_merge_head(const PassP& P, int g, unsigned 
   }
 }
 
+// MFMA operand of 8 cache elements from their raw 16-byte word(s): bf16 is
+// the word itself (lo part zero), fp32 is split into hi and lo.
+template <bool KVF32>
+__device__ __forceinline__ void kv_op(const u4* w, u4& hi, u4& lo) {
+  if constexpr (KVF32) {
+    float v[8] = {__uint_as_float(w[0][0]), __uint_as_float(w[0][1]), __uint_as_float(w[0][2]),
+                  __uint_as_float(w[0][3]), __uint_as_float(w[1][0]), __uint_as_float(w[1][1]),
+                  __uint_as_float(w[1][2]), __uint_as_float(w[1][3])};
+    split8(v, hi, lo);
+  } else {
+    hi = w[0];
+    lo = u4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Zeroes cache elements at positions p0 .. p0+7 that lie at or past nvalid.
+template <bool KVF32>
+__device__ __forceinline__ void kv_mask(u4* w, int p0, int nvalid) {
+  if constexpr (KVF32) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (p0 + e >= nvalid) w[e >> 2][e & 3] = 0u;
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (p0 + 2 * c >= nvalid) w[0][c] &= 0xFFFF0000u;
+      if (p0 + 2 * c + 1 >= nvalid) w[0][c] &= 0x0000FFFFu;
+    }
+  }
+}
+
+// Softmax of a group is taken in two passes with one maximum per row over
+// the whole group: p = exp(s - max), l = sum over sub-chunks (in order) of
+// the sub-chunk's sum (16 threads per row, 4 positions each, then a tree),
+// O = sum over sub-chunks and 32-position chunks (in order) of P V.  With
+// bf16 values and one row tile the whole group is scored at once; otherwise
+// scores are recomputed per sub-chunk in the second pass -- the same
+// operations in the same order, so both give identical bits.
 template <bool KVF32, int MAXRT>
 __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, unsigned char* smem,
                                                 unsigned long long* wst) {
-  constexpr int W = KVF32 ? 2 : 1;          // 16-byte words per 8 cache elements
-  // sub-chunks whose operands are loaded together (bounded by registers)
-  constexpr int NPF = KVF32 ? (MAXRT == 1 ? 2 : 1) : (MAXRT == 1 ? 4 : 2);
-  const int D = P.D, H = D / 2, KDC = D / 32;
+  constexpr int W = KVF32 ? 2 : 1;                    // 16-byte words per 8 cache elements
+  constexpr bool ONE = !KVF32 && MAXRT == 1;          // the whole group at once
+  constexpr int NPF = ONE ? kGroupPages : 1;          // sub-chunks whose operands are loaded together
+  const int D = P.D, KDC = D / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   Ctl* C = ctl(smem, (size_t)P.lds_bytes);
   const int R = P.m * P.G;
   const int RT = (R + 15) >> 4;
   const int T = P.L + P.m;
-  u4* Qf = reinterpret_cast<u4*>(smem);                              // [RT][KDC][2][64]
-  float* Ps = reinterpret_cast<float*>(smem + (size_t)RT * KDC * 2 * 1024);   // [RT*16][kPsStride]
-  float* mrun = Ps + RT * 16 * kPsStride;
+  constexpr int PSW = (ONE ? kGroupPos : kPage) + 4;  // floats per score row
+  u4* Qf = reinterpret_cast<u4*>(smem);                              // [RT][KDC][2][64] (two-pass path)
+  float* Ps = reinterpret_cast<float*>(smem + (size_t)RT * KDC * 2 * 1024);   // [RT*16][PSW]
+  float* mrun = Ps + RT * 16 * PSW;
   float* lrun = mrun + RT * 16;
-  float* alpha = lrun + RT * 16;
   const int n_items = P.Hkv * P.n_groups;
-  const int DTW = D / 16 / kWaves;   // value tiles (16 d) per wave: 1 or 2
+  const int DTW = D / 16 / kWaves;           // value tiles (16 d) per wave: 1 or 2
   const int key = 16 * wave + (lane & 15);   // this lane's key within a sub-chunk (scores)
   const int kq = 8 * (lane >> 4);            // first of this lane's 8 k in a 32-k chunk
+  const int srow = tid >> 4, sq = (tid & 15) * 4;   // softmax: row, first of 4 positions
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
     const int g = item / P.n_groups, grp = item % P.n_groups;
     const int gt0 = grp * kGroupPos;
-    // ---- new positions of the block inside this group -> cache
-    const int n0 = max(P.L, gt0), n1 = min(T, gt0 + kGroupPos);
-    if (n0 < n1) {
-      // inputs of every element this thread writes are loaded first (the
-      // cache stores could otherwise alias the next element's loads)
-      constexpr int NE = (kMaxRows * 128 + kThreads - 1) / kThreads;   // elements per thread at most
-      float kv_k[NE], kv_v[NE];
+    const int nsc = min(kGroupPages, (T - gt0 + kPage - 1) / kPage);   // sub-chunks holding positions
+    const gu4* qsrc = (const gu4*)(P.qf + (long long)g * kAttnRT * KDC * 2 * 64);
+    // ---- query fragments: registers (one row tile) or LDS
+    u4 qh[4], ql[4];
+    if constexpr (ONE) {
 #pragma unroll
-      for (int q = 0; q < NE; ++q) {
-        const int i = tid + q * kThreads;
-        kv_k[q] = kv_v[q] = 0.f;
-        if (i < (n1 - n0) * D) {
-          const int t = n0 + i / D, d = i % D;
-          const int j = t - P.L;
-          const float* krow = P.qkv + (long long)j * P.ldqkv + (P.Hq + g) * D;
-          const int ii = d < H ? d : d - H;
-          const float cs = P.rope_cs[((long long)t * H + ii) * 2 + 0];
-          const float sn = P.rope_cs[((long long)t * H + ii) * 2 + 1];
-          const float a = krow[ii], b = krow[ii + H];
-          kv_k[q] = d < H ? (a * cs - b * sn) : (b * cs + a * sn);
-          kv_v[q] = P.qkv[(long long)j * P.ldqkv + (P.Hq + P.Hkv + g) * D + d];
+      for (int kc = 0; kc < 4; ++kc)
+        if (kc < KDC) {
+          qh[kc] = qsrc[(kc * 2 + 0) * 64 + lane];
+          ql[kc] = qsrc[(kc * 2 + 1) * 64 + lane];
         }
-      }
+    } else {
+      constexpr int QB = 8;
+      for (int i0 = tid; i0 < RT * KDC * 2 * 64; i0 += kThreads * QB) {
+        u4 v[QB];
 #pragma unroll
-      for (int q = 0; q < NE; ++q) {
-        const int i = tid + q * kThreads;
-        if (i < (n1 - n0) * D) {
-          const int t = n0 + i / D, d = i % D;
-          const int phys = P.page_table[t / kPage];
-          const long long kb = (((long long)phys * P.Hkv + g) * 2 + 0) * kPage * D;
-          const long long vb = kb + (long long)kPage * D;
-          kv_st<KVF32>(kv, kb + (long long)(t % kPage) * D + d, kv_k[q]);
-          kv_st<KVF32>(kv, vb + (long long)d * kPage + (t % kPage), kv_v[q]);
-        }
+        for (int q = 0; q < QB; ++q)
+          if (i0 + q * kThreads < RT * KDC * 2 * 64) v[q] = qsrc[i0 + q * kThreads];
+#pragma unroll
+        for (int q = 0; q < QB; ++q)
+          if (i0 + q * kThreads < RT * KDC * 2 * 64) Qf[i0 + q * kThreads] = v[q];
       }
-      // the writes must be complete before this workgroup's operand loads
-      // below (same L2; no cache here holds these lines yet in this pass)
-      release_all_waves();
-      __syncthreads();
     }
+    for (int r = tid; r < RT * 16; r += kThreads) {
+      mrun[r] = -INFINITY;
+      lrun[r] = 0.f;
+    }
+    // operand words of one sub-chunk: keys 16*wave.. of this lane (scores)
+    // and values of this wave's d tiles (output)
+    // pages of the group's sub-chunks, looked up together
+    int phys[kGroupPages];
+#pragma unroll
+    for (int sc = 0; sc < kGroupPages; ++sc) phys[sc] = P.page_table[min(gt0 / kPage + sc, (T - 1) / kPage)];
+    auto load_ops = [&](int sc, u4 (&kr)[4 * W], u4 (&vr)[2][2 * W]) {
+      const long long kb = (((long long)phys[sc] * P.Hkv + g) * 2 + 0) * kPage * D;
+      const long long vb = kb + (long long)kPage * D;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        if (kc >= KDC) break;
+        const gu4* src = (const gu4*)(static_cast<const char*>(kv) + (kb + (long long)key * D + kc * 32 + kq) * (KVF32 ? 4 : 2));
+#pragma unroll
+        for (int w = 0; w < W; ++w) kr[kc * W + w] = src[w];
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if (q >= DTW) break;
+        const int d = (wave * DTW + q) * 16 + (lane & 15);
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const gu4* src = (const gu4*)(static_cast<const char*>(kv) + (vb + (long long)d * kPage + kc * 32 + kq) * (KVF32 ? 4 : 2));
+#pragma unroll
+          for (int w = 0; w < W; ++w) vr[q][kc * W + w] = src[w];
+        }
+      }
+    };
+    // scores of this wave's 16 keys of sub-chunk sc for row tile rt, masked
+    auto scores = [&](int sc, int rt, const u4 (&kr)[4 * W]) -> f32x4 {
+      const int t0 = gt0 + sc * kPage;
+      const int nkeys = min(kPage, T - t0);
+      f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        if (kc >= KDC) break;
+        u4 w[W];
+#pragma unroll
+        for (int x = 0; x < W; ++x) w[x] = kr[kc * W + x];
+        if (key >= nkeys) {
+#pragma unroll
+          for (int x = 0; x < W; ++x) w[x] = u4{0u, 0u, 0u, 0u};
+        }
+        u4 kh, kl;
+        kv_op<KVF32>(w, kh, kl);
+        u4 a_h, a_l;
+        if constexpr (ONE) {
+          a_h = qh[kc];
+          a_l = ql[kc];
+        } else {
+          a_h = Qf[((rt * KDC + kc) * 2 + 0) * 64 + lane];
+          a_l = Qf[((rt * KDC + kc) * 2 + 1) * 64 + lane];
+        }
+        s4 = mfma(a_h, kh, s4);
+        s4 = mfma(a_l, kh, s4);
+        if constexpr (KVF32) {
+          s4 = mfma(a_h, kl, s4);
+          s4 = mfma(a_l, kl, s4);
+        }
+      }
+      const int tk = t0 + key;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = rt * 16 + 4 * (lane >> 4) + i;
+        const bool vis = r < R && key < nkeys && tk <= P.L + r / P.G;
+        s4[i] = vis ? s4[i] : -INFINITY;
+      }
+      return s4;
+    };
+    // O += P V for sub-chunk sc (P in Ps at column offset pc)
     f32x4 acc[MAXRT][2];
 #pragma unroll
     for (int rt = 0; rt < MAXRT; ++rt)
 #pragma unroll
       for (int q = 0; q < 2; ++q) acc[rt][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bool first = true;
-    for (int sc0 = 0; sc0 < kGroupPages; sc0 += NPF) {
-      if (gt0 + sc0 * kPage >= T) break;
-      // ---- operand words of NPF sub-chunks, loaded together: keys
-      // 16*wave.. of this lane (scores) and values of this wave's d tiles
-      u4 kr[NPF][4 * W], vr[NPF][2][2 * W];
-      int phys[NPF];
+    auto pv = [&](int sc, int pc, u4 (&vr)[2][2 * W]) {
+      const int nkeys = min(kPage, T - (gt0 + sc * kPage));
+      u4 vh[2][2], vl[2][2];
 #pragma unroll
-      for (int s = 0; s < NPF; ++s) {
-        const int t0 = gt0 + (sc0 + s) * kPage;
-        phys[s] = t0 < T ? P.page_table[t0 / kPage] : 0;
-      }
+      for (int q = 0; q < 2; ++q) {
+        if (q >= DTW) break;
 #pragma unroll
-      for (int s = 0; s < NPF; ++s) {
-        const int t0 = gt0 + (sc0 + s) * kPage;
-        if (t0 >= T) continue;
-        const long long kb = (((long long)phys[s] * P.Hkv + g) * 2 + 0) * kPage * D;
-        const long long vb = kb + (long long)kPage * D;
+        for (int kc = 0; kc < 2; ++kc) {
+          u4 w[W];
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          if (kc >= KDC) break;
-          const gu4* src = (const gu4*)(static_cast<const char*>(kv) + (kb + (long long)key * D + kc * 32 + kq) * (KVF32 ? 4 : 2));
-#pragma unroll
-          for (int w = 0; w < W; ++w) kr[s][kc * W + w] = src[w];
-        }
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          if (q >= DTW) break;
-          const int d = (wave * DTW + q) * 16 + (lane & 15);
-#pragma unroll
-          for (int kc = 0; kc < 2; ++kc) {
-            const gu4* src = (const gu4*)(static_cast<const char*>(kv) + (vb + (long long)d * kPage + kc * 32 + kq) * (KVF32 ? 4 : 2));
-#pragma unroll
-            for (int w = 0; w < W; ++w) vr[s][q][kc * W + w] = src[w];
-          }
+          for (int x = 0; x < W; ++x) w[x] = vr[q][kc * W + x];
+          kv_mask<KVF32>(w, kc * 32 + kq, nkeys);
+          kv_op<KVF32>(w, vh[q][kc], vl[q][kc]);
         }
       }
-      if (first) {
-        // ---- Q fragments (rotated, scaled, hi/lo); padding rows are zero
-        for (int i = tid; i < RT * 16 * (D / 8); i += kThreads) {
-          const int r = i / (D / 8), dg = i % (D / 8);
-          const int d0 = dg * 8;
+#pragma unroll
+      for (int rt = 0; rt < MAXRT; ++rt) {
+        if (rt >= RT) break;
+        u4 ph[2], pl[2];
+#pragma unroll
+        for (int kc = 0; kc < 2; ++kc) {
+          const float* pr = Ps + (rt * 16 + (lane & 15)) * PSW + pc + kc * 32 + kq;
           float v[8];
-          if (r < R) {
-            const int j = r / P.G, h = g * P.G + r % P.G;
-            const float* qrow = P.qkv + (long long)j * P.ldqkv + h * D;
-            const int pos = P.L + j;
-            const int i0 = d0 < H ? d0 : d0 - H;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float cs = P.rope_cs[((long long)pos * H + i0 + e) * 2 + 0];
-              const float sn = P.rope_cs[((long long)pos * H + i0 + e) * 2 + 1];
-              const float a = qrow[i0 + e], b = qrow[i0 + e + H];
-              v[e] = (d0 < H ? (a * cs - b * sn) : (b * cs + a * sn)) * P.attn_scale;
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = 0.f;
-          }
-          u4 hi, lo;
-          split8(v, hi, lo);
-          const int rt = r >> 4, kc = d0 >> 5, ln = (r & 15) + 16 * ((d0 & 31) >> 3);
-          Qf[((rt * KDC + kc) * 2 + 0) * 64 + ln] = hi;
-          Qf[((rt * KDC + kc) * 2 + 1) * 64 + ln] = lo;
+          for (int e = 0; e < 8; ++e) v[e] = pr[e];
+          split8(v, ph[kc], pl[kc]);
         }
-        for (int r = tid; r < RT * 16; r += kThreads) {
-          mrun[r] = -INFINITY;
-          lrun[r] = 0.f;
-        }
-        __syncthreads();
-        first = false;
-        wstamp(wst, 1);
-      }
-#pragma unroll
-      for (int s = 0; s < NPF; ++s) {
-        const int t0 = gt0 + (sc0 + s) * kPage;
-        if (t0 >= T) break;
-        const int nkeys = min(kPage, T - t0);
-        // ---- scores of this wave's 16 keys for every row tile
-        u4 kh[4], kl[4];
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          if (kc >= KDC) break;
-          if constexpr (KVF32) {
-            const u4 a = kr[s][kc * 2], b = kr[s][kc * 2 + 1];
-            float v[8] = {__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3]),
-                          __uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3])};
-            if (key >= nkeys)
-#pragma unroll
-              for (int e = 0; e < 8; ++e) v[e] = 0.f;
-            split8(v, kh[kc], kl[kc]);
-          } else {
-            kh[kc] = key < nkeys ? kr[s][kc] : u4{0u, 0u, 0u, 0u};
-          }
-        }
-#pragma unroll
-        for (int rt = 0; rt < MAXRT; ++rt) {
-          if (rt >= RT) break;
-          f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kc = 0; kc < 4; ++kc) {
-            if (kc >= KDC) break;
-            const u4 qh = Qf[((rt * KDC + kc) * 2 + 0) * 64 + lane];
-            const u4 ql = Qf[((rt * KDC + kc) * 2 + 1) * 64 + lane];
-            s4 = mfma(qh, kh[kc], s4);
-            s4 = mfma(ql, kh[kc], s4);
-            if constexpr (KVF32) {
-              s4 = mfma(qh, kl[kc], s4);
-              s4 = mfma(ql, kl[kc], s4);
-            }
-          }
-          const int tk = t0 + key;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = rt * 16 + 4 * (lane >> 4) + i;
-            const bool vis = r < R && key < nkeys && tk <= P.L + r / P.G;
-            Ps[r * kPsStride + key] = vis ? s4[i] : -INFINITY;
-          }
-        }
-        __syncthreads();
-        // ---- running softmax per row: 16 threads per row, 4 keys each
-        // (the summation order is the same for any number of rows)
-        for (int r = tid >> 4; r < RT * 16; r += kThreads / 16) {
-          const int k0 = (tid & 15) * 4;
-          float sv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sv[e] = Ps[r * kPsStride + k0 + e];
-          float mc = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-#pragma unroll
-          for (int o = 1; o < 16; o <<= 1) mc = fmaxf(mc, __shfl_xor(mc, o, 64));
-          const float mo = mrun[r];
-          const float mn = fmaxf(mo, mc);
-          float sum = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float p = (mn == -INFINITY || sv[e] == -INFINITY) ? 0.f : expf(sv[e] - mn);
-            Ps[r * kPsStride + k0 + e] = p;
-            sum += p;
-          }
-#pragma unroll
-          for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
-          if ((tid & 15) == 0) {
-            const float al = (mn == -INFINITY) ? 1.f : expf(mo - mn);
-            alpha[r] = al;
-            lrun[r] = lrun[r] * al + sum;
-            mrun[r] = mn;
-          }
-        }
-        __syncthreads();
-        // ---- O = O * alpha + P V for this wave's d tiles
-        u4 vh[2][2], vl[2][2];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           if (q >= DTW) break;
+          f32x4 a4 = acc[rt][q];
 #pragma unroll
           for (int kc = 0; kc < 2; ++kc) {
-            const int p0 = kc * 32 + kq;   // first position of this lane's 8
+            a4 = mfma(ph[kc], vh[q][kc], a4);
+            a4 = mfma(pl[kc], vh[q][kc], a4);
             if constexpr (KVF32) {
-              const u4 a = vr[s][q][kc * 2], b = vr[s][q][kc * 2 + 1];
-              float v[8] = {__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3]),
-                            __uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3])};
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                if (p0 + e >= nkeys) v[e] = 0.f;
-              split8(v, vh[q][kc], vl[q][kc]);
-            } else {
-              u4 w = vr[s][q][kc];
-#pragma unroll
-              for (int c = 0; c < 4; ++c) {
-                if (p0 + 2 * c >= nkeys) w[c] &= 0xFFFF0000u;
-                if (p0 + 2 * c + 1 >= nkeys) w[c] &= 0x0000FFFFu;
-              }
-              vh[q][kc] = w;
+              a4 = mfma(ph[kc], vl[q][kc], a4);
+              a4 = mfma(pl[kc], vl[q][kc], a4);
             }
           }
+          acc[rt][q] = a4;
         }
+      }
+    };
+    // p = exp(s - max) over positions pc .. pc+63 of score row r (this
+    // thread's 4); returns the sub-chunk sum over the row's 16 threads
+    auto expsum = [&](int r, int pc) -> float {
+      const float mr = mrun[r];
+      float l = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float sv = Ps[r * PSW + pc + sq + e];
+        const float p = (mr == -INFINITY || sv == -INFINITY) ? 0.f : expf(sv - mr);
+        Ps[r * PSW + pc + sq + e] = p;
+        l += p;
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) l += __shfl_xor(l, o, 64);
+      return l;
+    };
+
+    if constexpr (ONE) {
+      u4 kr[NPF][4 * W], vr[NPF][2][2 * W];
+#pragma unroll
+      for (int sc = 0; sc < NPF; ++sc)
+        if (sc < nsc) load_ops(sc, kr[sc], vr[sc]);
+      __syncthreads();   // mrun / lrun initialised
+      wstamp(wst, 1);
+#pragma unroll
+      for (int sc = 0; sc < NPF; ++sc) {
+        if (sc >= nsc) break;
+        const f32x4 s4 = scores(sc, 0, kr[sc]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Ps[(4 * (lane >> 4) + i) * PSW + sc * kPage + key] = s4[i];
+      }
+      __syncthreads();
+      {
+        // row maximum over the group, then the sums
+        float mx = -INFINITY;
+        for (int sc = 0; sc < nsc; ++sc)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, Ps[srow * PSW + sc * kPage + sq + e]);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        if ((tid & 15) == 0) mrun[srow] = mx;
+        __syncthreads();
+        float l = 0.f;
+        for (int sc = 0; sc < nsc; ++sc) l += expsum(srow, sc * kPage);
+        if ((tid & 15) == 0) lrun[srow] = l;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int sc = 0; sc < NPF; ++sc) {
+        if (sc >= nsc) break;
+        pv(sc, sc * kPage, vr[sc]);
+      }
+    } else {
+      __syncthreads();   // query fragments and mrun / lrun in LDS
+      wstamp(wst, 1);
+      // pass 1: row maxima
+      for (int sc = 0; sc < nsc; ++sc) {
+        u4 kr[4 * W], vr[2][2 * W];
+        load_ops(sc, kr, vr);
 #pragma unroll
         for (int rt = 0; rt < MAXRT; ++rt) {
           if (rt >= RT) break;
-          u4 ph[2], pl[2];
+          const f32x4 s4 = scores(sc, rt, kr);
 #pragma unroll
-          for (int kc = 0; kc < 2; ++kc) {
-            const float* pr = Ps + (rt * 16 + (lane & 15)) * kPsStride + kc * 32 + kq;
-            float v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = pr[e];
-            split8(v, ph[kc], pl[kc]);
-          }
-          float al[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) al[i] = alpha[rt * 16 + 4 * (lane >> 4) + i];
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            if (q >= DTW) break;
-            f32x4 a4 = acc[rt][q];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a4[i] *= al[i];
-#pragma unroll
-            for (int kc = 0; kc < 2; ++kc) {
-              a4 = mfma(ph[kc], vh[q][kc], a4);
-              a4 = mfma(pl[kc], vh[q][kc], a4);
-              if constexpr (KVF32) {
-                a4 = mfma(ph[kc], vl[q][kc], a4);
-                a4 = mfma(pl[kc], vl[q][kc], a4);
-              }
-            }
-            acc[rt][q] = a4;
-          }
+          for (int i = 0; i < 4; ++i) Ps[(rt * 16 + 4 * (lane >> 4) + i) * PSW + key] = s4[i];
         }
+        __syncthreads();
+        for (int r = srow; r < RT * 16; r += kThreads / 16) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mx = fmaxf(mx, Ps[r * PSW + sq + e]);
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+          if ((tid & 15) == 0) mrun[r] = fmaxf(mrun[r], mx);
+        }
+        __syncthreads();
+      }
+      // pass 2: the same scores again, probabilities, sums and P V
+      for (int sc = 0; sc < nsc; ++sc) {
+        u4 kr[4 * W], vr[2][2 * W];
+        load_ops(sc, kr, vr);
+#pragma unroll
+        for (int rt = 0; rt < MAXRT; ++rt) {
+          if (rt >= RT) break;
+          const f32x4 s4 = scores(sc, rt, kr);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Ps[(rt * 16 + 4 * (lane >> 4) + i) * PSW + key] = s4[i];
+        }
+        __syncthreads();
+        for (int r = srow; r < RT * 16; r += kThreads / 16) {
+          const float l = expsum(r, 0);
+          if ((tid & 15) == 0) lrun[r] += l;
+        }
+        __syncthreads();
+        pv(sc, 0, vr);
         __syncthreads();
       }
     }
@@ -1127,6 +1223,7 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, unsign
         }
       }
     }
+    __syncthreads();   // lrun complete
     for (int r = tid; r < R; r += kThreads) {
       cst(P.pm + ib + r, mrun[r]);
       cst(P.ps + ib + r, lrun[r]);
@@ -1338,6 +1435,11 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
         gemm_phase<WF, EPI_STORE, 1>(P, d->M, io, sm, d->slot_mode == 2, ring, smem, wst);
         break;
       }
+      case PH_QKV:
+        sync([&] { gemm_prefetch<WF, 1>(d->M, dense, false, ring); });
+        io.kv = d->kv;
+        gemm_phase<WF, EPI_QKV, 1>(P, d->M, io, dense, false, ring, smem, wst);
+        break;
       case PH_RESID:
         sync([&] { gemm_prefetch<WF, 1>(d->M, dense, false, ring); });
         gemm_phase<WF, EPI_RESID, 1>(P, d->M, io, dense, false, ring, smem, wst);

@@ -16,11 +16,14 @@ __device__ __forceinline__ uint32_t f2bf_r(float f) {
 // ((sg * nkc + c) * kWaves + w) * tpu + half with sg = unit / kWaves,
 // w = unit % kWaves.  bf16 / fp32 fragment lane l holds k = 32c + 8(l/16) + e
 // (e = 0..7) of column 16t + l%16; int4 dword cc of lane l holds nibbles
-// k = 128c + 32cc + 8(l/16) + e.  K and N tails are zero.
+// k = 128c + 32cc + 8(l/16) + e.  K and N tails are zero.  With
+// pair_dim > 0 the columns of every pair_dim-wide head are taken
+// interleaved: destination column 2i + h of a head is source column
+// i + h * pair_dim / 2 (rotary pairs side by side).
 template <int WF>
 __global__ void k_retile(const void* __restrict__ src, const uint16_t* __restrict__ ssc, int K, int N,
                          uint4* __restrict__ dst, uint4* __restrict__ dst2, int nkc, int tpu, int tile_off,
-                         int tile_stride) {
+                         int tile_stride, int pair_dim) {
   const int n_src_tiles = (N + 15) / 16;
   const long long total = (long long)n_src_tiles * nkc * 64;
   for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
@@ -30,6 +33,11 @@ __global__ void k_retile(const void* __restrict__ src, const uint16_t* __restric
     const int c = (int)(fc % nkc);
     const int t = (int)(fc / nkc);
     const int n = t * 16 + (l & 15);
+    int sn = n;   // source column
+    if (pair_dim > 0) {
+      const int hd = n / pair_dim, p = n - hd * pair_dim;
+      sn = hd * pair_dim + (p >> 1) + (p & 1) * (pair_dim >> 1);
+    }
     const int dt = tile_off + t * tile_stride;
     const int unit = dt / tpu, half = dt % tpu;
     const int sg = unit / kWaves, w = unit % kWaves;
@@ -44,13 +52,13 @@ __global__ void k_retile(const void* __restrict__ src, const uint16_t* __restric
         for (int e = 0; e < 8; ++e) {
           const int k = c * 128 + cc * 32 + (l >> 4) * 8 + e;
           uint32_t nib = 0;
-          if (n < N && k < K) nib = (sq[(long long)(k >> 1) * N + n] >> ((k & 1) * 4)) & 0xFu;
+          if (n < N && k < K) nib = (sq[(long long)(k >> 1) * N + sn] >> ((k & 1) * 4)) & 0xFu;
           d |= nib << (4 * e);
         }
         dw[cc] = d;
       }
       dst[fi * 64 + l] = make_uint4(dw[0], dw[1], dw[2], dw[3]);
-      if (l < 16) reinterpret_cast<uint16_t*>(dst2)[fi * 16 + l] = (n < N) ? ssc[(long long)c * N + n] : (uint16_t)0;
+      if (l < 16) reinterpret_cast<uint16_t*>(dst2)[fi * 16 + l] = (n < N) ? ssc[(long long)c * N + sn] : (uint16_t)0;
     } else {
       const int kb = c * 32 + (l >> 4) * 8;
       uint32_t hw[4], lw[4];
@@ -62,11 +70,11 @@ __global__ void k_retile(const void* __restrict__ src, const uint16_t* __restric
           const int kk = kb + 2 * e2 + hh;
           const bool ok = n < N && kk < K;
           if constexpr (WF == W_F32) {
-            const float v = ok ? static_cast<const float*>(src)[(long long)kk * N + n] : 0.f;
+            const float v = ok ? static_cast<const float*>(src)[(long long)kk * N + sn] : 0.f;
             hb[hh] = f2bf_r(v);
             lb[hh] = f2bf_r(v - __uint_as_float(hb[hh] << 16));
           } else {
-            hb[hh] = ok ? static_cast<const uint16_t*>(src)[(long long)kk * N + n] : 0u;
+            hb[hh] = ok ? static_cast<const uint16_t*>(src)[(long long)kk * N + sn] : 0u;
             lb[hh] = 0;
           }
         }
@@ -87,20 +95,20 @@ static dim3 grid_for(long long total) {
 }
 
 hipError_t launch_retile(int wfmt, const void* src, const void* src_scales, int K, int N, void* dst, void* dst2,
-                         int nkc, int tpu, int tile_off, int tile_stride, hipStream_t s) {
+                         int nkc, int tpu, int tile_off, int tile_stride, int pair_dim, hipStream_t s) {
   const long long total = (long long)((N + 15) / 16) * nkc * 64;
   const uint16_t* sc = static_cast<const uint16_t*>(src_scales);
   uint4* d1 = static_cast<uint4*>(dst);
   uint4* d2 = static_cast<uint4*>(dst2);
   if (wfmt == W_INT4)
     hipLaunchKernelGGL(k_retile<W_INT4>, grid_for(total), dim3(256), 0, s, src, sc, K, N, d1, d2, nkc, tpu, tile_off,
-                       tile_stride);
+                       tile_stride, pair_dim);
   else if (wfmt == W_F32)
     hipLaunchKernelGGL(k_retile<W_F32>, grid_for(total), dim3(256), 0, s, src, sc, K, N, d1, d2, nkc, tpu, tile_off,
-                       tile_stride);
+                       tile_stride, pair_dim);
   else
     hipLaunchKernelGGL(k_retile<W_BF16>, grid_for(total), dim3(256), 0, s, src, sc, K, N, d1, d2, nkc, tpu, tile_off,
-                       tile_stride);
+                       tile_stride, pair_dim);
   return hipGetLastError();
 }
 

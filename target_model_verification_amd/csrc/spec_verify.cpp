@@ -60,8 +60,9 @@ struct spec_verify {
   int* page_table = nullptr;
   float* rope_cs = nullptr;
   // activations / scratch
-  int ldx = 0, ldqkv = 0, ldl = 0, n_ss = 0, n_stat = 0, ldr = 0;
-  float *x = nullptr, *qkv = nullptr, *ss = nullptr, *logits = nullptr;
+  int ldx = 0, ldl = 0, n_ss = 0, n_stat = 0, ldr = 0;
+  float *x = nullptr, *ss = nullptr, *logits = nullptr;
+  uint4* qf = nullptr;     // attention query fragments
   uint4 *a_norm = nullptr, *a_o = nullptr, *a_act = nullptr;
   long long a_act_slot = 0;
   float *st_max = nullptr, *st_sum = nullptr;
@@ -314,7 +315,10 @@ struct Uploader {
   }
 
   // upload host matrix [K][N] into tiles tile_off + t * tile_stride of stack slot e
-  int put(HostMat& H, int kind, int layer, int expert, int K, int N, int tile_off, int tile_stride, int e) {
+  // (pair_dim > 0: columns of every pair_dim-wide head interleaved as rotary
+  // pairs, see k_retile)
+  int put(HostMat& H, int kind, int layer, int expert, int K, int N, int tile_off, int tile_stride, int e,
+          int pair_dim = 0) {
     const int wf = h->wfmt;
     Mat& M = H.m;
     char* wdst = const_cast<char*>(static_cast<const char*>(M.w)) + (long long)e * M.w_stride;
@@ -332,14 +336,15 @@ struct Uploader {
         he = hipMemcpyAsync(static_cast<char*>(staging) + soff, ts->data, sb, hipMemcpyHostToDevice, h->stream);
       if (he == hipSuccess)
         he = launch_retile(wf, staging, static_cast<char*>(staging) + soff, K, N, wdst, w2dst, M.nkc, H.tpu,
-                           tile_off, tile_stride, h->stream);
+                           tile_off, tile_stride, pair_dim, h->stream);
     } else {
       const size_t eb = wf == W_F32 ? 4 : 2;
       const spec_tensor* t = get(kind, layer, expert, 0, (uint64_t)K * N * eb);
       if (!t) return SPEC_EINVAL;
       he = hipMemcpyAsync(staging, t->data, (size_t)K * N * eb, hipMemcpyHostToDevice, h->stream);
       if (he == hipSuccess)
-        he = launch_retile(wf, staging, nullptr, K, N, wdst, w2dst, M.nkc, H.tpu, tile_off, tile_stride, h->stream);
+        he = launch_retile(wf, staging, nullptr, K, N, wdst, w2dst, M.nkc, H.tpu, tile_off, tile_stride, pair_dim,
+                           h->stream);
     }
     if (he == hipSuccess) he = hipStreamSynchronize(h->stream);
     if (he != hipSuccess) return fail(h, SPEC_EHIP, std::string("weight upload: ") + hipGetErrorString(he));
@@ -439,7 +444,8 @@ bool check_tensors(const spec_config& c, const spec_tensor* t, int n, std::strin
 }
 
 bool prog_kind_is_gemm(int kind) {
-  return kind == PH_STORE || kind == PH_RESID || kind == PH_SWIGLU || kind == PH_LOGITS || kind == PH_ROUTE_SWIGLU;
+  return kind == PH_STORE || kind == PH_RESID || kind == PH_SWIGLU || kind == PH_LOGITS || kind == PH_ROUTE_SWIGLU ||
+         kind == PH_QKV;
 }
 
 Phase gemm_phase_desc(int kind, int layer, const HostMat& H) {
@@ -506,8 +512,10 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
     if ((rc = up.put_vec(&Lw.attn_norm, SPEC_T_ATTN_NORM, l, d))) return rc;
     if ((rc = up.put_vec(&Lw.ffn_norm, SPEC_T_FFN_NORM, l, d))) return rc;
     if ((rc = up.alloc_mat(Lw.qkv, plan.qkv))) return rc;
-    if ((rc = up.put(Lw.qkv, SPEC_T_WQ, l, -1, d, Hq * D, 0, 1, 0))) return rc;
-    if ((rc = up.put(Lw.qkv, SPEC_T_WK, l, -1, d, Hkv * D, Hq * D / 16, 1, 0))) return rc;
+    // query and key heads with rotary pairs side by side (the QKV epilogue
+    // rotates with its neighbouring lane)
+    if ((rc = up.put(Lw.qkv, SPEC_T_WQ, l, -1, d, Hq * D, 0, 1, 0, D))) return rc;
+    if ((rc = up.put(Lw.qkv, SPEC_T_WK, l, -1, d, Hkv * D, Hq * D / 16, 1, 0, D))) return rc;
     if ((rc = up.put(Lw.qkv, SPEC_T_WV, l, -1, d, Hkv * D, (Hq + Hkv) * D / 16, 1, 0))) return rc;
     if ((rc = up.alloc_mat(Lw.o, plan.o))) return rc;
     if ((rc = up.put(Lw.o, SPEC_T_WO, l, -1, Hq * D, d, 0, 1, 0))) return rc;
@@ -576,14 +584,13 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   }
   // activations and scratch (zero-filled)
   h->ldx = rup(d, 32);
-  h->ldqkv = rup((Hq + 2 * Hkv) * D, 32);
   h->ldl = rup(V, 32);
   h->n_ss = cdiv(d, 16);
   h->n_stat = cdiv(V, 16);
   h->ldr = rup(std::max(E, 1), 32);
   const int n_slots_max = moe ? E + S : 1;
   if ((rc = dalloc_z(h, &h->x, 16 * (size_t)h->ldx))) return rc;
-  if ((rc = dalloc_z(h, &h->qkv, 16 * (size_t)h->ldqkv))) return rc;
+  if ((rc = dalloc_z(h, &h->qf, (size_t)Hkv * kAttnRT * (D / 32) * 2 * 64))) return rc;
   if ((rc = dalloc_z(h, &h->ss, 16 * (size_t)h->n_ss))) return rc;
   if ((rc = dalloc_z(h, &h->logits, 16 * (size_t)h->ldl))) return rc;
   if ((rc = dalloc_z(h, &h->a_norm, (size_t)plan.a_norm))) return rc;
@@ -630,8 +637,8 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   for (int l = 0; l < c.n_layers; ++l) {
     HostLayer& Lw = h->layers[l];
     const float* next_gain = l + 1 < c.n_layers ? h->layers[l + 1].attn_norm : h->final_norm;
-    Phase q = gemm_phase_desc(PH_STORE, l, Lw.qkv);
-    q.a = h->a_norm; q.out = h->qkv; q.ldo = h->ldqkv; q.scale = 1;
+    Phase q = gemm_phase_desc(PH_QKV, l, Lw.qkv);
+    q.a = h->a_norm; q.kv = Lw.kv;
     add(q, SPEC_K_QKV, Lw.qkv.alg_bytes);
     Phase at{};
     at.kind = PH_ATTN; at.layer = l; at.kv = Lw.kv;
@@ -719,9 +726,10 @@ double phase_bytes(const spec_verify* h, int i, int m, int L, int experts_loaded
   const double w = h->prog_bytes_fixed[i];
   switch (h->prog_cls[i]) {
     case SPEC_K_EMBED: return (double)m * d * (c.weight_dtype == SPEC_DT_F32 ? 4 : 2) + (double)m * d * 4;
-    case SPEC_K_QKV: return w + (double)m * d * 4 + (double)m * (Hq + 2 * Hkv) * D * 4;
-    case SPEC_K_ATTN:
-      return (double)L * Hkv * D * 2 * kvb + (double)m * Hkv * D * 2 * kvb + (double)m * (Hq + 2 * Hkv) * D * 4;
+    case SPEC_K_QKV:   // weights, A operand, queries out (hi/lo), new keys and values into the cache
+      return w + (double)m * d * 4 + (double)m * Hq * D * 4 + (double)m * Hkv * D * 2 * kvb;
+    case SPEC_K_ATTN:  // the cache over L + m positions, queries in, attention output (hi/lo)
+      return (double)(L + m) * Hkv * D * 2 * kvb + 2.0 * m * Hq * D * 4;
     case SPEC_K_O: return w + (double)m * Hq * D * 4 + 2.0 * m * d * 4;
     case SPEC_K_GATEUP: return w + (double)m * d * 4 + (double)m * c.d_ff * 4;
     case SPEC_K_DOWN: return w + (double)m * c.d_ff * 4 + 2.0 * m * d * 4;
@@ -784,7 +792,7 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   p.tokens = h->tokens_dev; p.page_table = h->page_table; p.rope_cs = h->rope_cs;
   p.x = h->x; p.ldx = h->ldx; p.ss = h->ss;
   p.a_norm = h->a_norm; p.a_o = h->a_o; p.a_act = h->a_act; p.a_act_slot = h->a_act_slot;
-  p.qkv = h->qkv; p.ldqkv = h->ldqkv; p.logits = h->logits; p.ldl = h->ldl;
+  p.qf = h->qf; p.logits = h->logits; p.ldl = h->ldl;
   p.st_max = h->st_max; p.st_sum = h->st_sum; p.st_idx = h->st_idx; p.n_stat = h->n_stat;
   p.pm = h->pm; p.ps = h->ps; p.pacc = h->pacc;
   p.rlog = h->rlog; p.ldr = h->ldr; p.ey = h->ey; p.ey_slot = h->ey_slot; p.ldy = h->ldx;

@@ -26,6 +26,7 @@ constexpr int kPage = 64;             // KV page (positions); attention sub-chun
 constexpr int kGroupPages = 4;        // pages per attention work item (fixed grid)
 constexpr int kGroupPos = kPage * kGroupPages;
 constexpr int kMaxAttnRows = 128;     // (k+1) * (n_q_heads / n_kv_heads) per KV head
+constexpr int kAttnRT = kMaxAttnRows / 16;   // attention row tiles per KV head at most
 constexpr long long kInlineMergeElems = 16384;   // rows * head_dim * groups merged by one workgroup
 constexpr int kRing = 32;             // weight fragments per prefetch batch (per wave)
 constexpr int kAWindowBytes = 128 * 1024;  // LDS bytes of the staged A window (2048 k of hi/lo rows)
@@ -64,7 +65,8 @@ enum PhKind : int {
   PH_ATTN = 5,         // causal attention over the paged cache -> per-group partials
   PH_ROUTE_SWIGLU = 6, // MoE routing of the block, then SWIGLU over the union
   PH_COMBINE = 7,      // MoE weighted combine -> x, next A operand
-  PH_ATTN_MERGE = 8    // merge of the attention partials -> A operand of O
+  PH_ATTN_MERGE = 8,   // merge of the attention partials -> A operand of O
+  PH_QKV = 9           // Q/K/V projection: rotary, queries -> fragments, keys / values -> cache
 };
 
 struct Phase {
@@ -99,9 +101,9 @@ struct PassP {
   float* ss;                 // [16][n_ss]
   uint4* a_norm;             // A operand of norm-fed GEMMs: x * gain, hi/lo fragments
   uint4* a_o;                // attention output, hi/lo fragments
+  uint4* qf;                 // rotated, scaled queries: [Hkv][kAttnRT][D/32][hi|lo][64] fragments
   uint4* a_act;              // SwiGLU output [slot][..], hi/lo fragments
   long long a_act_slot;      // uint4 per slot
-  float* qkv; int ldqkv;     // [16][ldqkv]
   float* logits; int ldl;    // [16][ldl]
   float* st_max; float* st_sum; int* st_idx; int n_stat;   // per 16-column tile of the LM head
   float* pm; float* ps; float* pacc;                      // attention partials
@@ -148,7 +150,7 @@ hipError_t pass_occupancy(int wfmt, size_t lds, int* blocks_per_cu);
 constexpr int kMaxPending = 512;
 hipError_t launch_accept(const AcceptParams& p, hipStream_t s);
 hipError_t launch_retile(int wfmt, const void* src, const void* src_scales, int K, int N, void* dst,
-                         void* dst2, int nkc, int tpu, int tile_off, int tile_stride, hipStream_t s);
+                         void* dst2, int nkc, int tpu, int tile_off, int tile_stride, int pair_dim, hipStream_t s);
 hipError_t launch_kv_import(int kv_f32, const void* src, int P, int Hkv, int D, void* layer_base,
                             const int* page_table, hipStream_t s);
 
