@@ -106,6 +106,24 @@ __device__ __forceinline__ f32x4 cld4(const float* p) {   // p 16-byte aligned
                __uint_as_float((uint32_t)(b >> 32))};
 }
 
+// Ready counters: a producer adds one per finished unit of output (after
+// its stores are complete); a consumer waits until a counter reaches the
+// pass's target (bounded, like the grid barrier: on a timeout it raises
+// the error flag and goes on).
+__device__ __forceinline__ void ready_add(unsigned long long* c, unsigned long long n = 1) {
+  __hip_atomic_fetch_add(c, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void ready_wait(const unsigned long long* c, unsigned long long target, int* err) {
+  unsigned spins = 0;
+  while (__hip_atomic_load(const_cast<unsigned long long*>(c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins == (1u << 24)) {
+      __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+  }
+}
+
 // Element (row, col) of an A operand in hi/lo fragment layout: 32-k chunk
 // col/32 holds 128 uint4 (hi[64], lo[64]); lane l of a fragment holds 8
 // consecutive k of row l%16 starting at 8*(l/16).
@@ -308,18 +326,20 @@ struct GemmIO {
   uint4* a_out; long long a_out_slot;        // RESID / SWIGLU: next A operand
   float* trace;              // RESID: residual copy for this layer (nullable)
   void* kv;                  // QKV: the layer's cache pages
+  unsigned long long* ready;  // this layer's ready counters
+  int dep, notify;            // DepKind of the inputs / outputs
 };
 
 // Query element (block row j, query head h, dim d), already rotated and
 // scaled, into the attention's MFMA A fragments: per KV head g = h / G,
 // row r = j * G + h % G of row tile r / 16, 32-dim chunk d / 32, hi and lo
 // bf16 parts; lane (r % 16) + 16 * ((d % 32) / 8) holds 8 consecutive dims.
-__device__ __forceinline__ void qfrag_put(const PassP& P, int h, int j, int d, float v) {
+__device__ __forceinline__ void qfrag_put(const PassP& P, uint4* qf, int h, int j, int d, float v) {
   const int g = h / P.G, r = j * P.G + (h - g * P.G);
   const int KDC = P.D >> 5;
-  const long long f = (((long long)g * kAttnRT + (r >> 4)) * KDC + (d >> 5)) * 2;   // hi fragment
+  const long long f = (((long long)g * P.qf_rt + (r >> 4)) * KDC + (d >> 5)) * 2;   // hi fragment
   const int ln = (r & 15) + 16 * ((d & 31) >> 3), e = d & 7;
-  uint16_t* q = reinterpret_cast<uint16_t*>(P.qf);
+  uint16_t* q = reinterpret_cast<uint16_t*>(qf);
   const uint32_t hb = f2bf(v);
   cst16(q + (f * 64 + ln) * 8 + e, (uint16_t)hb);
   cst16(q + ((f + 1) * 64 + ln) * 8 + e, (uint16_t)f2bf(v - bf2f(hb)));
@@ -414,7 +434,7 @@ __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const Gem
           const float a = odd ? pv[i] : v[i], b = odd ? v[i] : pv[i];   // x[ii], x[ii + H]
           const float rot = odd ? (b * cs[i] + a * sn[i]) : (a * cs[i] - b * sn[i]);
           const int dd = ii + odd * H;
-          if (col < qc) qfrag_put(P, head, row, dd, rot * P.attn_scale);
+          if (col < qc) qfrag_put(P, io.a_out, head, row, dd, rot * P.attn_scale);
           else kv_put<WF == W_F32>(io.kv, ((pg[i] + head) * 2 + 0) * kPage * D + (long long)(t % kPage) * D + dd, rot);
         } else {
           kv_put<WF == W_F32>(io.kv, ((pg[i] + head) * 2 + 1) * kPage * D + (long long)p * kPage + (t % kPage), v[i]);
@@ -507,6 +527,35 @@ __device__ __forceinline__ void stage_window(const Lin& L, const GemmIO& io, int
     __builtin_amdgcn_global_load_lds((gvoid*)(src + i0 + lane), (lvoid*)(smem + (size_t)i0 * 16), 16, 0, 0);
 }
 
+// Dependency bookkeeping of the dataflow edges (one 64-column block of a
+// phase's output = one supergroup).
+// KV head of the QKV output block starting at column c0.
+__device__ __forceinline__ int qkv_block_head(const PassP& P, int c0) {
+  const int qc = P.Hq * P.D, kc = P.Hkv * P.D;
+  if (c0 < qc) return (c0 / P.D) / P.G;
+  return c0 < qc + kc ? (c0 - qc) / P.D : (c0 - qc - kc) / P.D;
+}
+// QKV blocks feeding one KV head's attention: its G query heads, key, value.
+__device__ __forceinline__ unsigned long long heads_expect(const PassP& P) {
+  return (unsigned long long)(P.G + 2) * (P.D / 64);
+}
+// O-input window w: the query heads whose columns meet it.
+__device__ __forceinline__ unsigned long long owin_expect(const PassP& P, int w) {
+  const int c0 = w * P.o_wcols, c1 = min(c0 + P.o_wcols, P.Hq * P.D);
+  return (unsigned long long)((c1 - 1) / P.D - c0 / P.D + 1);
+}
+// announces a finished output block (stores complete) of a producing phase
+__device__ __forceinline__ void notify_block(const PassP& P, const GemmIO& io, int sg) {
+  if (io.notify == kDepHeads) ready_add(io.ready + qkv_block_head(P, sg * 64));
+}
+// waits (workgroup-wide) until the input window win of a consuming phase is ready
+__device__ __forceinline__ void wait_window(const PassP& P, const GemmIO& io, int win) {
+  if (io.dep == kDepOWin) {
+    if (threadIdx.x == 0) ready_wait(io.ready + 256 + win, P.epoch * owin_expect(P, win), P.err);
+    __syncthreads();
+  }
+}
+
 // One weight-streaming phase over `sm.n_slots` slots (experts) of M.
 template <int WF, int EPI, int TPU>
 __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const GemmIO io, const SlotMap sm,
@@ -528,6 +577,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     const Cur a = cur_at(L, u0);
     sk = slot_major ? a.slot : 0;
     sw = a.win;
+    wait_window(P, io, sw);
     stage_window<WF>(L, io, sk, sw, smem);
   }
   if (EPI == EPI_SWIGLU || EPI == EPI_LOGITS || EPI == EPI_QKV || (EPI == EPI_STORE && io.scale)) row_scales(P, C->rs);
@@ -628,9 +678,11 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
         for (int t = 0; t < TPU; ++t) cst4(p + t * 256 + lane * 4, acc[t]);
       }
     }
-    if (nseg > 1 && threadIdx.x == 0) {
+    // split segments (and, for producing phases, blocks finished here) are
+    // listed; bit 31 marks a finished block
+    if ((nseg > 1 || io.notify) && threadIdx.x == 0) {
       const int k = C->pend_n;   // capacity guaranteed by the host (kMaxPending)
-      C->pend[k] = cc.slot << 20 | cc.sg;
+      C->pend[k] = (nseg > 1 ? 0 : (int)0x80000000u) | cc.slot << 20 | cc.sg;
       C->pend_n = k + 1;
     }
     if (cc.u >= u1) break;
@@ -640,6 +692,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
       __syncthreads();   // every wave is done with the staged window
       sk = key;
       sw = cc.win;
+      wait_window(P, io, sw);
       stage_window<WF>(L, io, sk, sw, smem);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -654,8 +707,10 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
   __syncthreads();
   const int np = C->pend_n;
   for (int k = threadIdx.x; k < np; k += kThreads) {
-    const int s = C->pend[k] >> 20, sg = C->pend[k] & 0xfffff;
-    __hip_atomic_fetch_add(P.tickets + (long long)s * M.n_sg + sg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int e = C->pend[k];
+    const int s = (e >> 20) & 0x7ff, sg = e & 0xfffff;
+    if (e < 0) notify_block(P, io, sg);
+    else __hip_atomic_fetch_add(P.tickets + (long long)s * M.n_sg + sg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const int nb = L.n_slots * M.n_sg;
   const int b0 = range_begin(nb, g, G), b1 = range_begin(nb, g + 1, G);
@@ -679,7 +734,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     }
     __syncthreads();   // the partials are read with agent-scope loads
     const int unit = sg * kWaves + wave;
-    if (unit >= M.n_units) continue;
+    if (unit < M.n_units) {
     f32x4 sum[TPU];
 #pragma unroll
     for (int t = 0; t < TPU; ++t) sum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -702,6 +757,12 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
       }
     }
     epilogue<WF, EPI, TPU>(P, M, io, C->rs, s, unit, sum);
+    }
+    if (io.notify) {
+      release_all_waves();
+      __syncthreads();
+      if (threadIdx.x == 0) notify_block(P, io, sg);
+    }
   }
 }
 
@@ -828,15 +889,15 @@ __device__ __forceinline__ float attn_merge_one(const PassP& P, int g, int r, in
   return A / S;
 }
 
-__device__ __forceinline__ void attn_merge_store(const PassP& P, int g, int r, int d) {
+__device__ __forceinline__ void attn_merge_store(const PassP& P, uint4* a_o, int g, int r, int d) {
   const int j = r / P.G, h = g * P.G + r % P.G;
-  afrag_put(P.a_o, j, h * P.D + d, attn_merge_one(P, g, r, d));
+  afrag_put(a_o, j, h * P.D + d, attn_merge_one(P, g, r, d));
 }
 
 // The whole merge of KV head g by one workgroup (its last attention item):
 // per-row group factors once in LDS, then each thread's outputs with their
 // partial loads in flight together.  Same arithmetic as attn_merge_one.
-__device__ __forceinline__ void attn_merge_head(const PassP& P, int g, unsigned char* smem) {
+__device__ __forceinline__ void attn_merge_head(const PassP& P, uint4* a_o, int g, unsigned char* smem) {
   const int D = P.D, R = P.m * P.G, NG = P.n_groups;
   const int tid = threadIdx.x;
   float* fv = reinterpret_cast<float*>(smem);   // [NG][R]: pm, then the factors
@@ -893,7 +954,7 @@ __device__ __forceinline__ void attn_merge_head(const PassP& P, int g, unsigned 
       if (e < R * D) {
         const int r = e / D, d = e % D;
         const int j = r / P.G, h = g * P.G + r % P.G;
-        afrag_put(P.a_o, j, h * D + d, A[k] / Sr[r]);
+        afrag_put(a_o, j, h * D + d, A[k] / Sr[r]);
       }
     }
   }
@@ -938,7 +999,8 @@ __device__ __forceinline__ void kv_mask(u4* w, int p0, int nvalid) {
 // scores are recomputed per sub-chunk in the second pass -- the same
 // operations in the same order, so both give identical bits.
 template <bool KVF32, int MAXRT>
-__device__ __forceinline__ void attention_phase(const PassP& P, void* kv, unsigned char* smem,
+__device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const uint4* qf, uint4* a_o,
+                                                unsigned long long* ready, int dep, unsigned char* smem,
                                                 unsigned long long* wst) {
   constexpr int W = KVF32 ? 2 : 1;                    // 16-byte words per 8 cache elements
   constexpr bool ONE = !KVF32 && MAXRT == 1;          // the whole group at once
@@ -963,7 +1025,12 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, unsign
     const int g = item / P.n_groups, grp = item % P.n_groups;
     const int gt0 = grp * kGroupPos;
     const int nsc = min(kGroupPages, (T - gt0 + kPage - 1) / kPage);   // sub-chunks holding positions
-    const gu4* qsrc = (const gu4*)(P.qf + (long long)g * kAttnRT * KDC * 2 * 64);
+    if (dep == kDepHeads) {
+      // this KV head's query fragments and new cache rows are written
+      if (tid == 0) ready_wait(ready + g, P.epoch * heads_expect(P), P.err);
+      __syncthreads();
+    }
+    const gu4* qsrc = (const gu4*)(qf + (long long)g * P.qf_rt * KDC * 2 * 64);
     // ---- query fragments: registers (one row tile) or LDS
     u4 qh[4], ql[4];
     if constexpr (ONE) {
@@ -1239,7 +1306,15 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, unsign
         C->misc[0] = last ? 1 : 0;   // the partials are then read with agent-scope loads
       }
       __syncthreads();
-      if (C->misc[0]) attn_merge_head(P, g, smem);
+      if (C->misc[0]) {
+        attn_merge_head(P, a_o, g, smem);
+        // the O projection's windows that hold these query heads
+        release_all_waves();
+        __syncthreads();
+        if (tid == 0)
+          for (int h = g * P.G; h < (g + 1) * P.G; ++h)
+            for (int w = h * D / P.o_wcols; w <= ((h + 1) * D - 1) / P.o_wcols; ++w) ready_add(ready + 256 + w);
+      }
     }
     __syncthreads();
   }
@@ -1247,13 +1322,13 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, unsign
 
 // The merge as a phase of its own (heads with many groups or rows): one
 // output element per thread over the whole grid.
-__device__ __forceinline__ void attn_merge_phase(const PassP& P) {
+__device__ __forceinline__ void attn_merge_phase(const PassP& P, uint4* a_o) {
   const int D = P.D, R = P.m * P.G;
   const long long total = (long long)P.Hkv * R * D;
   for (long long e = (long long)blockIdx.x * kThreads + threadIdx.x; e < total; e += (long long)gridDim.x * kThreads) {
     const int d = (int)(e % D);
     const long long gr = e / D;
-    attn_merge_store(P, (int)(gr / R), (int)(gr % R), d);
+    attn_merge_store(P, a_o, (int)(gr / R), (int)(gr % R), d);
   }
 }
 
@@ -1407,20 +1482,26 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
     io.out = d->out; io.ldo = d->ldo; io.out_slot = d->out_slot; io.scale = d->scale;
     io.gain = d->gain; io.a_out = d->a_out; io.a_out_slot = d->a_out_slot;
     io.trace = (d->trace && P.trace) ? P.trace + (long long)d->layer * P.m * P.d : nullptr;
+    io.ready = P.ready + (long long)max(d->layer, 0) * kReadyStride;
+    io.dep = d->dep;
+    io.notify = d->notify;
+    // the O projection waits on merged heads only when attention merges
+    // inline; otherwise the merge phase and a barrier come first
+    const bool dataflow = d->dep != kDepNone && !(d->dep == kDepOWin && !P.attn_inline);
+    if (!dataflow) io.dep = kDepNone;
     const SlotMap dense{nullptr, 0, 0, 1};
     const SlotMap slots{C->ulist, C->uc, P.E, C->uc + P.n_shared};
-    // Each phase but the first starts with a grid barrier.  A weight-
-    // streaming phase issues its first weight batch during that barrier;
-    // the ring is written right before every phase that reads it, so it is
-    // dead (and its registers free) in the other phases.
+    // Each phase but the first starts with a grid barrier, unless its inputs
+    // come over ready counters (it then waits on those where it reads
+    // them).  A weight-streaming phase issues its first weight batch during
+    // that barrier (or right away); the ring is written right before every
+    // phase that reads it, so it is dead (and its registers free) in the
+    // other phases.
     unsigned long long* wst = P.wstamps ? P.wstamps + ((long long)ph * gridDim.x + blockIdx.x) * 4 : nullptr;
     auto sync = [&](auto&& prefetch) {
-      if (ph > 0) {
-        wstamp(wst ? wst - (long long)gridDim.x * 4 : nullptr, 3);   // end of the previous phase's work
-        grid_sync(gb, prefetch);
-      } else {
-        prefetch();
-      }
+      if (ph > 0) wstamp(wst ? wst - (long long)gridDim.x * 4 : nullptr, 3);   // end of the previous phase's work
+      if (ph > 0 && !dataflow) grid_sync(gb, prefetch);
+      else prefetch();
       stamp(P, ph);
       wstamp(wst, 0);
     };
@@ -1465,8 +1546,10 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
         sync([] {});
         wstamp(wst, 1);
         wstamp(wst, 2);
-        if (P.m * P.G <= 16) attention_phase<WF == W_F32, 1>(P, d->kv, smem, wst);
-        else attention_phase<WF == W_F32, kAttnRT>(P, d->kv, smem, wst);
+        if (P.m * P.G <= 16)
+          attention_phase<WF == W_F32, 1>(P, d->kv, d->a, d->a_out, io.ready, io.dep, smem, wst);
+        else
+          attention_phase<WF == W_F32, kAttnRT>(P, d->kv, d->a, d->a_out, io.ready, io.dep, smem, wst);
         break;
       case PH_ATTN_MERGE:
         if (P.attn_inline) {
@@ -1479,7 +1562,7 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
           break;
         }
         sync([] {});
-        attn_merge_phase(P);
+        attn_merge_phase(P, d->a_out);
         break;
       case PH_COMBINE:
         sync([] {});

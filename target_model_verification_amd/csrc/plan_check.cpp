@@ -138,8 +138,10 @@ bool check_gemm_walk(const GemmShape& s, int G, size_t ws_floats, size_t n_ticke
                                       s.tpu * 256) + (long long)(s.tpu - 1) * 256 + 63 * 4 + 4;
           if (last > (long long)ws_floats) return fail("split-K partial past the workspace");
           if ((long long)cc.slot * M.n_sg + cc.sg >= (long long)n_tickets) return fail("ticket out of range");
-          if (++pend > kMaxPending) return fail("too many split segments for one workgroup");
         }
+        // every segment may be listed (split ones, and finished blocks of
+        // phases that announce their outputs)
+        if (++pend > kMaxPending) return fail("too many segments for one workgroup's list");
         if (cc.u >= u1) break;
         seg_advance(L, cc);
         const int nkey = s.slot_major ? cc.slot : 0;

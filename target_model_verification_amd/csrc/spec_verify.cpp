@@ -76,6 +76,11 @@ struct spec_verify {
   unsigned* attn_tickets = nullptr;
   unsigned long long* bar = nullptr;
   unsigned long long bar_gen = 0;
+  int n_barriers_inline = 0, n_barriers_merge = 0;   // grid barriers per pass
+  unsigned long long epoch = 0;        // passes run (ready counters count up by pass)
+  unsigned long long* ready = nullptr; // [n_layers][kReadyStride]
+  int qf_rt = 1, o_wcols = 0;
+  long long qf_layer = 0, a_o_layer = 0;   // uint4 per layer
   int* tokens_dev = nullptr;
   int* result_dev = nullptr;
   int* tokens_host = nullptr;   // pinned
@@ -167,6 +172,7 @@ bool check_cfg(const spec_config* c, std::string& msg) {
   if (c->n_layers < 1 || c->d_model < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->vocab < 2)
     return bad("n_layers, d_model, heads must be >= 1 and vocab >= 2");
   if (c->n_q_heads % c->n_kv_heads != 0) return bad("n_q_heads must be a multiple of n_kv_heads");
+  if (c->n_kv_heads > 256) return bad("n_kv_heads must be at most 256");
   if (c->head_dim != 64 && c->head_dim != 128) return bad("head_dim must be 64 or 128");
   if (c->weight_dtype < SPEC_DT_F32 || c->weight_dtype > SPEC_DT_INT4G128) return bad("bad weight_dtype");
   if (c->kv_dtype != SPEC_DT_F32 && c->kv_dtype != SPEC_DT_BF16) return bad("kv_dtype must be F32 or BF16");
@@ -265,6 +271,11 @@ bool build_plan(const spec_config& c, int wf, int G, PassPlan& P, std::string& e
     P.ws_floats = std::max(P.ws_floats, (size_t)s->max_slots * s->M.n_sg * ms * kWaves * s->tpu * 256);
     P.n_tickets = std::max(P.n_tickets, (size_t)s->max_slots * s->M.n_sg);
   }
+  for (GemmShape* s : P.used)
+    if (s->M.n_win > 256) {   // ready counters per layer
+      err = std::string(s->name) + ": too many activation windows";
+      return false;
+    }
   for (GemmShape* s : P.used)
     if (!check_gemm_walk(*s, G, P.ws_floats, P.n_tickets, err)) return false;
   return true;
@@ -590,11 +601,18 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   h->ldr = rup(std::max(E, 1), 32);
   const int n_slots_max = moe ? E + S : 1;
   if ((rc = dalloc_z(h, &h->x, 16 * (size_t)h->ldx))) return rc;
-  if ((rc = dalloc_z(h, &h->qf, (size_t)Hkv * kAttnRT * (D / 32) * 2 * 64))) return rc;
+  // per-layer buffers for data crossing a dataflow edge (each address is
+  // written once per pass, so no cache can hold a stale copy of it)
+  h->qf_rt = cdiv(max_rows_attn(&c), 16);
+  h->qf_layer = (long long)Hkv * h->qf_rt * (D / 32) * 2 * 64;
+  if ((rc = dalloc_z(h, &h->qf, (size_t)h->qf_layer * c.n_layers))) return rc;
+  if ((rc = dalloc_z(h, &h->ready, (size_t)kReadyStride * c.n_layers))) return rc;
+  h->o_wcols = plan.o.M.win * (h->wfmt == W_INT4 ? kGroupK : kChunkK);
   if ((rc = dalloc_z(h, &h->ss, 16 * (size_t)h->n_ss))) return rc;
   if ((rc = dalloc_z(h, &h->logits, 16 * (size_t)h->ldl))) return rc;
   if ((rc = dalloc_z(h, &h->a_norm, (size_t)plan.a_norm))) return rc;
-  if ((rc = dalloc_z(h, &h->a_o, (size_t)plan.a_o))) return rc;
+  h->a_o_layer = plan.a_o;
+  if ((rc = dalloc_z(h, &h->a_o, (size_t)plan.a_o * c.n_layers))) return rc;
   h->a_act_slot = plan.a_act_slot;
   if ((rc = dalloc_z(h, &h->a_act, (size_t)h->a_act_slot * n_slots_max))) return rc;
   if ((rc = dalloc_z(h, &h->st_max, 16 * (size_t)h->n_stat))) return rc;
@@ -637,17 +655,19 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   for (int l = 0; l < c.n_layers; ++l) {
     HostLayer& Lw = h->layers[l];
     const float* next_gain = l + 1 < c.n_layers ? h->layers[l + 1].attn_norm : h->final_norm;
+    uint4* qf_l = h->qf + (long long)l * h->qf_layer;
+    uint4* a_o_l = h->a_o + (long long)l * h->a_o_layer;
     Phase q = gemm_phase_desc(PH_QKV, l, Lw.qkv);
-    q.a = h->a_norm; q.kv = Lw.kv;
+    q.a = h->a_norm; q.kv = Lw.kv; q.a_out = qf_l; q.notify = kDepHeads;
     add(q, SPEC_K_QKV, Lw.qkv.alg_bytes);
     Phase at{};
-    at.kind = PH_ATTN; at.layer = l; at.kv = Lw.kv;
+    at.kind = PH_ATTN; at.layer = l; at.kv = Lw.kv; at.a = qf_l; at.a_out = a_o_l; at.dep = kDepHeads;
     add(at, SPEC_K_ATTN, 0);
     Phase mg{};
-    mg.kind = PH_ATTN_MERGE; mg.layer = l;
+    mg.kind = PH_ATTN_MERGE; mg.layer = l; mg.a_out = a_o_l;
     add(mg, SPEC_K_ATTN_COMBINE, 0);
     Phase o = gemm_phase_desc(PH_RESID, l, Lw.o);
-    o.a = h->a_o; o.gain = Lw.ffn_norm; o.a_out = h->a_norm;
+    o.a = a_o_l; o.gain = Lw.ffn_norm; o.a_out = h->a_norm; o.dep = kDepOWin;
     add(o, SPEC_K_O, Lw.o.alg_bytes);
     if (!moe) {
       Phase g = gemm_phase_desc(PH_SWIGLU, l, Lw.gateup);
@@ -678,6 +698,16 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
     add(lm, SPEC_K_LMHEAD, h->lm_head.alg_bytes);
   }
   h->n_prog = (int)prog.size();
+  // grid barriers per pass (every phase but the first, except those fed by
+  // ready counters and, with the inline merge, the merge phases)
+  h->n_barriers_inline = h->n_barriers_merge = 0;
+  for (int i = 1; i < h->n_prog; ++i) {
+    const Phase& q = prog[i];
+    const bool dep_inline = q.dep != kDepNone || q.kind == PH_ATTN_MERGE;
+    const bool dep_merge = q.dep != kDepNone && q.dep != kDepOWin;
+    h->n_barriers_inline += dep_inline ? 0 : 1;
+    h->n_barriers_merge += dep_merge ? 0 : 1;
+  }
   for (int i = h->n_prog - 1, nx = h->n_prog; i >= 0; --i) {
     prog[i].next_gemm = nx;
     if (prog_kind_is_gemm(prog[i].kind)) nx = i;
@@ -792,7 +822,8 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   p.tokens = h->tokens_dev; p.page_table = h->page_table; p.rope_cs = h->rope_cs;
   p.x = h->x; p.ldx = h->ldx; p.ss = h->ss;
   p.a_norm = h->a_norm; p.a_o = h->a_o; p.a_act = h->a_act; p.a_act_slot = h->a_act_slot;
-  p.qf = h->qf; p.logits = h->logits; p.ldl = h->ldl;
+  p.logits = h->logits; p.ldl = h->ldl;
+  p.ready = h->ready; p.epoch = h->epoch + 1; p.qf_rt = h->qf_rt; p.o_wcols = h->o_wcols;
   p.st_max = h->st_max; p.st_sum = h->st_sum; p.st_idx = h->st_idx; p.n_stat = h->n_stat;
   p.pm = h->pm; p.ps = h->ps; p.pacc = h->pacc;
   p.rlog = h->rlog; p.ldr = h->ldr; p.ey = h->ey; p.ey_slot = h->ey_slot; p.ldy = h->ldx;
@@ -809,7 +840,8 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
     h->broken = true;
     return fail(h, SPEC_EHIP, std::string("pass launch: ") + hipGetErrorString(he));
   }
-  h->bar_gen += (unsigned long long)(h->n_prog - 1 - (p.attn_inline ? c.n_layers : 0));
+  h->bar_gen += (unsigned long long)(p.attn_inline ? h->n_barriers_inline : h->n_barriers_merge);
+  h->epoch = p.epoch;
   if (h->profiling) he = hipEventRecord(h->ev[1], h->stream);
   AcceptParams a{};
   a.k = k; a.V = c.vocab; a.L = L; a.mode = mode; a.n_stat = h->n_stat;

@@ -79,9 +79,18 @@ struct Phase {
   const float* gain;      // RESID / COMBINE: gain of the next norm
   uint4* a_out; long long a_out_slot;
   const float* bias;      // ROUTE: router bias
-  void* kv;               // ATTN: the layer's KV pages
+  void* kv;               // QKV / ATTN: the layer's KV pages
   int next_gemm;          // index of the next weight-streaming phase (n_prog if none)
+  int dep;                // inputs: 0 after a grid barrier; else waits on this layer's
+                          // ready counters (kDepHeads / kDepOWin)
+  int notify;             // outputs announced on ready counters (kDepHeads)
 };
+// Ready counters per layer (64-bit, monotonic: pass e waits for e times the
+// expected count): KV heads' query / key / value blocks, and windows of the
+// O projection's input (merged heads).  Edges whose consumers depend on
+// many producers (a normalised row, a gate/up window) keep grid barriers.
+enum DepKind : int { kDepNone = 0, kDepHeads = 1, kDepOWin = 2 };
+constexpr int kReadyStride = 512;   // counters per layer: [0,256) KV heads, [256,512) O windows
 
 // Everything one pass needs; passed by value to the pass kernel.
 struct PassP {
@@ -101,7 +110,6 @@ struct PassP {
   float* ss;                 // [16][n_ss]
   uint4* a_norm;             // A operand of norm-fed GEMMs: x * gain, hi/lo fragments
   uint4* a_o;                // attention output, hi/lo fragments
-  uint4* qf;                 // rotated, scaled queries: [Hkv][kAttnRT][D/32][hi|lo][64] fragments
   uint4* a_act;              // SwiGLU output [slot][..], hi/lo fragments
   long long a_act_slot;      // uint4 per slot
   float* logits; int ldl;    // [16][ldl]
@@ -113,6 +121,10 @@ struct PassP {
   // split-K workspace and tickets
   float* ws; unsigned* tickets;
   unsigned* attn_tickets;     // [Hkv] groups finished per KV head (inline merge)
+  unsigned long long* ready;  // [n_layers][kReadyStride] ready counters
+  unsigned long long epoch;   // passes run by this handle, this one included
+  int o_wcols;                // input columns per window of the O projection
+  int qf_rt;                  // row tiles per KV head in the query fragments
   int attn_inline;           // 1: attention's last arrivers merge, the merge phase is skipped
   // grid barrier
   unsigned long long* bar; unsigned long long bar_base;
