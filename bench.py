@@ -62,8 +62,45 @@ def parse():
     ap.add_argument("--k-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 1 GiB device copy (the HBM counter calibration for --traffic-from)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: turn two rocprofv3 counter CSVs (FETCH_SIZE and WRITE_SIZE runs of "
+                         "bench.py --calib-copy) into " + os.path.relpath(TRAFFIC_FILE, ROOT))
     return ap.parse_args()
+
+
+def traffic_from(fetch_csv: str, write_csv: str, command: str):
+    """HBM bytes per pass-kernel launch from rocprofv3 counters (KiB per
+    dispatch), each scaled by what the same counter reads for the
+    calibration copy of 1 GiB read + 1 GiB written.  The pass-kernel value
+    is the median over its last dispatches (the timed k=8 steps)."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r.get("Counter_Name") == counter]
+        passes = [float(r["Counter_Value"]) for r in rows if "k_pass" in r["Kernel_Name"]]
+        copies = [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()]
+        if not passes or not copies:
+            raise SystemExit(f"{path}: no {counter} rows for the pass kernel or the calibration copy")
+        return statistics.median(passes[-8:]), max(copies)
+
+    fetch, fcopy = per_kernel(fetch_csv, "FETCH_SIZE")
+    write, wcopy = per_kernel(write_csv, "WRITE_SIZE")
+    gib_kib = float(1 << 20)
+    f_scale, w_scale = gib_kib / fcopy, gib_kib / wcopy
+    traffic = (fetch * f_scale + write * w_scale) * 1024.0
+    out = {"pass_source_sha256_16": source_digest(PASS_SOURCE),
+           "per_launch_bytes": {"pass": round(traffic)},
+           "fetch_kib_per_launch": fetch, "write_kib_per_launch": write,
+           "copy_fetch_kib": fcopy, "copy_write_kib": wcopy,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "command": command}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    log(f"[bench] traffic per pass launch: {traffic / 1e9:.3f} GB (fetch {fetch * f_scale / 2**20:.3f} GiB, "
+        f"write {write * w_scale / 2**20:.3f} GiB) -> {TRAFFIC_FILE}")
 
 
 class Session:
@@ -220,6 +257,9 @@ def cpu_baseline(wl, W, k: int, L: int, seconds: float, mean_accept: float):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        traffic_from(args.traffic_from[0], args.traffic_from[1], " ".join(sys.argv))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build measures the "
               "verification step on a single MI355X; multi-GPU sharding is a design note, not a code path.",
