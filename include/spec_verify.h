@@ -228,6 +228,14 @@ int spec_profile_read(const spec_verify_t* h, int64_t* launches, double* ms, dou
  * wait.  out: host array of 8 * SPEC_K_NCLASSES doubles. */
 int spec_profile_detail(const spec_verify_t* h, double* out);
 
+/* The per-workgroup stamps of the last profiled step (device wall clock,
+ * 100 MHz on MI355X): out[(phase * n_wg + wg) * 4 + j] for j = 0 start,
+ * 1 after staging, 2 after the stream, 3 end of work (same meaning as in
+ * spec_profile_detail; phases in program order).  *count (host, may be
+ * NULL) receives phases * n_wg * 4; out (host array of n uint64) may be
+ * NULL to ask for the count only; SPEC_ECAPACITY if n is smaller. */
+int spec_profile_raw(const spec_verify_t* h, uint64_t* out, int64_t n, int64_t* count);
+
 /* Like spec_verify_step, and additionally copies the residual stream after
  * every layer into trace_dev (device fp32 [n_layers][k+1][d_model], may be
  * NULL) and, for MoE models, the number of routed experts loaded by each

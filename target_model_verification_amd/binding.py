@@ -74,6 +74,7 @@ def _load():
         "spec_profile_enable": (I, [P, I]),
         "spec_profile_read": (I, [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(D), ctypes.POINTER(D)]),
         "spec_profile_detail": (I, [P, ctypes.POINTER(D)]),
+        "spec_profile_raw": (I, [P, ctypes.POINTER(ctypes.c_uint64), ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
         "spec_pass_bytes": (D, [P, I, I, I, ctypes.c_int64]),
     }
     for name, (res, args) in sig.items():
@@ -98,6 +99,7 @@ spec_verify_destroy = lib.spec_verify_destroy
 spec_profile_enable = lib.spec_profile_enable
 spec_profile_read = lib.spec_profile_read
 spec_profile_detail = lib.spec_profile_detail
+spec_profile_raw = lib.spec_profile_raw
 spec_pass_bytes = lib.spec_pass_bytes
 
 
@@ -231,6 +233,17 @@ class Verifier:
         return {KERNEL_CLASSES[i]: (tuple(float(out[8 * i + j]) for j in range(4)),
                                     tuple(float(out[8 * i + 4 + j]) for j in range(4)))
                 for i in range(SPEC_K_NCLASSES)}
+
+    def profile_raw(self) -> np.ndarray:
+        """Per-workgroup stamps of the last profiled step: [phases][n_wg][4]
+        device wall-clock ticks (flattened; see spec_profile_raw)."""
+        n = ctypes.c_int64()
+        spec_profile_raw(self.h, None, 0, ctypes.byref(n))
+        out = np.zeros(n.value, dtype=np.uint64)
+        rc = spec_profile_raw(self.h, out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), n.value, None)
+        if rc != SPEC_OK:
+            raise SpecError(rc, self.last_error())
+        return out
 
     def pass_bytes(self, L: int, k: int, mode: int = SPEC_ACCEPT_GREEDY, experts_loaded: int = 0) -> float:
         return spec_pass_bytes(self.h, L, k, mode, experts_loaded)

@@ -271,9 +271,10 @@ struct LCur {
   bool done;
 };
 
-// Loads the next batch (up to U chunks of the current segment) into the ring
-// and advances the cursor.  Slots past the batch re-read its last fragment
-// (they are not used); idle waves (unit past the matrix) skip the loads.
+// Loads the next batch (up to U chunks of the current segment) into the ring;
+// slots past the batch are zero (never read).  An idle wave (unit past the
+// matrix) loads nothing: its ring is zero and its compute is skipped, so the
+// ring is provably rewritten by every batch and dead between phases.
 template <int WF, int TPU>
 __device__ __forceinline__ void next_batch(const Mat& M, const Lin& L, LCur& l, int u1, Ring& ring) {
   using F = Fmt<WF, TPU>;
@@ -282,34 +283,34 @@ __device__ __forceinline__ void next_batch(const Mat& M, const Lin& L, LCur& l, 
   const int n = min(F::U, seg_left(q, u1));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (q.sg * kWaves + wave >= M.n_units) {
-    // idle wave: a defined ring (its compute is skipped), so the ring is
-    // provably overwritten by every batch and dead between phases
+  const bool live = q.sg * kWaves + wave < M.n_units;
+  const long long fi0 = (((long long)q.sg * M.nkc + (long long)q.win * M.win + q.c) * kWaves + wave) * TPU;
+  const char* wb = static_cast<const char*>(M.w) + (long long)q.e * M.w_stride + fi0 * 1024 + lane * 16;
+  const char* wb2 = static_cast<const char*>(M.w2) + (long long)q.e * M.w2_stride;
+  constexpr int RPC = TPU * (WF == W_F32 ? 2 : 1);   // ring slots per chunk
 #pragma unroll
-    for (int i = 0; i < kRing; ++i) {
-      ring.r[i] = u4{0u, 0u, 0u, 0u};
-      ring.s[i] = 0.f;
-    }
-  } else {
-    const long long fi0 = (((long long)q.sg * M.nkc + (long long)q.win * M.win + q.c) * kWaves + wave) * TPU;
-    const char* wb = static_cast<const char*>(M.w) + (long long)q.e * M.w_stride + fi0 * 1024 + lane * 16;
-    const char* wb2 = static_cast<const char*>(M.w2) + (long long)q.e * M.w2_stride;
-#pragma unroll
-    for (int i = 0; i < F::U; ++i) {
-      const int ii = i < n ? i : n - 1;
+  for (int i = 0; i < F::U; ++i) {
+    if (live && i < n) {   // (wave-uniform)
 #pragma unroll
       for (int t = 0; t < TPU; ++t) {
-        const long long fo = ((long long)ii * kWaves * TPU + t) * 1024;
+        const long long fo = ((long long)i * kWaves * TPU + t) * 1024;
         if constexpr (WF == W_F32) {
           ring.r[(i * TPU + t) * 2 + 0] = __builtin_nontemporal_load((gu4*)(wb + fo));
           ring.r[(i * TPU + t) * 2 + 1] = __builtin_nontemporal_load((gu4*)(wb2 + fi0 * 1024 + lane * 16 + fo));
         } else {
           ring.r[i * TPU + t] = __builtin_nontemporal_load((gu4*)(wb + fo));
           if constexpr (WF == W_INT4) {
-            const gu16* sp = (gu16*)(wb2 + (fi0 + (long long)ii * kWaves * TPU + t) * 32 + (lane & 15) * 2);
+            const gu16* sp = (gu16*)(wb2 + (fi0 + (long long)i * kWaves * TPU + t) * 32 + (lane & 15) * 2);
             ring.s[i * TPU + t] = (float)__builtin_bit_cast(_Float16, (uint16_t)*sp);
           }
         }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < RPC; ++t) ring.r[i * RPC + t] = u4{0u, 0u, 0u, 0u};
+      if constexpr (WF == W_INT4) {
+#pragma unroll
+        for (int t = 0; t < TPU; ++t) ring.s[i * TPU + t] = 0.f;
       }
     }
   }
@@ -594,9 +595,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
   LCur lc;
   lc.q = cur_at(L, u0);
   lc.done = false;
-  {
-    batch_advance(L, lc.q, min(F::U, seg_left(lc.q, u1)), u1, lc.done);
-  }
+  batch_advance(L, lc.q, min(F::U, seg_left(lc.q, u1)), u1, lc.done);
 
   Cur cc = cur_at(L, u0);
   f32x4 acc[TPU];
@@ -1025,21 +1024,19 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
     const int g = item / P.n_groups, grp = item % P.n_groups;
     const int gt0 = grp * kGroupPos;
     const int nsc = min(kGroupPages, (T - gt0 + kPage - 1) / kPage);   // sub-chunks holding positions
-    if (dep == kDepHeads) {
-      // this KV head's query fragments and new cache rows are written
-      if (tid == 0) ready_wait(ready + g, P.epoch * heads_expect(P), P.err);
-      __syncthreads();
-    }
+    // waits until this KV head's query fragments and new cache rows are written
+    auto wait_head = [&]() {
+      if (dep == kDepHeads) {
+        if (tid == 0) ready_wait(ready + g, P.epoch * heads_expect(P), P.err);
+        __syncthreads();
+      }
+    };
     const gu4* qsrc = (const gu4*)(qf + (long long)g * P.qf_rt * KDC * 2 * 64);
     // ---- query fragments: registers (one row tile) or LDS
     u4 qh[4], ql[4];
+    if constexpr (!ONE) wait_head();
     if constexpr (ONE) {
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc)
-        if (kc < KDC) {
-          qh[kc] = qsrc[(kc * 2 + 0) * 64 + lane];
-          ql[kc] = qsrc[(kc * 2 + 1) * 64 + lane];
-        }
+      // (loaded below, after the old positions' operands and the wait)
     } else {
       constexpr int QB = 8;
       for (int i0 = tid; i0 < RT * KDC * 2 * 64; i0 += kThreads * QB) {
@@ -1193,10 +1190,23 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
     };
 
     if constexpr (ONE) {
+      // sub-chunks wholly before L hold no new rows: their operands go out
+      // before the wait on this head's QKV blocks
+      const int n_old = min(nsc, max(0, (P.L - gt0) / kPage));
       u4 kr[NPF][4 * W], vr[NPF][2][2 * W];
 #pragma unroll
       for (int sc = 0; sc < NPF; ++sc)
-        if (sc < nsc) load_ops(sc, kr[sc], vr[sc]);
+        if (sc < n_old) load_ops(sc, kr[sc], vr[sc]);
+      wait_head();
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc)
+        if (kc < KDC) {
+          qh[kc] = qsrc[(kc * 2 + 0) * 64 + lane];
+          ql[kc] = qsrc[(kc * 2 + 1) * 64 + lane];
+        }
+#pragma unroll
+      for (int sc = 0; sc < NPF; ++sc)
+        if (sc >= n_old && sc < nsc) load_ops(sc, kr[sc], vr[sc]);
       __syncthreads();   // mrun / lrun initialised
       wstamp(wst, 1);
 #pragma unroll
@@ -1216,9 +1226,28 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
         if ((tid & 15) == 0) mrun[srow] = mx;
-        __syncthreads();
+        // per-sub-chunk sums (the four trees interleaved), added in order
+        float ls[kGroupPages];
+#pragma unroll
+        for (int sc = 0; sc < kGroupPages; ++sc) {
+          ls[sc] = 0.f;
+          if (sc < nsc) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float* pp = Ps + srow * PSW + sc * kPage + sq + e;
+              const float sv = *pp;
+              const float p = (mx == -INFINITY || sv == -INFINITY) ? 0.f : expf(sv - mx);
+              *pp = p;
+              ls[sc] += p;
+            }
+          }
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+          for (int sc = 0; sc < kGroupPages; ++sc) ls[sc] += __shfl_xor(ls[sc], o, 64);
         float l = 0.f;
-        for (int sc = 0; sc < nsc; ++sc) l += expsum(srow, sc * kPage);
+        for (int sc = 0; sc < nsc; ++sc) l += ls[sc];
         if ((tid & 15) == 0) lrun[srow] = l;
       }
       __syncthreads();

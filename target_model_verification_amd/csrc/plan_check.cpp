@@ -90,10 +90,9 @@ bool check_gemm_walk(const GemmShape& s, int G, size_t ws_floats, size_t n_ticke
         for (int w = 0; w < kWaves; ++w) {
           if (lq.sg * kWaves + w >= M.n_units) continue;   // idle wave: no loads
           const long long fi0 = (((long long)lq.sg * M.nkc + (long long)lq.win * M.win + lq.c) * kWaves + w) * s.tpu;
-          for (int i = 0; i < U; ++i) {
-            const int ii = i < n ? i : n - 1;
+          for (int i = 0; i < n; ++i) {   // slots past n are zero-filled
             for (int t = 0; t < s.tpu; ++t) {
-              const long long fi = fi0 + (long long)ii * kWaves * s.tpu + t;
+              const long long fi = fi0 + (long long)i * kWaves * s.tpu + t;
               if (fi < 0 || fi >= frags) return false;
             }
           }

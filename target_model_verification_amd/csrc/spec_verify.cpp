@@ -1039,6 +1039,16 @@ int spec_profile_enable(spec_verify_t* h, int32_t on) {
   return SPEC_OK;
 }
 
+int spec_profile_raw(const spec_verify_t* h, uint64_t* out, int64_t n, int64_t* count) {
+  if (!h) return SPEC_EINVAL;
+  const int64_t total = (int64_t)h->n_prog * h->n_wg * 4;
+  if (count) *count = total;
+  if (!out) return SPEC_OK;
+  if (n < total) return SPEC_ECAPACITY;
+  for (int64_t i = 0; i < total; ++i) out[i] = h->wstamps_host[i];
+  return SPEC_OK;
+}
+
 int spec_profile_detail(const spec_verify_t* h, double* out) {
   if (!h || !out) return SPEC_EINVAL;
   for (int i = 0; i < SPEC_K_NCLASSES; ++i)
