@@ -76,9 +76,9 @@ __device__ __forceinline__ u4 nib8_to_bf16(uint32_t d) {
 // Data one workgroup writes and another reads later in the same pass is
 // stored through to the device-coherent level (agent-scope relaxed atomic
 // stores, "sc1"): a signal then needs no L2 write-back, only each wave's
-// wait on its own stores.  Reads that follow a grid barrier are plain (the
-// barrier's acquire drops stale cache lines); reads that follow a ticket
-// instead of a barrier use agent-scope loads.
+// wait on its own stores.  Buffers rewritten during a pass are read with
+// agent-scope loads; buffers written once per pass may be read with plain
+// (L2-cached) loads, since no cache can hold an older copy of them.
 __device__ __forceinline__ void cst(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -97,6 +97,9 @@ __device__ __forceinline__ void cst4(float* p, f32x4 v) {   // p 16-byte aligned
 }
 __device__ __forceinline__ float cld(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int cld(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ f32x4 cld4(const float* p) {   // p 16-byte aligned
   unsigned long long* q = reinterpret_cast<unsigned long long*>(const_cast<float*>(p));
@@ -159,6 +162,15 @@ __device__ __forceinline__ void wstamp(unsigned long long* ws, int i) {
 // are 64-bit and monotonic over the handle's lifetime; the host passes the
 // generation reached before the launch.  Layout (u64, 128-byte lines):
 // group g at 16*g, top at 128, flag g at 16*(9+g).
+//
+// No acquire (L2 invalidation) follows the wait.  Data produced in a pass
+// and read by another workgroup is stored through to memory (agent-scope
+// stores) and read either with agent-scope loads (the residual stream, norm
+// partials, split-K partials, attention partials, MoE routing and expert
+// outputs) or from addresses written once per pass (the per-site A
+// operands, per-layer query fragments and cache rows), which no XCD's L2
+// can hold from earlier in the pass since the L2s start every launch
+// invalidated.
 struct GridBar {
   unsigned long long* bar;
   unsigned long long gen;
@@ -219,7 +231,6 @@ __device__ __forceinline__ void grid_sync(GridBar& gb, PF&& prefetch) {
         break;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   raw_barrier();
 }
@@ -329,6 +340,9 @@ struct GemmIO {
   void* kv;                  // QKV: the layer's cache pages
   unsigned long long* ready;  // this layer's ready counters
   int dep, notify;            // DepKind of the inputs / outputs
+  const float* ss_in;         // sum-of-squares partials of the input's norm
+  float* ss_out;              // RESID: partials of the next norm
+  float* ws; unsigned* tickets;   // the phase's split-K workspace bank
 };
 
 // Query element (block row j, query head h, dim d), already rotated and
@@ -374,7 +388,7 @@ __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const Gem
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * rg + i;
-      xv[i] = (row < P.m && col < M.N) ? P.x[(long long)row * P.ldx + col] : 0.f;
+      xv[i] = (row < P.m && col < M.N) ? cld(P.x + (long long)row * P.ldx + col) : 0.f;
     }
     const float gn = col < M.N ? io.gain[col] : 0.f;
     float sq[4];
@@ -399,7 +413,7 @@ __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const Gem
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 4 * rg + i;
-        if (row < P.m) cst(P.ss + row * P.n_ss + unit, sq[i]);
+        if (row < P.m) cst(io.ss_out + row * P.n_ss + unit, sq[i]);
       }
     }
   } else if constexpr (EPI == EPI_QKV) {
@@ -488,11 +502,11 @@ __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const Gem
 
 // Row scales 1/sqrt(mean(x^2) + eps) from the sum-of-squares partials, in
 // a fixed order (identical in every workgroup).
-__device__ __forceinline__ void row_scales(const PassP& P, float* rs) {
+__device__ __forceinline__ void row_scales(const PassP& P, const float* ss, float* rs) {
   const int t = threadIdx.x;
   const int row = t >> 4, j = t & 15;   // 16 rows x 16 lanes
   constexpr int B = 16;                 // loads in flight per lane
-  const float* src = P.ss + row * P.n_ss;
+  const float* src = ss + row * P.n_ss;
   float s = 0.f;
   if (row < P.m) {
     for (int i0 = j; i0 < P.n_ss; i0 += 16 * B) {
@@ -500,7 +514,7 @@ __device__ __forceinline__ void row_scales(const PassP& P, float* rs) {
 #pragma unroll
       for (int q = 0; q < B; ++q) {
         const int i = i0 + 16 * q;
-        v[q] = i < P.n_ss ? src[i] : 0.f;
+        v[q] = i < P.n_ss ? cld(src + i) : 0.f;
       }
 #pragma unroll
       for (int q = 0; q < B; ++q) s += v[q];
@@ -581,7 +595,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     wait_window(P, io, sw);
     stage_window<WF>(L, io, sk, sw, smem);
   }
-  if (EPI == EPI_SWIGLU || EPI == EPI_LOGITS || EPI == EPI_QKV || (EPI == EPI_STORE && io.scale)) row_scales(P, C->rs);
+  if (EPI == EPI_SWIGLU || EPI == EPI_LOGITS || EPI == EPI_QKV || (EPI == EPI_STORE && io.scale)) row_scales(P, io.ss_in, C->rs);
   __builtin_amdgcn_s_waitcnt(0);   // the window's direct loads
   __syncthreads();
   wstamp(wst, 1);
@@ -672,7 +686,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
       if (nseg == 1) {
         epilogue<WF, EPI, TPU>(P, M, io, C->rs, cc.slot, cc.sg * kWaves + wave, acc);
       } else {
-        float* p = P.ws + ((((long long)cc.slot * M.n_sg + cc.sg) * M.max_seg + idx) * kWaves + wave) * TPU * 256;
+        float* p = io.ws + ((((long long)cc.slot * M.n_sg + cc.sg) * M.max_seg + idx) * kWaves + wave) * TPU * 256;
 #pragma unroll
         for (int t = 0; t < TPU; ++t) cst4(p + t * 256 + lane * 4, acc[t]);
       }
@@ -709,7 +723,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     const int e = C->pend[k];
     const int s = (e >> 20) & 0x7ff, sg = e & 0xfffff;
     if (e < 0) notify_block(P, io, sg);
-    else __hip_atomic_fetch_add(P.tickets + (long long)s * M.n_sg + sg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else __hip_atomic_fetch_add(io.tickets + (long long)s * M.n_sg + sg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const int nb = L.n_slots * M.n_sg;
   const int b0 = range_begin(nb, g, G), b1 = range_begin(nb, g + 1, G);
@@ -720,7 +734,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     seg_info(L, s, sg, 0, g, G, idx, n);
     if (n == 1) continue;   // finished inside the stream
     if (threadIdx.x == 0) {
-      unsigned* t = P.tickets + b;
+      unsigned* t = io.tickets + b;
       unsigned spins = 0;
       while (__hip_atomic_load(t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)n) {
         __builtin_amdgcn_s_sleep(1);
@@ -737,7 +751,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     f32x4 sum[TPU];
 #pragma unroll
     for (int t = 0; t < TPU; ++t) sum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const float* p = P.ws + ((((long long)s * M.n_sg + sg) * M.max_seg) * kWaves + wave) * TPU * 256 + lane * 4;
+    const float* p = io.ws + ((((long long)s * M.n_sg + sg) * M.max_seg) * kWaves + wave) * TPU * 256 + lane * 4;
     for (int j0 = 0; j0 < n; j0 += RB) {
       f32x4 v[RB][TPU];
 #pragma unroll
@@ -789,7 +803,7 @@ __device__ __forceinline__ void gemm_prefetch(const Mat M, const SlotMap sm, boo
 
 // ------------------------------------------------------------ embedding
 // x[j] = E[t_j]; A operand x * gain0; sum-of-squares partials per 16 columns.
-__device__ __forceinline__ void embed_phase(const PassP& P, bool emb_f32) {
+__device__ __forceinline__ void embed_phase(const PassP& P, bool emb_f32, uint4* a_out, float* ss_out) {
   const int n_tiles = (P.d + 15) / 16;
   const int t = threadIdx.x;
   const int row = t >> 4, cl = t & 15;
@@ -803,11 +817,11 @@ __device__ __forceinline__ void embed_phase(const PassP& P, bool emb_f32) {
                   : bf2f(static_cast<const uint16_t*>(P.embed)[tok * P.d + col]);
       cst(P.x + (long long)row * P.ldx + col, v);
     }
-    if (col < P.d) afrag_put(P.a_norm, row, col, v * P.gain0[col]);
+    if (col < P.d) afrag_put(a_out, row, col, v * P.gain0[col]);
     float sq = v * v;
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o, 64);
-    if (cl == 0 && row < P.m) cst(P.ss + row * P.n_ss + tile, sq);
+    if (cl == 0 && row < P.m) cst(ss_out + row * P.n_ss + tile, sq);
   }
 }
 
@@ -861,7 +875,7 @@ __device__ __forceinline__ float attn_merge_one(const PassP& P, int g, int r, in
   for (int c0 = 0; c0 < NG; c0 += B) {
     float v[B];
 #pragma unroll
-    for (int q = 0; q < B; ++q) v[q] = c0 + q < NG ? P.pm[base + (long long)(c0 + q) * R] : -INFINITY;
+    for (int q = 0; q < B; ++q) v[q] = c0 + q < NG ? cld(P.pm + base + (long long)(c0 + q) * R) : -INFINITY;
 #pragma unroll
     for (int q = 0; q < B; ++q) M = fmaxf(M, v[q]);
   }
@@ -872,9 +886,9 @@ __device__ __forceinline__ float attn_merge_one(const PassP& P, int g, int r, in
     for (int q = 0; q < B; ++q) {
       const bool ok = c0 + q < NG;
       const long long pi = base + (long long)(c0 + q) * R;
-      vm[q] = ok ? P.pm[pi] : -INFINITY;
-      vs[q] = ok ? P.ps[pi] : 0.f;
-      va[q] = ok ? P.pacc[pi * D + d] : 0.f;
+      vm[q] = ok ? cld(P.pm + pi) : -INFINITY;
+      vs[q] = ok ? cld(P.ps + pi) : 0.f;
+      va[q] = ok ? cld(P.pacc + pi * D + d) : 0.f;
     }
 #pragma unroll
     for (int q = 0; q < B; ++q) {
@@ -1382,7 +1396,7 @@ __device__ __forceinline__ void route_block(const PassP& P, const float* bias, u
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
-      z[i] = e < P.E ? P.rlog[row * P.ldr + e] + bias[e] : -INFINITY;
+      z[i] = e < P.E ? cld(P.rlog + row * P.ldr + e) + bias[e] : -INFINITY;
       mx = fmaxf(mx, z[i]);
     }
 #pragma unroll
@@ -1451,13 +1465,14 @@ __device__ __forceinline__ void route_block(const PassP& P, const float* bias, u
 
 // x_j += sum_r w_{j,r} y[slot(sel_{j,r})]_j + sum_s y[shared slot s]_j, in
 // rank order then shared; new sum-of-squares partials and next A operand.
-__device__ __forceinline__ void moe_combine_phase(const PassP& P, const float* next_gain, float* trace) {
+__device__ __forceinline__ void moe_combine_phase(const PassP& P, const float* next_gain, float* trace, uint4* a_out,
+                                                  float* ss_out) {
   const int n_tiles = (P.d + 15) / 16;
   const int t = threadIdx.x;
   const int row = t >> 4, cl = t & 15;
   const int* rec = P.route;
   const int E = P.E, K = P.top_k;
-  const int uc = rec[0];
+  const int uc = cld(rec);
   for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
     if (t >= 256) continue;
     const int col = tile * 16 + cl;
@@ -1465,21 +1480,21 @@ __device__ __forceinline__ void moe_combine_phase(const PassP& P, const float* n
     if (row < P.m && col < P.d) {
       float y = 0.f;
       for (int r = 0; r < K; ++r) {
-        const int e = rec[1 + 2 * E + row * K + r];
-        const float w = reinterpret_cast<const float*>(rec)[1 + 2 * E + 16 * K + row * K + r];
-        const int s = rec[1 + E + e];
-        y += w * P.ey[(long long)s * P.ey_slot + (long long)row * P.ldy + col];
+        const int e = cld(rec + 1 + 2 * E + row * K + r);
+        const float w = cld(reinterpret_cast<const float*>(rec) + 1 + 2 * E + 16 * K + row * K + r);
+        const int s = cld(rec + 1 + E + e);
+        y += w * cld(P.ey + (long long)s * P.ey_slot + (long long)row * P.ldy + col);
       }
-      for (int s = 0; s < P.n_shared; ++s) y += P.ey[(long long)(uc + s) * P.ey_slot + (long long)row * P.ldy + col];
-      v = P.x[(long long)row * P.ldx + col] + y;
+      for (int s = 0; s < P.n_shared; ++s) y += cld(P.ey + (long long)(uc + s) * P.ey_slot + (long long)row * P.ldy + col);
+      v = cld(P.x + (long long)row * P.ldx + col) + y;
       cst(P.x + (long long)row * P.ldx + col, v);
       if (trace) trace[(long long)row * P.d + col] = v;
     }
-    if (col < P.d) afrag_put(P.a_norm, row, col, v * next_gain[col]);
+    if (col < P.d) afrag_put(a_out, row, col, v * next_gain[col]);
     float sq = v * v;
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o, 64);
-    if (cl == 0 && row < P.m) cst(P.ss + row * P.n_ss + tile, sq);
+    if (cl == 0 && row < P.m) cst(ss_out + row * P.n_ss + tile, sq);
   }
 }
 
@@ -1512,6 +1527,8 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
     io.gain = d->gain; io.a_out = d->a_out; io.a_out_slot = d->a_out_slot;
     io.trace = (d->trace && P.trace) ? P.trace + (long long)d->layer * P.m * P.d : nullptr;
     io.ready = P.ready + (long long)max(d->layer, 0) * kReadyStride;
+    io.ss_in = d->ss_in; io.ss_out = d->ss_out;
+    io.ws = d->ws; io.tickets = d->tickets;
     io.dep = d->dep;
     io.notify = d->notify;
     // the O projection waits on merged heads only when attention merges
@@ -1537,7 +1554,7 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
     switch (kind) {
       case PH_EMBED:
         sync([] {});
-        embed_phase(P, WF == W_F32);
+        embed_phase(P, WF == W_F32, d->a_out, d->ss_out);
         break;
       case PH_STORE: {
         const SlotMap sm = d->slot_mode ? slots : dense;
@@ -1595,7 +1612,7 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
         break;
       case PH_COMBINE:
         sync([] {});
-        moe_combine_phase(P, d->gain, io.trace);
+        moe_combine_phase(P, d->gain, io.trace, d->a_out, d->ss_out);
         break;
       default:
         sync([] {});

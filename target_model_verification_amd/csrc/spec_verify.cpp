@@ -64,7 +64,8 @@ struct spec_verify {
   float *x = nullptr, *ss = nullptr, *logits = nullptr;
   uint4* qf = nullptr;     // attention query fragments
   uint4 *a_norm = nullptr, *a_o = nullptr, *a_act = nullptr;
-  long long a_act_slot = 0;
+  long long a_act_slot = 0, a_act_layer = 0;   // uint4 per slot / per layer
+  long long a_norm_site = 0, ss_site = 0;       // uint4 / floats per norm site
   float *st_max = nullptr, *st_sum = nullptr;
   int* st_idx = nullptr;
   float *pm = nullptr, *ps = nullptr, *pacc = nullptr;
@@ -608,13 +609,20 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   if ((rc = dalloc_z(h, &h->qf, (size_t)h->qf_layer * c.n_layers))) return rc;
   if ((rc = dalloc_z(h, &h->ready, (size_t)kReadyStride * c.n_layers))) return rc;
   h->o_wcols = plan.o.M.win * (h->wfmt == W_INT4 ? kGroupK : kChunkK);
-  if ((rc = dalloc_z(h, &h->ss, 16 * (size_t)h->n_ss))) return rc;
+  // norm sites: 2l = input of layer l's QKV, 2l+1 = input of its FFN /
+  // router, 2L = input of the LM head; each site's A operand and
+  // sum-of-squares partials are written once per pass
+  const int n_sites = 2 * c.n_layers + 1;
+  h->ss_site = 16LL * h->n_ss;
+  if ((rc = dalloc_z(h, &h->ss, (size_t)h->ss_site * n_sites))) return rc;
   if ((rc = dalloc_z(h, &h->logits, 16 * (size_t)h->ldl))) return rc;
-  if ((rc = dalloc_z(h, &h->a_norm, (size_t)plan.a_norm))) return rc;
+  h->a_norm_site = plan.a_norm;
+  if ((rc = dalloc_z(h, &h->a_norm, (size_t)plan.a_norm * n_sites))) return rc;
   h->a_o_layer = plan.a_o;
   if ((rc = dalloc_z(h, &h->a_o, (size_t)plan.a_o * c.n_layers))) return rc;
   h->a_act_slot = plan.a_act_slot;
-  if ((rc = dalloc_z(h, &h->a_act, (size_t)h->a_act_slot * n_slots_max))) return rc;
+  h->a_act_layer = h->a_act_slot * n_slots_max;
+  if ((rc = dalloc_z(h, &h->a_act, (size_t)h->a_act_layer * c.n_layers))) return rc;
   if ((rc = dalloc_z(h, &h->st_max, 16 * (size_t)h->n_stat))) return rc;
   if ((rc = dalloc_z(h, &h->st_sum, 16 * (size_t)h->n_stat))) return rc;
   if ((rc = dalloc_z(h, &h->st_idx, 16 * (size_t)h->n_stat))) return rc;
@@ -623,8 +631,11 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   if ((rc = dalloc_z(h, &h->pm, Hkv * max_groups * Rmax))) return rc;
   if ((rc = dalloc_z(h, &h->ps, Hkv * max_groups * Rmax))) return rc;
   if ((rc = dalloc_z(h, &h->pacc, Hkv * max_groups * Rmax * D))) return rc;
-  if ((rc = dalloc_z(h, &h->ws, plan.ws_floats))) return rc;
-  if ((rc = dalloc_z(h, &h->tickets, plan.n_tickets))) return rc;
+  // two split-K banks, alternating between consecutive weight-streaming
+  // phases (a phase fed over ready counters may start while its
+  // predecessor's reductions still run)
+  if ((rc = dalloc_z(h, &h->ws, 2 * plan.ws_floats))) return rc;
+  if ((rc = dalloc_z(h, &h->tickets, 2 * plan.n_tickets))) return rc;
   if ((rc = dalloc_z(h, &h->attn_tickets, (size_t)Hkv + 16))) return rc;
   if ((rc = dalloc_z(h, &h->bar, 512))) return rc;
   if ((rc = dalloc_z(h, &h->tokens_dev, 16))) return rc;
@@ -652,13 +663,18 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
     p.kind = PH_EMBED;
     add(p, SPEC_K_EMBED, 0);
   }
+  auto a_site = [&](int i) { return h->a_norm + (long long)i * h->a_norm_site; };
+  auto ss_site = [&](int i) { return h->ss + (long long)i * h->ss_site; };
+  prog[0].a_out = a_site(0);
+  prog[0].ss_out = ss_site(0);
   for (int l = 0; l < c.n_layers; ++l) {
     HostLayer& Lw = h->layers[l];
     const float* next_gain = l + 1 < c.n_layers ? h->layers[l + 1].attn_norm : h->final_norm;
+    uint4* act_l = h->a_act + (long long)l * h->a_act_layer;
     uint4* qf_l = h->qf + (long long)l * h->qf_layer;
     uint4* a_o_l = h->a_o + (long long)l * h->a_o_layer;
     Phase q = gemm_phase_desc(PH_QKV, l, Lw.qkv);
-    q.a = h->a_norm; q.kv = Lw.kv; q.a_out = qf_l; q.notify = kDepHeads;
+    q.a = a_site(2 * l); q.ss_in = ss_site(2 * l); q.kv = Lw.kv; q.a_out = qf_l; q.notify = kDepHeads;
     add(q, SPEC_K_QKV, Lw.qkv.alg_bytes);
     Phase at{};
     at.kind = PH_ATTN; at.layer = l; at.kv = Lw.kv; at.a = qf_l; at.a_out = a_o_l; at.dep = kDepHeads;
@@ -667,37 +683,46 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
     mg.kind = PH_ATTN_MERGE; mg.layer = l; mg.a_out = a_o_l;
     add(mg, SPEC_K_ATTN_COMBINE, 0);
     Phase o = gemm_phase_desc(PH_RESID, l, Lw.o);
-    o.a = a_o_l; o.gain = Lw.ffn_norm; o.a_out = h->a_norm; o.dep = kDepOWin;
+    o.a = a_o_l; o.gain = Lw.ffn_norm; o.a_out = a_site(2 * l + 1); o.ss_out = ss_site(2 * l + 1); o.dep = kDepOWin;
     add(o, SPEC_K_O, Lw.o.alg_bytes);
     if (!moe) {
       Phase g = gemm_phase_desc(PH_SWIGLU, l, Lw.gateup);
-      g.a = h->a_norm; g.a_out = h->a_act;
+      g.a = a_site(2 * l + 1); g.ss_in = ss_site(2 * l + 1); g.a_out = act_l;
       add(g, SPEC_K_GATEUP, Lw.gateup.alg_bytes);
       Phase dn = gemm_phase_desc(PH_RESID, l, Lw.down);
-      dn.a = h->a_act; dn.gain = next_gain; dn.a_out = h->a_norm; dn.trace = 1;
+      dn.a = act_l; dn.gain = next_gain; dn.a_out = a_site(2 * l + 2); dn.ss_out = ss_site(2 * l + 2); dn.trace = 1;
       add(dn, SPEC_K_DOWN, Lw.down.alg_bytes);
     } else {
       Phase r = gemm_phase_desc(PH_STORE, l, Lw.router);
-      r.a = h->a_norm; r.out = h->rlog; r.ldo = h->ldr; r.scale = 1;
+      r.a = a_site(2 * l + 1); r.ss_in = ss_site(2 * l + 1); r.out = h->rlog; r.ldo = h->ldr; r.scale = 1;
       add(r, SPEC_K_ROUTER, Lw.router.alg_bytes);
       Phase g = gemm_phase_desc(PH_ROUTE_SWIGLU, l, Lw.ex_gateup);
-      g.slot_mode = 1; g.a = h->a_norm; g.a_out = h->a_act; g.a_out_slot = h->a_act_slot; g.bias = Lw.router_bias;
+      g.slot_mode = 1; g.a = a_site(2 * l + 1); g.ss_in = ss_site(2 * l + 1); g.a_out = act_l;
+      g.a_out_slot = h->a_act_slot; g.bias = Lw.router_bias;
       add(g, SPEC_K_EXPERT_GATEUP, Lw.ex_gateup.alg_bytes);
       Phase dn = gemm_phase_desc(PH_STORE, l, Lw.ex_down);
-      dn.slot_mode = 2; dn.a = h->a_act; dn.a_slot = h->a_act_slot; dn.out = h->ey; dn.ldo = h->ldx;
+      dn.slot_mode = 2; dn.a = act_l; dn.a_slot = h->a_act_slot; dn.out = h->ey; dn.ldo = h->ldx;
       dn.out_slot = h->ey_slot; dn.scale = 0;
       add(dn, SPEC_K_EXPERT_DOWN, Lw.ex_down.alg_bytes);
       Phase cb{};
       cb.kind = PH_COMBINE; cb.layer = l; cb.gain = next_gain; cb.trace = 1;
+      cb.a_out = a_site(2 * l + 2); cb.ss_out = ss_site(2 * l + 2);
       add(cb, SPEC_K_MOE_COMBINE, 0);
     }
   }
   {
     Phase lm = gemm_phase_desc(PH_LOGITS, -1, h->lm_head);
-    lm.a = h->a_norm; lm.out = h->logits; lm.ldo = h->ldl;
+    lm.a = a_site(2 * c.n_layers); lm.ss_in = ss_site(2 * c.n_layers); lm.out = h->logits; lm.ldo = h->ldl;
     add(lm, SPEC_K_LMHEAD, h->lm_head.alg_bytes);
   }
   h->n_prog = (int)prog.size();
+  // split-K banks alternate between consecutive weight-streaming phases
+  for (int i = 0, ng = 0; i < h->n_prog; ++i) {
+    if (!prog_kind_is_gemm(prog[i].kind)) continue;
+    const int bank = ng++ & 1;
+    prog[i].ws = h->ws + (size_t)bank * plan.ws_floats;
+    prog[i].tickets = h->tickets + (size_t)bank * plan.n_tickets;
+  }
   // grid barriers per pass (every phase but the first, except those fed by
   // ready counters and, with the inline merge, the merge phases)
   h->n_barriers_inline = h->n_barriers_merge = 0;
@@ -820,15 +845,13 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   p.prog = h->prog; p.n_prog = h->n_prog;
   p.embed = h->embed; p.gain0 = h->layers[0].attn_norm;
   p.tokens = h->tokens_dev; p.page_table = h->page_table; p.rope_cs = h->rope_cs;
-  p.x = h->x; p.ldx = h->ldx; p.ss = h->ss;
-  p.a_norm = h->a_norm; p.a_o = h->a_o; p.a_act = h->a_act; p.a_act_slot = h->a_act_slot;
+  p.x = h->x; p.ldx = h->ldx;
   p.logits = h->logits; p.ldl = h->ldl;
   p.ready = h->ready; p.epoch = h->epoch + 1; p.qf_rt = h->qf_rt; p.o_wcols = h->o_wcols;
   p.st_max = h->st_max; p.st_sum = h->st_sum; p.st_idx = h->st_idx; p.n_stat = h->n_stat;
   p.pm = h->pm; p.ps = h->ps; p.pacc = h->pacc;
   p.rlog = h->rlog; p.ldr = h->ldr; p.ey = h->ey; p.ey_slot = h->ey_slot; p.ldy = h->ldx;
   p.route = h->route;
-  p.ws = h->ws; p.tickets = h->tickets;
   p.bar = h->bar; p.bar_base = h->bar_gen; p.err = h->result_dev + 3;
   p.trace = trace_dev; p.union_hist = union_rec;
   p.stamps = h->profiling ? h->stamps_dev : nullptr;

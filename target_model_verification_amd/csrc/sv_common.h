@@ -84,6 +84,10 @@ struct Phase {
   int dep;                // inputs: 0 after a grid barrier; else waits on this layer's
                           // ready counters (kDepHeads / kDepOWin)
   int notify;             // outputs announced on ready counters (kDepHeads)
+  const float* ss_in;     // sum-of-squares partials of the input's norm (row scales)
+  float* ss_out;          // EMBED / RESID / COMBINE: partials of the next norm
+  float* ws;              // split-K workspace bank (GEMM phases; a phase that may
+  unsigned* tickets;      // overlap its predecessor's reductions uses the other bank)
 };
 // Ready counters per layer (64-bit, monotonic: pass e waits for e times the
 // expected count): KV heads' query / key / value blocks, and windows of the
@@ -105,21 +109,14 @@ struct PassP {
   const int* tokens;         // [m]
   const int* page_table;
   const float* rope_cs;      // [max_ctx][D/2][2]
-  // activations
+  // activations (A operands and norm partials are per phase, in the program)
   float* x; int ldx;         // residual stream [16][ldx]
-  float* ss;                 // [16][n_ss]
-  uint4* a_norm;             // A operand of norm-fed GEMMs: x * gain, hi/lo fragments
-  uint4* a_o;                // attention output, hi/lo fragments
-  uint4* a_act;              // SwiGLU output [slot][..], hi/lo fragments
-  long long a_act_slot;      // uint4 per slot
   float* logits; int ldl;    // [16][ldl]
   float* st_max; float* st_sum; int* st_idx; int n_stat;   // per 16-column tile of the LM head
   float* pm; float* ps; float* pacc;                      // attention partials
   float* rlog; int ldr;      // MoE router logits [16][ldr]
   float* ey; long long ey_slot; int ldy;                  // expert outputs [slot][16][ldy]
   int* route;                // MoE routing record (route_words)
-  // split-K workspace and tickets
-  float* ws; unsigned* tickets;
   unsigned* attn_tickets;     // [Hkv] groups finished per KV head (inline merge)
   unsigned long long* ready;  // [n_layers][kReadyStride] ready counters
   unsigned long long epoch;   // passes run by this handle, this one included
