@@ -367,10 +367,34 @@ __device__ __forceinline__ void kv_put(void* kv, long long i, float v) {
   else cst16(static_cast<uint16_t*>(kv) + i, (uint16_t)f2bf(v));
 }
 
+// Rotary factors and cache pages of one QKV unit's rows (they depend only
+// on the unit, so a reducer loads them before it waits for the partials).
+struct QkvPre {
+  float cs[4], sn[4];
+  long long pg[4];
+};
+__device__ __forceinline__ void qkv_pre(const PassP& P, int unit, QkvPre& q) {
+  const int lane = threadIdx.x & 63;
+  const int col = unit * kTileN + (lane & 15), rg = lane >> 4;
+  const int D = P.D, H = D >> 1;
+  const int qc = P.Hq * D, kc = P.Hkv * D;
+  const bool rot_col = col < qc + kc;
+  const int c2 = col < qc ? col : col - qc;
+  const int ii = (c2 % D) >> 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = P.L + min(4 * rg + i, P.m - 1);
+    q.pg[i] = (long long)P.page_table[t / kPage] * P.Hkv;
+    q.cs[i] = rot_col ? P.rope_cs[((long long)t * H + ii) * 2 + 0] : 0.f;
+    q.sn[i] = rot_col ? P.rope_cs[((long long)t * H + ii) * 2 + 1] : 0.f;
+  }
+}
+
 // Epilogue of one finished unit (one wave, acc[t] = tile t of the unit).
+// QKV takes the unit's rotary factors and pages (qkv_pre).
 template <int WF, int EPI, int TPU>
 __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const GemmIO& io, const float* rs, int slot,
-                                         int unit, f32x4 (&acc)[TPU]) {
+                                         int unit, f32x4 (&acc)[TPU], const QkvPre* qp = nullptr) {
   const int lane = threadIdx.x & 63;
   const int cl = lane & 15, rg = lane >> 4;
   if constexpr (EPI == EPI_STORE) {
@@ -427,18 +451,15 @@ __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const Gem
     const bool rot_col = col < qc + kc;
     const int c2 = col < qc ? col : (rot_col ? col - qc : col - qc - kc);
     const int head = c2 / D, p = c2 - head * D, ii = p >> 1, odd = p & 1;
-    // every load first (the stores below could alias later loads)
-    float v[4], pv[4], cs[4], sn[4];
-    long long pg[4];
+    const float* cs = qp->cs;
+    const float* sn = qp->sn;
+    const long long* pg = qp->pg;
+    float v[4], pv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * rg + i;
       v[i] = rs[row] * acc[0][i];
       pv[i] = __shfl_xor(v[i], 1, 64);
-      const int t = P.L + min(row, P.m - 1);
-      pg[i] = (long long)P.page_table[t / kPage] * P.Hkv;
-      cs[i] = rot_col ? P.rope_cs[((long long)t * H + ii) * 2 + 0] : 0.f;
-      sn[i] = rot_col ? P.rope_cs[((long long)t * H + ii) * 2 + 1] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -684,7 +705,9 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     seg_info(L, cc.slot, cc.sg, cc.win, g, G, idx, nseg);
     if (live) {
       if (nseg == 1) {
-        epilogue<WF, EPI, TPU>(P, M, io, C->rs, cc.slot, cc.sg * kWaves + wave, acc);
+        QkvPre qp;
+        if constexpr (EPI == EPI_QKV) qkv_pre(P, cc.sg * kWaves + wave, qp);
+        epilogue<WF, EPI, TPU>(P, M, io, C->rs, cc.slot, cc.sg * kWaves + wave, acc, &qp);
       } else {
         float* p = io.ws + ((((long long)cc.slot * M.n_sg + cc.sg) * M.max_seg + idx) * kWaves + wave) * TPU * 256;
 #pragma unroll
@@ -733,6 +756,10 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     int idx, n;
     seg_info(L, s, sg, 0, g, G, idx, n);
     if (n == 1) continue;   // finished inside the stream
+    QkvPre qp;
+    if constexpr (EPI == EPI_QKV) {
+      if (sg * kWaves + wave < M.n_units) qkv_pre(P, sg * kWaves + wave, qp);
+    }
     if (threadIdx.x == 0) {
       unsigned* t = io.tickets + b;
       unsigned spins = 0;
@@ -769,7 +796,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
         }
       }
     }
-    epilogue<WF, EPI, TPU>(P, M, io, C->rs, s, unit, sum);
+    epilogue<WF, EPI, TPU>(P, M, io, C->rs, s, unit, sum, &qp);
     }
     if (io.notify) {
       release_all_waves();
