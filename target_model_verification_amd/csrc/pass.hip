@@ -45,6 +45,13 @@ typedef __attribute__((address_space(1))) const u4 gu4;
 typedef __attribute__((address_space(1))) const uint16_t gu16;
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
+// A generic pointer known to address global memory, as a global-space
+// pointer: its accesses then compile to global (not flat) instructions,
+// which never hold up the LDS counter.
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* glb(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
 
 enum Epi : int { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LOGITS = 3, EPI_QKV = 4 };
 
@@ -80,31 +87,31 @@ __device__ __forceinline__ u4 nib8_to_bf16(uint32_t d) {
 // agent-scope loads; buffers written once per pass may be read with plain
 // (L2-cached) loads, since no cache can hold an older copy of them.
 __device__ __forceinline__ void cst(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(glb(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void cst(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(glb(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void cst16(uint16_t* p, uint16_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(glb(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void cst4(float* p, f32x4 v) {   // p 16-byte aligned
   unsigned long long* q = reinterpret_cast<unsigned long long*>(p);
   const unsigned long long a = (unsigned long long)__float_as_uint(v[0]) | (unsigned long long)__float_as_uint(v[1]) << 32;
   const unsigned long long b = (unsigned long long)__float_as_uint(v[2]) | (unsigned long long)__float_as_uint(v[3]) << 32;
-  __hip_atomic_store(q, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(glb(q), a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(glb(q + 1), b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float cld(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(glb(const_cast<float*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int cld(const int* p) {
-  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(glb(const_cast<int*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ f32x4 cld4(const float* p) {   // p 16-byte aligned
   unsigned long long* q = reinterpret_cast<unsigned long long*>(const_cast<float*>(p));
-  const unsigned long long a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const unsigned long long b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long a = __hip_atomic_load(glb(q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned long long b = __hip_atomic_load(glb(q + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return f32x4{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)), __uint_as_float((uint32_t)b),
                __uint_as_float((uint32_t)(b >> 32))};
 }
@@ -114,14 +121,14 @@ __device__ __forceinline__ f32x4 cld4(const float* p) {   // p 16-byte aligned
 // pass's target (bounded, like the grid barrier: on a timeout it raises
 // the error flag and goes on).
 __device__ __forceinline__ void ready_add(unsigned long long* c, unsigned long long n = 1) {
-  __hip_atomic_fetch_add(c, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_fetch_add(glb(c), n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void ready_wait(const unsigned long long* c, unsigned long long target, int* err) {
   unsigned spins = 0;
-  while (__hip_atomic_load(const_cast<unsigned long long*>(c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+  while (__hip_atomic_load(glb(const_cast<unsigned long long*>(c)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
     __builtin_amdgcn_s_sleep(1);
     if (++spins == (1u << 24)) {
-      __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(glb(err), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
   }
@@ -207,13 +214,13 @@ __device__ __forceinline__ void grid_sync(GridBar& gb, PF&& prefetch) {
     // (no release fence: the phase's shared data was stored through, and
     // every wave waited for its stores before the workgroup barrier)
     const unsigned long long old =
-        __hip_atomic_fetch_add(gb.bar + 16 * g, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(glb(gb.bar + 16 * g), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == gb.gen * ng - 1) {
       const unsigned long long o2 =
-          __hip_atomic_fetch_add(gb.bar + 128, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_add(glb(gb.bar + 128), 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (o2 == gb.gen * ngr - 1) {
         for (int x = 0; x < 8; ++x)
-          __hip_atomic_store(gb.bar + 16 * (9 + x), gb.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(glb(gb.bar + 16 * (9 + x)), gb.gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -223,11 +230,11 @@ __device__ __forceinline__ void grid_sync(GridBar& gb, PF&& prefetch) {
   if (threadIdx.x == 0 && !gb.aborted) {
     const unsigned g = blockIdx.x & 7u;
     unsigned spins = 0;
-    while (__hip_atomic_load(gb.bar + 16 * (9 + g), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gb.gen) {
+    while (__hip_atomic_load(glb(gb.bar + 16 * (9 + g)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gb.gen) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins == kSpinLimit) {
         gb.aborted = true;
-        __hip_atomic_store(gb.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(glb(gb.err), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
@@ -414,7 +421,7 @@ __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const Gem
       const int row = 4 * rg + i;
       xv[i] = (row < P.m && col < M.N) ? cld(P.x + (long long)row * P.ldx + col) : 0.f;
     }
-    const float gn = col < M.N ? io.gain[col] : 0.f;
+    const float gn = col < M.N ? *glb(io.gain + col) : 0.f;
     float sq[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -500,7 +507,7 @@ __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const Gem
       const int row = 4 * rg + i;
       const bool ok = row < P.m && col < M.N;
       const float v = rs[row] * acc[0][i];
-      if (ok) io.out[(long long)row * io.ldo + col] = v;
+      if (ok) *glb(io.out + (long long)row * io.ldo + col) = v;
       float mx = ok ? v : -INFINITY;
       int ix = ok ? col : 0x7fffffff;
 #pragma unroll
@@ -746,7 +753,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     const int e = C->pend[k];
     const int s = (e >> 20) & 0x7ff, sg = e & 0xfffff;
     if (e < 0) notify_block(P, io, sg);
-    else __hip_atomic_fetch_add(io.tickets + (long long)s * M.n_sg + sg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else __hip_atomic_fetch_add(glb(io.tickets + (long long)s * M.n_sg + sg), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const int nb = L.n_slots * M.n_sg;
   const int b0 = range_begin(nb, g, G), b1 = range_begin(nb, g + 1, G);
@@ -763,14 +770,14 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     if (threadIdx.x == 0) {
       unsigned* t = io.tickets + b;
       unsigned spins = 0;
-      while (__hip_atomic_load(t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)n) {
+      while (__hip_atomic_load(glb(t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)n) {
         __builtin_amdgcn_s_sleep(1);
         if (++spins == kSpinLimit) {
-          __hip_atomic_store(P.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(glb(P.err), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
       }
-      __hip_atomic_store(t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(glb(t), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();   // the partials are read with agent-scope loads
     const int unit = sg * kWaves + wave;
@@ -1370,9 +1377,9 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
       release_all_waves();
       __syncthreads();
       if (tid == 0) {
-        const unsigned old = __hip_atomic_fetch_add(P.attn_tickets + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned old = __hip_atomic_fetch_add(glb(P.attn_tickets + g), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const bool last = old == (unsigned)(P.n_groups - 1);
-        if (last) __hip_atomic_store(P.attn_tickets + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (last) __hip_atomic_store(glb(P.attn_tickets + g), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         C->misc[0] = last ? 1 : 0;   // the partials are then read with agent-scope loads
       }
       __syncthreads();
@@ -1423,7 +1430,7 @@ __device__ __forceinline__ void route_block(const PassP& P, const float* bias, u
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
-      z[i] = e < P.E ? cld(P.rlog + row * P.ldr + e) + bias[e] : -INFINITY;
+      z[i] = e < P.E ? cld(P.rlog + row * P.ldr + e) + *glb(bias + e) : -INFINITY;
       mx = fmaxf(mx, z[i]);
     }
 #pragma unroll
@@ -1517,7 +1524,7 @@ __device__ __forceinline__ void moe_combine_phase(const PassP& P, const float* n
       cst(P.x + (long long)row * P.ldx + col, v);
       if (trace) trace[(long long)row * P.d + col] = v;
     }
-    if (col < P.d) afrag_put(a_out, row, col, v * next_gain[col]);
+    if (col < P.d) afrag_put(a_out, row, col, v * *glb(next_gain + col));
     float sq = v * v;
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) sq += __shfl_xor(sq, o, 64);
