@@ -58,11 +58,25 @@ SP_HD Lin make_lin(const Mat& M, int n_slots, bool slot_major, const int* ulist 
   return L;
 }
 
+// floor(p / q) for 0 <= p < 2^52 and 0 < q < 2^31.  The device evaluates
+// it in double precision: p and q are exact, the quotient is correctly
+// rounded with an error of at most (p / q) 2^-53 < 1 / (2q), and a
+// non-integral p / q lies at least 1 / q from either neighbouring integer,
+// so the floor is the integer quotient.  (A 64-bit integer division is a
+// long serial sequence of scalar instructions on the GPU.)
+SP_HD int floor_div(long long p, long long q) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return (int)floor((double)p / (double)q);
+#else
+  return (int)(p / q);
+#endif
+}
+
 // First unit of workgroup g.
-SP_HD int range_begin(int total, int g, int G) { return (int)((long long)total * g / G); }
+SP_HD int range_begin(int total, int g, int G) { return floor_div((long long)total * g, G); }
 
 // Workgroup owning unit u (the largest g with range_begin(g) <= u).
-SP_HD int wg_of(int u, int T, int G) { return (int)((((long long)u + 1) * G - 1) / T); }
+SP_HD int wg_of(int u, int T, int G) { return floor_div(((long long)u + 1) * G - 1, T); }
 
 // Position in the flattened space (advanced a segment at a time without
 // divisions).

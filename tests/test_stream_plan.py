@@ -72,3 +72,26 @@ def test_plan_moe_small_expert_counts():
 def test_plan_rejects_bad_grid():
     rc, msg = _plan(synth.TINY, 0)
     assert rc == b.SPEC_EINVAL and "n_wg" in msg
+
+
+def test_floor_div_in_double_matches_integer_division():
+    """The device computes range_begin / wg_of quotients as floor(p / q) in
+    double precision; over the ranges the plan allows (p < 2^52, q < 2^31)
+    that equals the integer quotient, including just below and at exact
+    multiples."""
+    import random
+
+    rng = random.Random(7)
+    cases = []
+    for _ in range(20000):
+        q = rng.randrange(1, 1 << 31)
+        k = rng.randrange(0, (1 << 52) // q)
+        for p in (k * q - 1, k * q, k * q + 1, k * q + q - 1):
+            if 0 <= p < (1 << 52):
+                cases.append((p, q))
+    for G in (1, 3, 255, 256, 304, 1000, 4096):
+        for total in (1, 7, 1 << 20, (1 << 31) - 1):
+            for g in range(0, G + 1, max(1, G // 17)):
+                cases.append((total * g, G))
+    for p, q in cases:
+        assert int(float(p) / float(q) // 1) == p // q, (p, q)
