@@ -402,7 +402,11 @@ __device__ __forceinline__ void qkv_pre(const PassP& P, int unit, QkvPre& q) {
 template <int WF, int EPI, int TPU>
 __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const GemmIO& io, const float* rs, int slot,
                                          int unit, f32x4 (&acc)[TPU], const QkvPre* qp = nullptr) {
-  const int lane = threadIdx.x & 63;
+  // the lane index is made opaque here, so the compiler cannot hoist the
+  // per-row addresses below out of a stream loop (they would stay live, and
+  // spill, across the whole loop)
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
   const int cl = lane & 15, rg = lane >> 4;
   if constexpr (EPI == EPI_STORE) {
     const int col = unit * kTileN + cl;
