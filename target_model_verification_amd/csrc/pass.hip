@@ -45,6 +45,7 @@ typedef __attribute__((address_space(1))) const u4 gu4;
 typedef __attribute__((address_space(1))) const uint16_t gu16;
 typedef __attribute__((address_space(1))) void gvoid;
 typedef __attribute__((address_space(3))) void lvoid;
+constexpr int kCpolSc1 = 16;   // cache-policy bit of a direct-to-LDS load: agent-coherent (sc1)
 // A generic pointer known to address global memory, as a global-space
 // pointer: its accesses then compile to global (not flat) instructions,
 // which never hold up the LDS counter.
@@ -945,20 +946,32 @@ __device__ __forceinline__ void attn_merge_store(const PassP& P, uint4* a_o, int
   afrag_put(a_o, j, h * P.D + d, attn_merge_one(P, g, r, d));
 }
 
-// The whole merge of KV head g by one workgroup (its last attention item):
-// per-row group factors once in LDS, then each thread's outputs with their
-// partial loads in flight together.  Same arithmetic as attn_merge_one.
+// The whole merge of KV head g by one workgroup (its last attention item).
+// The head's accumulator partials (one contiguous block) go to LDS by
+// direct agent-scope (sc1) global-to-LDS loads while the row maxima and
+// sums are read with agent-scope loads, so the merge waits on memory once;
+// then the per-row group factors, then each output from LDS.  Same
+// arithmetic as attn_merge_one.  The host enables this path only when the
+// head's partials fit in the LDS working set (kInlineMergeElems floats).
 __device__ __forceinline__ void attn_merge_head(const PassP& P, uint4* a_o, int g, unsigned char* smem) {
   const int D = P.D, R = P.m * P.G, NG = P.n_groups;
-  const int tid = threadIdx.x;
-  float* fv = reinterpret_cast<float*>(smem);   // [NG][R]: pm, then the factors
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float* pa = reinterpret_cast<float*>(smem);   // [NG][R][D]: accumulator partials
+  float* fv = pa + (long long)NG * R * D;       // [NG][R]: pm, then the factors
   float* sv = fv + NG * R;                      // [NG][R]: ps
   float* Sr = sv + NG * R;                      // [R]
   const long long gb = (long long)g * NG * R;
+  const int nbytes = NG * R * D * 4;
+  const char* src = reinterpret_cast<const char*>(P.pacc + gb * D);
+  for (int off = wave * 1024; off < nbytes; off += kWaves * 1024) {
+    if (off + lane * 16 < nbytes)
+      __builtin_amdgcn_global_load_lds((gvoid*)(src + off + lane * 16), (lvoid*)(smem + off), 16, 0, kCpolSc1);
+  }
   for (int i = tid; i < NG * R; i += kThreads) {
     fv[i] = cld(P.pm + gb + i);
     sv[i] = cld(P.ps + gb + i);
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int r = tid; r < R; r += kThreads) {
     float M = -INFINITY;
@@ -973,41 +986,12 @@ __device__ __forceinline__ void attn_merge_head(const PassP& P, uint4* a_o, int 
     Sr[r] = S;
   }
   __syncthreads();
-  constexpr int KB = 8;   // outputs per thread per round
-  constexpr int GB = 4;   // groups per round
-  for (int e0 = tid; e0 < R * D; e0 += kThreads * KB) {
-    float A[KB];
-#pragma unroll
-    for (int k = 0; k < KB; ++k) A[k] = 0.f;
-    for (int c0 = 0; c0 < NG; c0 += GB) {
-      float v[KB][GB];
-#pragma unroll
-      for (int k = 0; k < KB; ++k) {
-        const int e = e0 + k * kThreads;
-#pragma unroll
-        for (int q = 0; q < GB; ++q)
-          v[k][q] = (e < R * D && c0 + q < NG) ? cld(P.pacc + (gb + (long long)(c0 + q) * R) * D + e) : 0.f;
-      }
-#pragma unroll
-      for (int k = 0; k < KB; ++k) {
-        const int e = e0 + k * kThreads;
-        if (e < R * D) {
-          const int r = e / D;
-#pragma unroll
-          for (int q = 0; q < GB; ++q)
-            if (c0 + q < NG) A[k] += fv[(c0 + q) * R + r] * v[k][q];
-        }
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < KB; ++k) {
-      const int e = e0 + k * kThreads;
-      if (e < R * D) {
-        const int r = e / D, d = e % D;
-        const int j = r / P.G, h = g * P.G + r % P.G;
-        afrag_put(a_o, j, h * D + d, A[k] / Sr[r]);
-      }
-    }
+  for (int e = tid; e < R * D; e += kThreads) {
+    const int r = e / D, d = e - r * D;
+    float A = 0.f;
+    for (int c = 0; c < NG; ++c) A += fv[c * R + r] * pa[(c * R + r) * D + d];
+    const int j = r / P.G, h = g * P.G + r % P.G;
+    afrag_put(a_o, j, h * D + d, A / Sr[r]);
   }
 }
 
