@@ -647,18 +647,19 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
   Cur cc = cur_at(L, u0);
   f32x4 acc[TPU];
 
-  // one batch of n chunks starting at window chunk c0
+  // one batch of n chunks starting at window chunk c0.  Ring slots past n
+  // hold zeros (next_batch) and read a valid, finite A chunk, so they add
+  // exact zeros.  bf16 / fp32: the A fragments of the next group of GR
+  // chunks are read from LDS while the current group's MFMAs run (the
+  // scheduling barriers keep exactly one group in flight: bounded registers,
+  // hidden LDS latency).
   auto compute = [&](int c0, int n, bool live) {
     if (!live) return;
     const uint4* aw = reinterpret_cast<const uint4*>(smem) + (long long)c0 * F::ACH * 128;
-    const u4 z4 = u4{0u, 0u, 0u, 0u};
-    // branch-free over the batch: slots past n use zero weights and a valid
-    // (finite) A chunk, so they add exact zeros
+    if constexpr (WF == W_INT4) {
 #pragma unroll
-    for (int i = 0; i < F::U; ++i) {
-      const bool ok = i < n;
-      const int ai = ok ? i : 0;
-      if constexpr (WF == W_INT4) {
+      for (int i = 0; i < F::U; ++i) {
+        const int ai = i < n ? i : 0;
         f32x4 gacc[TPU];
 #pragma unroll
         for (int t = 0; t < TPU; ++t) gacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -668,35 +669,63 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
           const u4 al = __builtin_bit_cast(u4, aw[(ai * 4 + q4) * 128 + 64 + lane]);
 #pragma unroll
           for (int t = 0; t < TPU; ++t) {
-            const u4 wv = ok ? nib8_to_bf16(ring.r[i * TPU + t][q4]) : z4;
+            const u4 wv = nib8_to_bf16(ring.r[i * TPU + t][q4]);
             gacc[t] = mfma(ah, wv, gacc[t]);
             gacc[t] = mfma(al, wv, gacc[t]);
           }
         }
 #pragma unroll
-        for (int t = 0; t < TPU; ++t) acc[t] += (ok ? ring.s[i * TPU + t] : 0.f) * gacc[t];
-      } else {
-        const u4 ah = __builtin_bit_cast(u4, aw[ai * 128 + lane]);
-        const u4 al = __builtin_bit_cast(u4, aw[ai * 128 + 64 + lane]);
+        for (int t = 0; t < TPU; ++t) acc[t] += ring.s[i * TPU + t] * gacc[t];
+        // keep each chunk's A reads next to its MFMAs (bounded register use)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      }
+    } else {
+      constexpr int GR = 4;   // chunks per group
+      static_assert(F::U % GR == 0, "batch not a whole number of groups");
+      u4 ch[GR], cl[GR], nh[GR], nl[GR];
+      auto read_group = [&](int g0, u4 (&h)[GR], u4 (&l)[GR]) {
 #pragma unroll
-        for (int t = 0; t < TPU; ++t) {
-          if constexpr (WF == W_F32) {
-            const u4 wh = ok ? ring.r[(i * TPU + t) * 2 + 0] : z4, wl = ok ? ring.r[(i * TPU + t) * 2 + 1] : z4;
-            acc[t] = mfma(ah, wh, acc[t]);
-            acc[t] = mfma(al, wh, acc[t]);
-            acc[t] = mfma(ah, wl, acc[t]);
-            acc[t] = mfma(al, wl, acc[t]);
-          } else {
-            const u4 wv = ok ? ring.r[i * TPU + t] : z4;
-            acc[t] = mfma(ah, wv, acc[t]);
-            acc[t] = mfma(al, wv, acc[t]);
+        for (int j = 0; j < GR; ++j) {
+          const int ai = g0 + j < n ? g0 + j : 0;
+          h[j] = __builtin_bit_cast(u4, aw[ai * 128 + lane]);
+          l[j] = __builtin_bit_cast(u4, aw[ai * 128 + 64 + lane]);
+        }
+      };
+      read_group(0, ch, cl);
+#pragma unroll
+      for (int g0 = 0; g0 < F::U; g0 += GR) {
+        if (g0 + GR < F::U) read_group(g0 + GR, nh, nl);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < GR; ++j) {
+          const int i = g0 + j;
+#pragma unroll
+          for (int t = 0; t < TPU; ++t) {
+            if constexpr (WF == W_F32) {
+              const u4 wh = ring.r[(i * TPU + t) * 2 + 0], wl = ring.r[(i * TPU + t) * 2 + 1];
+              acc[t] = mfma(ch[j], wh, acc[t]);
+              acc[t] = mfma(cl[j], wh, acc[t]);
+              acc[t] = mfma(ch[j], wl, acc[t]);
+              acc[t] = mfma(cl[j], wl, acc[t]);
+            } else {
+              const u4 wv = ring.r[i * TPU + t];
+              acc[t] = mfma(ch[j], wv, acc[t]);
+              acc[t] = mfma(cl[j], wv, acc[t]);
+            }
           }
         }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < GR; ++j) {
+          ch[j] = nh[j];
+          cl[j] = nl[j];
+        }
       }
-      // keep each chunk's A reads next to its MFMAs (bounded register use)
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
     }
   };
+
 
   for (;;) {
     // ---- one segment: (slot, win, sg), chunks [cc.c, cc.c + nch)
