@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 GREEDY_WORKLOADS = ("llama7b", "llama7b_int4", "moe", "tiny")
+STOCHASTIC_WORKLOADS = ("qwen7b",)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 PASS_SOURCE = os.path.join(ROOT, "target_model_verification_amd", "csrc", "pass.hip")
 
@@ -57,7 +58,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="llama7b", choices=GREEDY_WORKLOADS)
+    ap.add_argument("--workload", default="llama7b", choices=GREEDY_WORKLOADS + STOCHASTIC_WORKLOADS)
     ap.add_argument("--k", type=int, default=None)
     ap.add_argument("--k-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -128,6 +129,10 @@ class Session:
             res = self.h.step(prompt[i:i + 16], B.SPEC_ACCEPT_NONE)
         self.L0 = self.h.kv_len
         self.pending0 = int(res.next_token)
+        if wl.accept == "stochastic":   # drafts are drawn per round from the target's own logits
+            self.ref = None
+            log(f"[bench] prompt {len(prompt)} prefilled in {time.time() - t:.1f} s")
+            return
         # the target's greedy continuation after the prompt (k = 0 steps)
         ref = [self.pending0]
         for _ in range(self.n_ref):
@@ -172,7 +177,82 @@ class Session:
         return out, s, pending, dt, prof
 
 
+def draft_round(sess: Session, rnd: int, pending: int, k: int, zbuf):
+    """Stochastic drafts of one round, as the stochastic workload defines
+    them: q_i = softmax(z_i + eps_i) with z_i the target's fp32 logits at
+    draft position i given pending, d_1..d_{i-1} (single-token passes on the
+    target's own cache, rolled back afterwards), d_i drawn from q_i by
+    inverse CDF with a seeded uniform.  Input preparation only: none of it
+    is timed."""
+    import numpy as np
+    import torch
+    from target_model_verification_amd import synth
+    B, h, wl = sess.B, sess.h, sess.wl
+    L = h.kv_len
+    toks, qs = [pending], []
+    for i in range(1, k + 1):
+        h.step([toks[-1]], B.SPEC_ACCEPT_NONE, 0, 0, zbuf.data_ptr())
+        z = zbuf[0].double() + torch.from_numpy(synth.draft_noise(wl, rnd, i)).to(zbuf.device).double()
+        q = torch.softmax(z, 0)
+        c = torch.cumsum(q, 0)
+        u = synth.draft_sample_uniform(wl, rnd, i)
+        d = int(torch.searchsorted(c, torch.tensor([u * float(c[-1])], dtype=torch.float64, device=c.device),
+                                   right=True)[0])
+        toks.append(min(d, wl.spec.vocab - 1))
+        qs.append(q.float())
+    h.rollback(L)
+    q_dev = torch.stack(qs).contiguous() if qs else torch.zeros((1, wl.spec.vocab), device=zbuf.device)
+    u_dev = torch.from_numpy(synth.round_uniforms(wl, rnd, k)).to(zbuf.device)
+    return np.asarray(toks, dtype=np.int32), q_dev, u_dev
+
+
+def measure_k_stochastic(sess: Session, k: int, warmup: int, steps: int):
+    """Stochastic acceptance (u < p/q, residual resample): each step is
+    timed alone (drafting between steps runs target passes of its own),
+    then the timed steps are replayed from the same state with HIP events
+    around every kernel launch."""
+    import torch
+    B, h = sess.B, sess.h
+    zbuf = torch.empty((1, sess.wl.spec.vocab), dtype=torch.float32, device="cuda")
+    h.rollback(sess.L0)
+    pending, rec, inputs, dt = sess.pending0, [], [], 0.0
+    L_start = None
+    for r in range(warmup + steps):
+        toks, q_dev, u_dev = draft_round(sess, r, pending, k, zbuf)
+        torch.cuda.synchronize()
+        L = h.kv_len
+        if r == warmup:
+            L_start = L
+        t0 = time.perf_counter()
+        res = h.step(toks, B.SPEC_ACCEPT_STOCHASTIC, q_dev.data_ptr(), u_dev.data_ptr())
+        el = time.perf_counter() - t0
+        if r >= warmup:
+            dt += el
+            rec.append((L, res.n_accepted))
+            inputs.append((toks, q_dev, u_dev))
+        pending = res.next_token
+    h.rollback(L_start)
+    h.profile(True)
+    rec2 = []
+    for toks, q_dev, u_dev in inputs:
+        rec2.append(h.step(toks, B.SPEC_ACCEPT_STOCHASTIC, q_dev.data_ptr(), u_dev.data_ptr()).n_accepted)
+    torch.cuda.synchronize()
+    prof = h.profile_read()
+    sess.detail = h.profile_detail()
+    h.profile(False)
+    if rec2 != [n for _, n in rec]:
+        raise RuntimeError("replayed steps accepted different counts: the pass is not deterministic")
+    accepted = sum(n + 1 for _, n in rec)
+    bytes_total = sum(h.pass_bytes(L, k, B.SPEC_ACCEPT_STOCHASTIC) for L, _ in rec)
+    return dict(k=k, steps=steps, seconds=dt, ms_per_step=dt / steps * 1e3, accepted=accepted,
+                acc_tok_s=accepted / dt, verified_tok_s=steps * (k + 1) / dt,
+                mean_accept=accepted / steps, pass_gb=bytes_total / steps / 1e9,
+                wall_gbs=bytes_total / dt / 1e9, L_start=L_start, prof=prof, profiled_seconds=None)
+
+
 def measure_k(sess: Session, k: int, warmup: int, steps: int):
+    if sess.wl.accept == "stochastic":
+        return measure_k_stochastic(sess, k, warmup, steps)
     corr = sess.rounds(k, warmup + steps)
     sess.h.rollback(sess.L0)
     _, s, pending, _, _ = sess.run(k, corr[:warmup], 0, sess.pending0)
@@ -322,17 +402,20 @@ def main():
                 "pass_wall_gbs": round(r["wall_gbs"], 1),
                 "pass_wall_frac": round(r["wall_gbs"] / HBM_PEAK_GBS, 4)}
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and wl.accept == "greedy":
         cpu = cpu_baseline(wl, W, k, r["L_start"], args.cpu_seconds, r["mean_accept"])
     line = {
         "metric": "accepted tok/s + verify-pass HBM GB/s vs peak, 7B bf16 k=8, single sequence",
         "value": round(r["acc_tok_s"], 2), "unit": "accepted tok/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": wl.spec.weight_dtype,
-        "data": "synthetic: random-init weights N(0,0.02), uniform random prompt ids, drafts = target's "
-                "greedy continuation with per-token corruption",
-        "config": {"workload": f"{wl.spec.name} verify pass, k={k}, context {wl.context}, "
-                               f"draft corruption {wl.corruption}, greedy acceptance, single sequence",
+        "data": ("synthetic: random-init weights N(0,0.02), uniform random prompt ids, drafts = target's "
+                 "greedy continuation with per-token corruption" if wl.accept == "greedy" else
+                 "synthetic: random-init weights N(0,0.02), uniform random prompt ids, drafts drawn from "
+                 "q = softmax(target logits + N(0,1) noise)"),
+        "config": {"workload": (f"{wl.spec.name} verify pass, k={k}, context {wl.context}, "
+                                + (f"draft corruption {wl.corruption}, greedy acceptance" if wl.accept == "greedy"
+                                   else "stochastic acceptance at temperature 1") + ", single sequence"),
                    "k": k, "context": wl.context, "verified_tok_s": round(r["verified_tok_s"], 2),
                    "mean_tokens_per_step": round(r["mean_accept"], 4),
                    "pass_bytes_gb": round(r["pass_gb"], 4)},

@@ -599,7 +599,7 @@ __device__ __forceinline__ void notify_block(const PassP& P, const GemmIO& io, i
 // waits (workgroup-wide) until the input window win of a consuming phase is ready
 __device__ __forceinline__ void wait_window(const PassP& P, const GemmIO& io, int win) {
   if (io.dep == kDepOWin) {
-    if (threadIdx.x == 0) ready_wait(io.ready + 256 + win, P.epoch * owin_expect(P, win), P.err);
+    if (threadIdx.x == 0) ready_wait(io.ready + kRdyOWin + win, P.epoch * owin_expect(P, win), P.err);
     __syncthreads();
   }
 }
@@ -1407,7 +1407,7 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
         __syncthreads();
         if (tid == 0)
           for (int h = g * P.G; h < (g + 1) * P.G; ++h)
-            for (int w = h * D / P.o_wcols; w <= ((h + 1) * D - 1) / P.o_wcols; ++w) ready_add(ready + 256 + w);
+            for (int w = h * D / P.o_wcols; w <= ((h + 1) * D - 1) / P.o_wcols; ++w) ready_add(ready + kRdyOWin + w);
       }
     }
     __syncthreads();
@@ -1416,13 +1416,21 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
 
 // The merge as a phase of its own (heads with many groups or rows): one
 // output element per thread over the whole grid.
-__device__ __forceinline__ void attn_merge_phase(const PassP& P, uint4* a_o) {
+// The O projection then follows a grid barrier, so nothing in this pass
+// waits on the O-window ready counters; they still advance by one pass's
+// count (a later pass that merges inline waits for the pass number times
+// that count).
+__device__ __forceinline__ void attn_merge_phase(const PassP& P, uint4* a_o, unsigned long long* ready) {
   const int D = P.D, R = P.m * P.G;
   const long long total = (long long)P.Hkv * R * D;
   for (long long e = (long long)blockIdx.x * kThreads + threadIdx.x; e < total; e += (long long)gridDim.x * kThreads) {
     const int d = (int)(e % D);
     const long long gr = e / D;
     attn_merge_store(P, a_o, (int)(gr / R), (int)(gr % R), d);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    const int n_win = (P.Hq * D + P.o_wcols - 1) / P.o_wcols;
+    for (int w = 0; w < n_win; ++w) ready_add(ready + kRdyOWin + w, owin_expect(P, w));
   }
 }
 
@@ -1659,7 +1667,7 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
           break;
         }
         sync([] {});
-        attn_merge_phase(P, d->a_out);
+        attn_merge_phase(P, d->a_out, io.ready);
         break;
       case PH_COMBINE:
         sync([] {});

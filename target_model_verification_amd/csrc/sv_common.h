@@ -95,6 +95,7 @@ struct Phase {
 // many producers (a normalised row, a gate/up window) keep grid barriers.
 enum DepKind : int { kDepNone = 0, kDepHeads = 1, kDepOWin = 2 };
 constexpr int kReadyStride = 512;   // counters per layer: [0,256) KV heads, [256,512) O windows
+constexpr int kRdyOWin = 256;
 
 // Everything one pass needs; passed by value to the pass kernel.
 struct PassP {

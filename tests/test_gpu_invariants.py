@@ -161,3 +161,35 @@ def test_capacity():
         assert h.step([pw.pending0]).kv_len == P + 1
     finally:
         h.close()
+
+
+def test_merge_modes_share_counters():
+    """Attention of a block with many rows x position groups is merged in a
+    phase of its own; single-token steps merge inline (the last group of a
+    head merges it and signals the O projection).  Both modes run on one
+    handle: a handle that appends blocks of 16 (the later ones merged in
+    their own phase) and one that appends the same tokens one at a time
+    (always inline) must then give bitwise equal logits for the same next
+    steps (dense model: the pass is independent of the block size)."""
+    pw = prepare(synth.ALL_WORKLOADS["small_gqa"])
+    L0 = pw.kv0.length
+    toks = [int(t) for t in synth.prompt_ids(pw.wl, 400)[200:296]]
+    hb = make_verifier(pw, max_k=15, gemm_k_split=256, max_ctx=L0 + 128)
+    ht = make_verifier(pw, max_k=15, gemm_k_split=256, max_ctx=L0 + 128)
+    try:
+        log(f"[invariants] merge modes: {len(toks)} tokens from L={L0} in blocks of 16 and one by one")
+        for i in range(0, len(toks), 16):
+            hb.step(toks[i:i + 16], B.SPEC_ACCEPT_NONE)
+        for t in toks:
+            ht.step([t], B.SPEC_ACCEPT_NONE)
+        assert hb.kv_len == ht.kv_len == L0 + len(toks)
+        tok_b = tok_t = toks[-1]
+        for _ in range(3):
+            rb, lb = _logits(hb, [tok_b, 5, 6])
+            rt, lt = _logits(ht, [tok_t, 5, 6])
+            assert np.array_equal(lb, lt)
+            assert (rb.n_accepted, rb.next_token, rb.kv_len) == (rt.n_accepted, rt.next_token, rt.kv_len)
+            tok_b, tok_t = rb.next_token, rt.next_token
+    finally:
+        hb.close()
+        ht.close()
