@@ -70,7 +70,8 @@ typedef enum {
  * a MoE FFN: softmax router with bias over n_experts, each token keeps its
  * top_k experts by probability (weights = those probabilities, not
  * renormalized), plus n_shared always-on experts of width d_ff_expert
- * (S2-MoE section 2.1 and Table 1 give the family). */
+ * (S2-MoE section 2.1 and Table 1 give the family).  vocab is at most
+ * 262144. */
 typedef struct {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, d_ff, vocab;
   int32_t n_experts, top_k, n_shared, d_ff_expert;

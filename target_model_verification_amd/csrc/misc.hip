@@ -10,21 +10,36 @@ namespace sv {
 // at the first rejection draw from max(0, p - q) (p if that is all zero),
 // else from p_k; draw = smallest x with C(x) > u_{k+1} * C(V-1), C the
 // running sum in ascending id order.  result = {n_acc, next, kv_len}.
+constexpr int kAccWaves = 16;            // 1024 threads
+constexpr int kAccTiles = 4 * 1024;      // 64-id tiles: vocabularies up to 262144 ids
 __global__ __launch_bounds__(1024) void k_accept(AcceptParams p) {
   __shared__ int amax[16];
   __shared__ float rowM[16], rowS[16];
-  __shared__ float segsum[1024];
+  __shared__ float tsum[kAccTiles], tpre[kAccTiles], wsum[kAccWaves];
   __shared__ int s_row, s_resid, s_nacc, s_cand, s_last;
-  __shared__ float s_thr;
+  __shared__ float s_thr, s_total;
+  __shared__ float sP[16], sQ[16], sU[16];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int m = p.k + 1;
+  constexpr int B = 16;   // loads in flight per lane
   if (w < m) {
     float M = -INFINITY;
     int I = 0x7fffffff;
-    for (int g = lane; g < p.n_stat; g += 64) {
-      const float v = p.st_max[w * p.n_stat + g];
-      const int ix = p.st_idx[w * p.n_stat + g];
-      if (v > M || (v == M && ix < I)) { M = v; I = ix; }
+    const float* smax = p.st_max + (long long)w * p.n_stat;
+    const float* ssum = p.st_sum + (long long)w * p.n_stat;
+    const int* sidx = p.st_idx + (long long)w * p.n_stat;
+    for (int g0 = lane; g0 < p.n_stat; g0 += 64 * B) {
+      float v[B];
+      int ix[B];
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        const int g = g0 + 64 * q;
+        v[q] = g < p.n_stat ? smax[g] : -INFINITY;
+        ix[q] = g < p.n_stat ? sidx[g] : 0x7fffffff;
+      }
+#pragma unroll
+      for (int q = 0; q < B; ++q)
+        if (v[q] > M || (v[q] == M && ix[q] < I)) { M = v[q]; I = ix[q]; }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
@@ -33,9 +48,17 @@ __global__ __launch_bounds__(1024) void k_accept(AcceptParams p) {
       if (ov > M || (ov == M && oi < I)) { M = ov; I = oi; }
     }
     float S = 0.f;
-    for (int g = lane; g < p.n_stat; g += 64) {
-      const float v = p.st_max[w * p.n_stat + g];
-      if (v != -INFINITY) S += p.st_sum[w * p.n_stat + g] * expf(v - M);
+    for (int g0 = lane; g0 < p.n_stat; g0 += 64 * B) {
+      float v[B], e[B];
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        const int g = g0 + 64 * q;
+        v[q] = g < p.n_stat ? smax[g] : -INFINITY;
+        e[q] = g < p.n_stat ? ssum[g] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < B; ++q)
+        if (v[q] != -INFINITY) S += e[q] * expf(v[q] - M);
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) S += __shfl_xor(S, o, 64);
@@ -56,14 +79,19 @@ __global__ __launch_bounds__(1024) void k_accept(AcceptParams p) {
     }
     return;
   }
-  // stochastic: sequential tests
+  // stochastic: the k tests' operands side by side, then the tests in order
+  if (tid >= 1 && tid <= p.k) {
+    const int i = tid, d = p.tokens[i];
+    sP[i] = expf(p.logits[(long long)(i - 1) * p.ldl + d] - rowM[i - 1]) / rowS[i - 1];
+    sQ[i] = p.q[(long long)(i - 1) * p.V + d];
+    sU[i] = p.u[i - 1];
+  }
+  __syncthreads();
   if (tid == 0) {
     int n = p.k, resid = 0;
     for (int i = 1; i <= p.k; ++i) {
-      const int d = p.tokens[i];
-      const float P = expf(p.logits[(long long)(i - 1) * p.ldl + d] - rowM[i - 1]) / rowS[i - 1];
-      const float Q = p.q[(long long)(i - 1) * p.V + d];
-      if (p.u[i - 1] * Q < P) continue;
+      const float P = sP[i], Q = sQ[i];
+      if (sU[i] * Q < P) continue;
       n = i - 1;
       resid = 1;
       break;
@@ -80,24 +108,75 @@ __global__ __launch_bounds__(1024) void k_accept(AcceptParams p) {
   const float* lrow = p.logits + (long long)row * p.ldl;
   // q has k rows; it is read only for a residual draw (row < k)
   const float* qrow = s_resid ? p.q + (long long)row * p.V : lrow;
-  const int seg = (p.V + 1023) / 1024;
-  const int x0 = tid * seg, x1 = min(p.V, x0 + seg);
+  // weight of id x from its logit l and draft probability qx
+  auto wfun = [&](float l, float qx, int resid) -> float {
+    const float px = expf(l - M) / S;
+    return resid ? fmaxf(0.f, px - qx) : px;
+  };
+  auto weight = [&](int x, int resid) -> float { return wfun(lrow[x], resid ? qrow[x] : 0.f, resid); };
+  // Inverse CDF over tiles of 64 consecutive ids: tile sums (one wave per
+  // tile, loads coalesced), an exclusive scan of the tile sums in id order,
+  // the first tile whose running sum passes the threshold, then a scan
+  // inside that tile.
+  const int nt = (p.V + 63) / 64;                 // <= kAccTiles (checked at launch)
+  const int per = (nt + kAccWaves - 1) / kAccWaves;
   for (int pass = 0; pass < 2; ++pass) {
     const int resid = s_resid;
-    float loc = 0.f;
-    for (int x = x0; x < x1; ++x) {
-      const float px = expf(lrow[x] - M) / S;
-      loc += resid ? fmaxf(0.f, px - qrow[x]) : px;
+    const int tend = min(nt, (w + 1) * per);
+    for (int t0 = w * per; t0 < tend; t0 += B) {
+      float lv[B], qv[B];
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        const int x = (t0 + q) * 64 + lane;
+        const bool ok = t0 + q < tend && x < p.V;
+        lv[q] = ok ? lrow[x] : 0.f;
+        qv[q] = ok && resid ? qrow[x] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        const int x = (t0 + q) * 64 + lane;
+        float v = (t0 + q < tend && x < p.V) ? wfun(lv[q], qv[q], resid) : 0.f;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+        if (lane == 0 && t0 + q < tend) tsum[t0 + q] = v;
+      }
     }
-    segsum[tid] = loc;
+    __syncthreads();
+    // thread j: tiles 4j .. 4j+3 in order, then a block scan of the totals
+    float loc[4], tot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * tid + e;
+      loc[e] = t < nt ? tsum[t] : 0.f;
+      tot += loc[e];
+    }
+    float inc = tot;   // inclusive scan within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    if (lane == 63) wsum[w] = inc;
     __syncthreads();
     if (tid == 0) {
       float run = 0.f;
-      for (int t = 0; t < 1024; ++t) {
-        const float v = segsum[t];
-        segsum[t] = run;
+      for (int i = 0; i < kAccWaves; ++i) {
+        const float v = wsum[i];
+        wsum[i] = run;
         run += v;
       }
+      s_total = run;
+    }
+    __syncthreads();
+    float pre = wsum[w] + inc - tot;   // exclusive prefix of tile 4*tid
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * tid + e;
+      if (t < nt) tpre[t] = pre;
+      pre += loc[e];
+    }
+    if (tid == 0) {
+      const float run = s_total;
       if (resid && !(run > 0.f)) {
         s_resid = 0;         // p == q everywhere: draw from p
         s_thr = -1.f;
@@ -111,26 +190,43 @@ __global__ __launch_bounds__(1024) void k_accept(AcceptParams p) {
   {
     const int resid = s_resid;
     const float thr = s_thr;
-    float c = segsum[tid];
-    for (int x = x0; x < x1; ++x) {
-      const float px = expf(lrow[x] - M) / S;
-      const float wx = resid ? fmaxf(0.f, px - qrow[x]) : px;
-      c += wx;
-      if (wx > 0.f) atomicMax(&s_last, x);
-      if (c > thr && wx > 0.f) { atomicMin(&s_cand, x); break; }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * tid + e;
+      if (t < nt && tsum[t] > 0.f) {
+        atomicMax(&s_last, t);
+        if (tpre[t] + tsum[t] > thr) atomicMin(&s_cand, t);
+      }
     }
-  }
-  __syncthreads();
-  if (tid == 0) {
-    const int x = (s_cand != 0x7fffffff) ? s_cand : s_last;
-    p.result[0] = s_nacc;
-    p.result[1] = x;
-    p.result[2] = p.L + 1 + s_nacc;
+    __syncthreads();
+    if (w == 0) {
+      // the chosen tile (or, when rounding left the threshold unpassed, the
+      // last tile holding any weight): first id whose running sum passes
+      // the threshold, else the tile's last id with weight
+      const int t = s_cand != 0x7fffffff ? s_cand : s_last;
+      const int x = t * 64 + lane;
+      const float v = (t >= 0 && x < p.V) ? weight(x, resid) : 0.f;
+      float c = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float y = __shfl_up(c, o, 64);
+        if (lane >= o) c += y;
+      }
+      c += t >= 0 ? tpre[t] : 0.f;
+      const unsigned long long hit = __ballot(v > 0.f && c > thr);
+      const unsigned long long pos = __ballot(v > 0.f);
+      if (lane == 0) {
+        const int xs = hit ? t * 64 + __builtin_ctzll(hit) : (pos ? t * 64 + 63 - __builtin_clzll(pos) : 0);
+        p.result[0] = s_nacc;
+        p.result[1] = xs;
+        p.result[2] = p.L + 1 + s_nacc;
+      }
+    }
   }
 }
 
 hipError_t launch_accept(const AcceptParams& p, hipStream_t s) {
-  if (p.k + 1 > 16) return hipErrorInvalidValue;
+  if (p.k + 1 > 16 || (p.V + 63) / 64 > kAccTiles) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_accept, dim3(1), dim3(1024), 0, s, p);
   return hipGetLastError();
 }

@@ -1073,20 +1073,38 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   Ctl* C = ctl(smem, (size_t)P.lds_bytes);
   const int R = P.m * P.G;
-  const int RT = (R + 15) >> 4;
+  const int NRT = (R + 15) >> 4;   // row tiles per KV head: one per work item
+  const int RT = MAXRT;            // row tiles of this item
   const int T = P.L + P.m;
   constexpr int PSW = (ONE ? kGroupPos : kPage) + 4;  // floats per score row
   u4* Qf = reinterpret_cast<u4*>(smem);                              // [RT][KDC][2][64] (two-pass path)
   float* Ps = reinterpret_cast<float*>(smem + (size_t)RT * KDC * 2 * 1024);   // [RT*16][PSW]
   float* mrun = Ps + RT * 16 * PSW;
   float* lrun = mrun + RT * 16;
-  const int n_items = P.Hkv * P.n_groups;
+  const int n_items = P.Hkv * P.n_groups * NRT;
   const int DTW = D / 16 / kWaves;           // value tiles (16 d) per wave: 1 or 2
   const int key = 16 * wave + (lane & 15);   // this lane's key within a sub-chunk (scores)
   const int kq = 8 * (lane >> 4);            // first of this lane's 8 k in a 32-k chunk
   const int srow = tid >> 4, sq = (tid & 15) * 4;   // softmax: row, first of 4 positions
+  // Items of one (KV head, group) read the same keys and values: they are
+  // numbered 8 apart, so they run on one XCD (workgroups are dealt to the
+  // eight XCDs in turn) and share its L2; the last, partial set of eight
+  // (head, group) pairs is numbered densely.
+  const int n_pairs = P.Hkv * P.n_groups;
+  const int n_full = (n_pairs / 8) * 8 * NRT;
   for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int g = item / P.n_groups, grp = item % P.n_groups;
+    int pair, rt0;
+    if (item < n_full) {
+      const int wi = item % (8 * NRT);
+      rt0 = wi / 8;
+      pair = item / (8 * NRT) * 8 + wi % 8;
+    } else {
+      const int rem = n_pairs % 8, wi = item - n_full;
+      rt0 = wi / rem;
+      pair = n_pairs / 8 * 8 + wi % rem;
+    }
+    const int g = pair / P.n_groups, grp = pair % P.n_groups;
+    const int rb = rt0 * 16;   // first block row of this item
     const int gt0 = grp * kGroupPos;
     const int nsc = min(kGroupPages, (T - gt0 + kPage - 1) / kPage);   // sub-chunks holding positions
     // waits until this KV head's query fragments and new cache rows are written
@@ -1096,7 +1114,7 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
         __syncthreads();
       }
     };
-    const gu4* qsrc = (const gu4*)(qf + (long long)g * P.qf_rt * KDC * 2 * 64);
+    const gu4* qsrc = (const gu4*)(qf + ((long long)g * P.qf_rt + rt0) * KDC * 2 * 64);
     // ---- query fragments: registers (one row tile) or LDS
     u4 qh[4], ql[4];
     if constexpr (!ONE) wait_head();
@@ -1181,7 +1199,7 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
       const int tk = t0 + key;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = rt * 16 + 4 * (lane >> 4) + i;
+        const int r = rb + rt * 16 + 4 * (lane >> 4) + i;
         const bool vis = r < R && key < nkeys && tk <= P.L + r / P.G;
         s4[i] = vis ? s4[i] : -INFINITY;
       }
@@ -1379,23 +1397,25 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
         const int d = (wave * DTW + q) * 16 + (lane & 15);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = rt * 16 + 4 * (lane >> 4) + i;
+          const int r = rb + rt * 16 + 4 * (lane >> 4) + i;
           if (r < R) cst(P.pacc + (ib + r) * D + d, acc[rt][q][i]);
         }
       }
     }
     __syncthreads();   // lrun complete
-    for (int r = tid; r < R; r += kThreads) {
-      cst(P.pm + ib + r, mrun[r]);
-      cst(P.ps + ib + r, lrun[r]);
+    for (int lr = tid; lr < RT * 16; lr += kThreads) {
+      if (rb + lr < R) {
+        cst(P.pm + ib + rb + lr, mrun[lr]);
+        cst(P.ps + ib + rb + lr, lrun[lr]);
+      }
     }
     if (P.attn_inline) {
-      // the last group of head g to finish merges the head's groups
+      // the last item (group, row tile) of head g to finish merges the head
       release_all_waves();
       __syncthreads();
       if (tid == 0) {
         const unsigned old = __hip_atomic_fetch_add(glb(P.attn_tickets + g), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = old == (unsigned)(P.n_groups - 1);
+        const bool last = old == (unsigned)(P.n_groups * NRT - 1);
         if (last) __hip_atomic_store(glb(P.attn_tickets + g), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         C->misc[0] = last ? 1 : 0;   // the partials are then read with agent-scope loads
       }
@@ -1651,10 +1671,7 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
         sync([] {});
         wstamp(wst, 1);
         wstamp(wst, 2);
-        if (P.m * P.G <= 16)
-          attention_phase<WF == W_F32, 1>(P, d->kv, d->a, d->a_out, io.ready, io.dep, smem, wst);
-        else
-          attention_phase<WF == W_F32, kAttnRT>(P, d->kv, d->a, d->a_out, io.ready, io.dep, smem, wst);
+        attention_phase<WF == W_F32, 1>(P, d->kv, d->a, d->a_out, io.ready, io.dep, smem, wst);
         break;
       case PH_ATTN_MERGE:
         if (P.attn_inline) {

@@ -172,6 +172,7 @@ bool check_cfg(const spec_config* c, std::string& msg) {
   if (!c) return bad("null config");
   if (c->n_layers < 1 || c->d_model < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->vocab < 2)
     return bad("n_layers, d_model, heads must be >= 1 and vocab >= 2");
+  if (c->vocab > 262144) return bad("vocab must be <= 262144 (on-device acceptance works in 4096 tiles of 64 ids)");
   if (c->n_q_heads % c->n_kv_heads != 0) return bad("n_q_heads must be a multiple of n_kv_heads");
   if (c->n_kv_heads > 256) return bad("n_kv_heads must be at most 256");
   if (c->head_dim != 64 && c->head_dim != 128) return bad("head_dim must be 64 or 128");
