@@ -69,15 +69,15 @@ __device__ __forceinline__ f32x4 mfma(const u4& a, const u4& b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// 8 signed nibbles of one dword -> 8 bf16 (exact: |q| <= 8)
+// 8 offset nibbles of one dword (u = q + 8, pairs (2j, 2j+1) at bits 4j and
+// 16 + 4j) -> 8 bf16 of value 128 + u = q + 136 (exact: bf16 holds every
+// integer below 256).  The constant 136 is taken out after the products:
+// sum_k a_k q_k = sum_k a_k (q_k + 136) - 136 sum_k a_k.
+constexpr float kInt4Bias = 136.f;
 __device__ __forceinline__ u4 nib8_to_bf16(uint32_t d) {
   uint32_t o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int lo = ((int)(d << (28 - 8 * i))) >> 28;
-    const int hi = ((int)(d << (24 - 8 * i))) >> 28;
-    o[i] = (__float_as_uint((float)lo) >> 16) | (__float_as_uint((float)hi) & 0xFFFF0000u);
-  }
+  for (int j = 0; j < 4; ++j) o[j] = ((d >> (4 * j)) & 0x000F000Fu) | 0x43004300u;
   return u4{o[0], o[1], o[2], o[3]};
 }
 
@@ -275,7 +275,7 @@ struct Fmt {
 // CU keep 4 x 32 KB in flight while they wait.
 struct Ring {
   u4 r[kRing];
-  float s[kRing];
+  uint32_t s[kRing];   // int4: fp16 scale bits of each fragment's column
 };
 
 struct SlotMap {
@@ -319,8 +319,10 @@ __device__ __forceinline__ void next_batch(const Mat& M, const Lin& L, LCur& l, 
         } else {
           ring.r[i * TPU + t] = __builtin_nontemporal_load((gu4*)(wb + fo));
           if constexpr (WF == W_INT4) {
+            // raw fp16 bits: converting here would wait on the load (and,
+            // with in-order load counting, on every load before it)
             const gu16* sp = (gu16*)(wb2 + (fi0 + (long long)i * kWaves * TPU + t) * 32 + (lane & 15) * 2);
-            ring.s[i * TPU + t] = (float)__builtin_bit_cast(_Float16, (uint16_t)*sp);
+            ring.s[i * TPU + t] = *sp;
           }
         }
       }
@@ -329,7 +331,7 @@ __device__ __forceinline__ void next_batch(const Mat& M, const Lin& L, LCur& l, 
       for (int t = 0; t < RPC; ++t) ring.r[i * RPC + t] = u4{0u, 0u, 0u, 0u};
       if constexpr (WF == W_INT4) {
 #pragma unroll
-        for (int t = 0; t < TPU; ++t) ring.s[i * TPU + t] = 0.f;
+        for (int t = 0; t < TPU; ++t) ring.s[i * TPU + t] = 0u;
       }
     }
   }
@@ -575,6 +577,31 @@ __device__ __forceinline__ void stage_window(const Lin& L, const GemmIO& io, int
     __builtin_amdgcn_global_load_lds((gvoid*)(src + i0 + lane), (lvoid*)(smem + (size_t)i0 * 16), 16, 0, 0);
 }
 
+// int4: per 128-k chunk of the staged window and per row, the sum of the A
+// operand (hi + lo) over the chunk's k, for the offset correction
+// (kInt4Bias); [chunk][16 rows] floats after the window.  Called by the whole
+// workgroup after the window's loads are complete and visible.
+__device__ __forceinline__ void int4_rowsums(const unsigned char* smem, int nch, float* S) {
+  const int t = threadIdx.x;
+  const int ai = t >> 4, row = t & 15;   // 256 threads: 16 chunks x 16 rows
+  if (ai < nch) {
+    const uint4* aw = reinterpret_cast<const uint4*>(smem) + (long long)ai * 4 * 128;
+    float sum = 0.f;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg) {
+        const uint4 h = aw[q4 * 128 + row + 16 * kg], l = aw[q4 * 128 + 64 + row + 16 * kg];
+        const uint32_t hw[4] = {h.x, h.y, h.z, h.w}, lw[4] = {l.x, l.y, l.z, l.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sum += (bf2f(hw[e] & 0xFFFFu) + bf2f(lw[e] & 0xFFFFu)) + (bf2f(hw[e] >> 16) + bf2f(lw[e] >> 16));
+      }
+    S[ai * 16 + row] = sum;
+  }
+  __syncthreads();
+}
+
 // Dependency bookkeeping of the dataflow edges (one 64-column block of a
 // phase's output = one supergroup).
 // KV head of the QKV output block starting at column c0.
@@ -631,6 +658,10 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
   if (EPI == EPI_SWIGLU || EPI == EPI_LOGITS || EPI == EPI_QKV || (EPI == EPI_STORE && io.scale)) row_scales(P, io.ss_in, C->rs);
   __builtin_amdgcn_s_waitcnt(0);   // the window's direct loads
   __syncthreads();
+  float* const S4 = reinterpret_cast<float*>(smem + kAWindowBytes);   // int4 row sums
+  if constexpr (WF == W_INT4) {
+    if (u0 < u1) int4_rowsums(smem, L.wlen(sw), S4);
+  }
   wstamp(wst, 1);
   if (u0 >= u1) {
     wstamp(wst, 2);
@@ -657,28 +688,66 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     if (!live) return;
     const uint4* aw = reinterpret_cast<const uint4*>(smem) + (long long)c0 * F::ACH * 128;
     if constexpr (WF == W_INT4) {
+      // The A fragments (and row sums) of chunk i + 1 are read from LDS
+      // while chunk i's MFMAs run, and chunk i's scaled, offset-corrected
+      // sum is added once chunk i + 1's MFMAs are issued (its result is
+      // ready by then); acc still takes the chunks in order.
+      u4 ch[4], cl[4], nh[4], nl[4];
+      f32x4 crs, nrs, prs = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 pg[TPU];
+      uint32_t psc[TPU];
+      auto read_chunk = [&](int i, u4 (&h)[4], u4 (&l)[4], f32x4& rs) {
+        const int ai = i < n ? i : 0;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          h[q4] = __builtin_bit_cast(u4, aw[(ai * 4 + q4) * 128 + lane]);
+          l[q4] = __builtin_bit_cast(u4, aw[(ai * 4 + q4) * 128 + 64 + lane]);
+        }
+        // this lane's four rows: 4 (lane / 16) .. +3
+        rs = *reinterpret_cast<const f32x4*>(S4 + (c0 + ai) * 16 + 4 * (lane >> 4));
+      };
+      auto fold = [&]() {
+#pragma unroll
+        for (int t = 0; t < TPU; ++t) {
+          const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)psc[t]);
+          acc[t] += sc * (pg[t] - kInt4Bias * prs);
+        }
+      };
+      read_chunk(0, ch, cl, crs);
 #pragma unroll
       for (int i = 0; i < F::U; ++i) {
-        const int ai = i < n ? i : 0;
+        if (i + 1 < F::U) read_chunk(i + 1, nh, nl, nrs);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 gacc[TPU];
 #pragma unroll
         for (int t = 0; t < TPU; ++t) gacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const u4 ah = __builtin_bit_cast(u4, aw[(ai * 4 + q4) * 128 + lane]);
-          const u4 al = __builtin_bit_cast(u4, aw[(ai * 4 + q4) * 128 + 64 + lane]);
 #pragma unroll
           for (int t = 0; t < TPU; ++t) {
             const u4 wv = nib8_to_bf16(ring.r[i * TPU + t][q4]);
-            gacc[t] = mfma(ah, wv, gacc[t]);
-            gacc[t] = mfma(al, wv, gacc[t]);
+            gacc[t] = mfma(ch[q4], wv, gacc[t]);
+            gacc[t] = mfma(cl[q4], wv, gacc[t]);
           }
         }
-#pragma unroll
-        for (int t = 0; t < TPU; ++t) acc[t] += ring.s[i * TPU + t] * gacc[t];
-        // keep each chunk's A reads next to its MFMAs (bounded register use)
+        if (i > 0) fold();
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < TPU; ++t) {
+          pg[t] = gacc[t];
+          psc[t] = ring.s[i * TPU + t];
+        }
+        prs = crs;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          ch[q4] = nh[q4];
+          cl[q4] = nl[q4];
+        }
+        crs = nrs;
       }
+      fold();
     } else {
       constexpr int GR = 4;   // chunks per group
       static_assert(F::U % GR == 0, "batch not a whole number of groups");
@@ -773,6 +842,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
       stage_window<WF>(L, io, sk, sw, smem);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      if constexpr (WF == W_INT4) int4_rowsums(smem, L.wlen(sw), S4);
     }
   }
 
@@ -859,7 +929,7 @@ __device__ __forceinline__ void gemm_prefetch(const Mat M, const SlotMap sm, boo
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {   // nothing to stream: a defined, unused ring
       ring.r[i] = u4{0u, 0u, 0u, 0u};
-      ring.s[i] = 0.f;
+      ring.s[i] = 0u;
     }
     return;
   }
@@ -1699,12 +1769,11 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
 }
 
 size_t pass_lds_bytes(int wfmt, int max_rows_attn, int D) {
-  const size_t gemm = (size_t)kAWindowBytes;
+  const size_t gemm = (size_t)kAWindowBytes + (wfmt == W_INT4 ? 16 * 16 * 4 : 0);   // + int4 row sums
   const size_t attn = attn_lds_bytes((max_rows_attn + 15) / 16, D);
   const size_t route = 4 * (256 + 16 * 16 * 2);
   size_t b = gemm > attn ? gemm : attn;
   if (route > b) b = route;
-  (void)wfmt;
   return b + kCtlBytes;
 }
 

@@ -15,8 +15,11 @@ __device__ __forceinline__ uint32_t f2bf_r(float f) {
 // dt / tpu, half dt % tpu; fragment (unit, chunk c) is stored at
 // ((sg * nkc + c) * kWaves + w) * tpu + half with sg = unit / kWaves,
 // w = unit % kWaves.  bf16 / fp32 fragment lane l holds k = 32c + 8(l/16) + e
-// (e = 0..7) of column 16t + l%16; int4 dword cc of lane l holds nibbles
-// k = 128c + 32cc + 8(l/16) + e.  K and N tails are zero.  With
+// (e = 0..7) of column 16t + l%16; int4 dword cc of lane l holds the
+// nibbles of k = 128c + 32cc + 8(l/16) + e, stored offset (u = q + 8, in
+// 0..15) with even e = 2j at bits 4j and odd e = 2j+1 at bits 16 + 4j, so
+// (dword >> 4j) & 0x000F000F holds the pair (e = 2j, 2j+1) in the low bits
+// of each 16-bit half.  K and N tails are zero (u = 8).  With
 // pair_dim > 0 the columns of every pair_dim-wide head are taken
 // interleaved: destination column 2i + h of a head is source column
 // i + h * pair_dim / 2 (rotary pairs side by side).
@@ -51,9 +54,9 @@ __global__ void k_retile(const void* __restrict__ src, const uint16_t* __restric
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int k = c * 128 + cc * 32 + (l >> 4) * 8 + e;
-          uint32_t nib = 0;
+          uint32_t nib = 0;   // two's complement q
           if (n < N && k < K) nib = (sq[(long long)(k >> 1) * N + sn] >> ((k & 1) * 4)) & 0xFu;
-          d |= nib << (4 * e);
+          d |= (nib ^ 0x8u) << (4 * (e >> 1) + 16 * (e & 1));
         }
         dw[cc] = d;
       }
