@@ -265,7 +265,11 @@ def measure_k(sess: Session, k: int, warmup: int, steps: int):
     if [r[1] for r in rec2] != [r[1] for r in rec]:
         raise RuntimeError("replayed steps accepted different counts: the pass is not deterministic")
     accepted = sum(n + 1 for _, n in rec)
-    bytes_total = sum(sess.h.pass_bytes(L, k) for L, _ in rec)
+    if sess.spec.moe:   # the loaded experts per pass come from the profiled replay's union counts
+        n_p, _, by_p = prof["pass"]
+        bytes_total = by_p / n_p * len(rec)
+    else:
+        bytes_total = sum(sess.h.pass_bytes(L, k) for L, _ in rec)
     return dict(k=k, steps=steps, seconds=dt, ms_per_step=dt / steps * 1e3, accepted=accepted,
                 acc_tok_s=accepted / dt, verified_tok_s=steps * (k + 1) / dt,
                 mean_accept=accepted / steps, pass_gb=bytes_total / steps / 1e9,
