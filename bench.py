@@ -41,16 +41,21 @@ HBM_PEAK_GBS = 8000.0
 GREEDY_WORKLOADS = ("llama7b", "llama7b_int4", "moe", "tiny")
 STOCHASTIC_WORKLOADS = ("qwen7b",)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-PASS_SOURCE = os.path.join(ROOT, "target_model_verification_amd", "csrc", "pass.hip")
+# the pass kernel's sources: counters recorded for other sources are stale
+PASS_SOURCES = [os.path.join(ROOT, "target_model_verification_amd", "csrc", f)
+                for f in ("pass.hip", "sv_common.h", "stream_plan.h")]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_digest(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_digest(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -92,7 +97,7 @@ def traffic_from(fetch_csv: str, write_csv: str, command: str):
     gib_kib = float(1 << 20)
     f_scale, w_scale = gib_kib / fcopy, gib_kib / wcopy
     traffic = (fetch * f_scale + write * w_scale) * 1024.0
-    out = {"pass_source_sha256_16": source_digest(PASS_SOURCE),
+    out = {"pass_sources_sha256_16": source_digest(PASS_SOURCES),
            "per_launch_bytes": {"pass": round(traffic)},
            "fetch_kib_per_launch": fetch, "write_kib_per_launch": write,
            "copy_fetch_kib": fcopy, "copy_write_kib": wcopy,
@@ -292,7 +297,7 @@ def traffic_for(kernel_class: str):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("pass_source_sha256_16") != source_digest(PASS_SOURCE):
+    if t.get("pass_sources_sha256_16") != source_digest(PASS_SOURCES):
         return None
     return t.get("per_launch_bytes", {}).get(kernel_class)
 

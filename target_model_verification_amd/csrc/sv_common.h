@@ -23,7 +23,7 @@ constexpr int kChunkK = 32;           // k per bf16 / fp32 fragment
 constexpr int kGroupK = 128;          // int4: k per fragment (= scale group)
 constexpr int kMaxRows = 16;          // block rows (k+1) per pass
 constexpr int kPage = 64;             // KV page (positions); attention sub-chunk
-constexpr int kGroupPages = 4;        // pages per attention work item (fixed grid)
+constexpr int kGroupPages = 3;        // pages per attention work item (fixed grid)
 constexpr int kGroupPos = kPage * kGroupPages;
 constexpr int kMaxAttnRows = 128;     // (k+1) * (n_q_heads / n_kv_heads) per KV head
 constexpr int kAttnRT = kMaxAttnRows / 16;   // attention row tiles per KV head at most
