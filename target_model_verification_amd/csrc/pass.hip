@@ -1538,14 +1538,32 @@ __device__ __forceinline__ void route_block(const PassP& P, const float* bias, u
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < P.E; e += kThreads) used[e] = 0;
   __syncthreads();
-  for (int row = wave; row < P.m; row += kWaves) {
-    constexpr int EPL = 4;
+  constexpr int EPL = 4;                 // experts per lane (E <= 256)
+  constexpr int RPW = kMaxRows / kWaves;  // rows per wave
+  // every row's router logits of this wave are loaded before any is used
+  float zr[RPW][EPL];
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    const int row = wave + kWaves * k;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      zr[k][i] = (row < P.m && e < P.E) ? cld(P.rlog + row * P.ldr + e) : 0.f;
+    }
+  }
+  float bz[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) bz[i] = lane + 64 * i < P.E ? *glb(bias + lane + 64 * i) : 0.f;
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    const int row = wave + kWaves * k;
+    if (row >= P.m) break;
     float z[EPL];
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
-      z[i] = e < P.E ? cld(P.rlog + row * P.ldr + e) + *glb(bias + e) : -INFINITY;
+      z[i] = e < P.E ? zr[k][i] + bz[i] : -INFINITY;
       mx = fmaxf(mx, z[i]);
     }
 #pragma unroll
