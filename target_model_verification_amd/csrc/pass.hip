@@ -1535,77 +1535,104 @@ __device__ __forceinline__ void route_block(const PassP& P, const float* bias, u
   int* used = reinterpret_cast<int*>(smem);            // [E] (scratch; A windows not live here)
   int* sel = used + 256;                              // [16][top_k]
   float* selw = reinterpret_cast<float*>(sel + 16 * 16);
+  float* prs = selw + 16 * 16;                        // [16][E] probabilities
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < P.E; e += kThreads) used[e] = 0;
-  __syncthreads();
   constexpr int EPL = 4;                 // experts per lane (E <= 256)
-  constexpr int RPW = kMaxRows / kWaves;  // rows per wave
+  constexpr int RPW = kMaxRows / kWaves;  // rows per wave: row = wave + kWaves k
   // every row's router logits of this wave are loaded before any is used
-  float zr[RPW][EPL];
+  float z[RPW][EPL];
 #pragma unroll
   for (int k = 0; k < RPW; ++k) {
     const int row = wave + kWaves * k;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
-      zr[k][i] = (row < P.m && e < P.E) ? cld(P.rlog + row * P.ldr + e) : 0.f;
+      z[k][i] = (row < P.m && e < P.E) ? cld(P.rlog + row * P.ldr + e) : 0.f;
     }
   }
   float bz[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) bz[i] = lane + 64 * i < P.E ? *glb(bias + lane + 64 * i) : 0.f;
+  // softmax of every row, the rows' reductions side by side
+  float mx[RPW], sum[RPW];
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    mx[k] = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      z[k][i] = lane + 64 * i < P.E ? z[k][i] + bz[i] : -INFINITY;
+      mx[k] = fmaxf(mx[k], z[k][i]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) mx[k] = fmaxf(mx[k], __shfl_xor(mx[k], o, 64));
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    sum[k] = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      z[k][i] = (lane + 64 * i < P.E) ? expf(z[k][i] - mx[k]) : 0.f;   // now the probabilities (unnormalised)
+      sum[k] += z[k][i];
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1)
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) sum[k] += __shfl_xor(sum[k], o, 64);
+  // top_k by rank: an expert's rank is the number of experts ahead of it in
+  // the order (probability descending, lower id first on ties); the top_k
+  // are the ranks below top_k, in rank order (a NaN counts as -inf, so the
+  // ranks always form a permutation)
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    const int row = wave + kWaves * k;
+    if (row < P.m) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        if (e < P.E) prs[row * P.E + e] = z[k][i] == z[k][i] ? z[k][i] : -INFINITY;
+      }
+    }
+  }
+  __syncthreads();   // prs and used[] complete
 #pragma unroll
   for (int k = 0; k < RPW; ++k) {
     const int row = wave + kWaves * k;
     if (row >= P.m) break;
-    float z[EPL];
-    float mx = -INFINITY;
+    const float* pr = prs + row * P.E;
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
-      z[i] = e < P.E ? zr[k][i] + bz[i] : -INFINITY;
-      mx = fmaxf(mx, z[i]);
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    float pr[EPL], sum = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      pr[i] = (lane + 64 * i < P.E) ? expf(z[i] - mx) : 0.f;
-      sum += pr[i];
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
-    bool taken[EPL] = {false, false, false, false};
-    for (int r = 0; r < P.top_k; ++r) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        const int e = lane + 64 * i;
-        if (e < P.E && !taken[i] && (pr[i] > bv || (pr[i] == bv && e < bi))) { bv = pr[i]; bi = e; }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      if (bi >= P.E) bi = 0;   // only reachable with non-finite router logits
-      if ((bi & 63) == lane) taken[bi >> 6] = true;
-      if (lane == 0) {
-        sel[row * P.top_k + r] = bi;
-        selw[row * P.top_k + r] = bv / sum;
-        used[bi] = 1;
+      if (e < P.E) {
+        const float pe = pr[e];
+        int rank = 0;
+        for (int j = 0; j < P.E; ++j) {
+          const float pj = pr[j];
+          rank += (pj > pe || (pj == pe && j < e)) ? 1 : 0;
+        }
+        if (rank < P.top_k) {
+          sel[row * P.top_k + rank] = e;
+          selw[row * P.top_k + rank] = z[k][i] / sum[k];
+          used[e] = 1;
+        }
       }
     }
   }
   __syncthreads();
-  if (tid == 0) {
+  // the union in ascending expert id (wave 0: a ballot scan)
+  if (wave == 0) {
     int cnt = 0;
-    for (int e = 0; e < P.E; ++e)
-      if (used[e]) C->ulist[cnt++] = e;
-    C->uc = cnt;
+    for (int e0 = 0; e0 < P.E; e0 += 64) {
+      const int e = e0 + lane;
+      const bool u = e < P.E && used[e] != 0;
+      const unsigned long long bal = __ballot(u);
+      if (u) C->ulist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = e;
+      cnt += __popcll(bal);
+    }
+    if (lane == 0) C->uc = cnt;
   }
   __syncthreads();
   if (blockIdx.x == 0) {
@@ -1789,7 +1816,7 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
 size_t pass_lds_bytes(int wfmt, int max_rows_attn, int D) {
   const size_t gemm = (size_t)kAWindowBytes + (wfmt == W_INT4 ? 16 * 16 * 4 : 0);   // + int4 row sums
   const size_t attn = attn_lds_bytes((max_rows_attn + 15) / 16, D);
-  const size_t route = 4 * (256 + 16 * 16 * 2);
+  const size_t route = 4 * (256 + 16 * 16 * 2 + 16 * 256);   // used, sel, selw, probabilities
   size_t b = gemm > attn ? gemm : attn;
   if (route > b) b = route;
   return b + kCtlBytes;
