@@ -1,0 +1,113 @@
+"""The on-device stochastic acceptance (rejection sampling at temperature 1,
+the rule the essay "LLM Inference: Speculative Decoding" names in "What is
+not here") against the oracle's acceptance applied to the GPU's own logits,
+on the cases that reduce to something plain:
+
+- q = p at every position: every draft is accepted (u < p/q = 1) and the
+  bonus token is the inverse-CDF draw from p_k;
+- q_1 a point mass on d_1 where p_0 is small: rejection at i = 1, and the
+  resample is drawn from p_0 with d_1 removed (max(0, p - q), normalised);
+- q = softmax(target logits + N(0,1) noise), as in the stochastic workload.
+
+Both sides start from the same logits (the GPU's own), so only the
+acceptance arithmetic differs: fp32 on the device, fp64 in the oracle.  A
+decision is flagged when it lies within a relative 1e-5 of flipping (the
+test's u*q against p, or u*S against the bracketing running sums); for a
+flagged decision the GPU's outcome must only be a valid one."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+from gpu_common import log, make_verifier  # noqa: E402
+from oracle import accept as oacc  # noqa: E402
+from oracle import numerics as onx  # noqa: E402
+from spec_harness import prepare  # noqa: E402
+from target_model_verification_amd import binding as B  # noqa: E402
+from target_model_verification_amd import synth  # noqa: E402
+
+K = 6
+ACC_TOL = 1e-5   # fp32 acceptance arithmetic on shared logits
+
+
+@pytest.fixture(scope="module")
+def verifier():
+    pw = prepare(synth.ALL_WORKLOADS["small_gqa"])
+    h = make_verifier(pw, max_k=15)
+    yield pw, h
+    h.close()
+
+
+def _block_logits(h, toks):
+    """Logits of the block (committed and rolled back again)."""
+    L = h.kv_len
+    lg = torch.empty((len(toks), h.spec.vocab), dtype=torch.float32, device="cuda")
+    h.step(toks, B.SPEC_ACCEPT_NONE, 0, 0, lg.data_ptr())
+    h.rollback(L)
+    return lg.cpu().numpy().astype(np.float64)
+
+
+def _check(pw, h, toks, q, u):
+    L = h.kv_len
+    V = pw.wl.spec.vocab
+    lg = torch.empty((len(toks), V), dtype=torch.float32, device="cuda")
+    qd = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float32)).cuda()
+    ud = torch.from_numpy(np.ascontiguousarray(u, dtype=np.float32)).cuda()
+    res = h.step(toks, B.SPEC_ACCEPT_STOCHASTIC, qd.data_ptr(), ud.data_ptr(), lg.data_ptr())
+    h.rollback(L)
+    ref = oacc.accept_stochastic(lg.cpu().numpy(), q, toks[1:], u, L, ACC_TOL)
+    got = (res.n_accepted, res.next_token, res.kv_len)
+    if ref.near_tie:
+        log(f"[stochastic edges] flagged {ref.tie_where}: gpu {got}, oracle "
+            f"{(ref.n_accepted, ref.next_token, ref.kv_len)}")
+        assert 0 <= res.n_accepted <= len(toks) - 1 and 0 <= res.next_token < V
+        assert res.kv_len == L + 1 + res.n_accepted
+    else:
+        assert got == (ref.n_accepted, ref.next_token, ref.kv_len)
+    return res
+
+
+def _tokens(pw, seed):
+    g = np.random.default_rng([pw.wl.seed, 71, seed])
+    return [int(pw.pending0)] + [int(x) for x in g.integers(0, pw.wl.spec.vocab, size=K)]
+
+
+def test_q_equals_p_accepts_all(verifier):
+    pw, h = verifier
+    for seed in range(4):
+        toks = _tokens(pw, seed)
+        p = onx.softmax(_block_logits(h, toks), axis=-1)
+        q = p[:K].astype(np.float32)            # q_i = p_{i-1}
+        u = np.random.default_rng([pw.wl.seed, 73, seed]).uniform(0.0, 0.99, K + 1)
+        res = _check(pw, h, toks, q, u)
+        assert res.n_accepted == K
+
+
+def test_point_mass_rejects_first(verifier):
+    pw, h = verifier
+    V = pw.wl.spec.vocab
+    for seed in range(4):
+        toks = _tokens(pw, 10 + seed)
+        lg = _block_logits(h, toks)
+        toks[1] = int(np.argmin(lg[0]))          # d_1 where p_0 is smallest
+        q = np.full((K, V), 1.0 / V, dtype=np.float32)
+        q[0] = 0.0
+        q[0, toks[1]] = 1.0
+        u = np.random.default_rng([pw.wl.seed, 79, seed]).uniform(0.01, 0.99, K + 1)
+        res = _check(pw, h, toks, q, u)
+        assert res.n_accepted == 0 and res.next_token != toks[1]
+
+
+def test_noisy_target_drafts(verifier):
+    pw, h = verifier
+    V = pw.wl.spec.vocab
+    for seed in range(6):
+        toks = _tokens(pw, 20 + seed)
+        z = _block_logits(h, toks)
+        g = np.random.default_rng([pw.wl.seed, 83, seed])
+        q = onx.softmax(z[:K] + g.standard_normal((K, V)), axis=-1).astype(np.float32)
+        u = g.uniform(0.0, 1.0, K + 1)
+        _check(pw, h, toks, q, u)
