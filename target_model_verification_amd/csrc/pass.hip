@@ -1525,12 +1525,80 @@ __device__ __forceinline__ void attn_merge_phase(const PassP& P, uint4* a_o, uns
 }
 
 // ------------------------------------------------------------ MoE routing
+// LDS of routing: used / sel / selw / probabilities from offset 0, the
+// block's router logits (when computed in the phase) from kRouteZl; both
+// inside the (then dead) A window.
+constexpr int kRouteZl = 32 * 1024;
 // Every workgroup routes the block redundantly (same inputs, same order):
 // pi = softmax(r + b) over the experts, each row keeps its top_k experts by
 // probability (ties to the lower id), weights = those probabilities; the
 // union of the rows' experts in ascending id order becomes the slot list.
 // Workgroup 0 also writes the routing record for the combine phase.
-__device__ __forceinline__ void route_block(const PassP& P, const float* bias, unsigned char* smem, int layer) {
+// Router logits of the block computed by this workgroup alone (bf16 router
+// weights, K in one A window): the normalised A operand is staged, each wave
+// takes router units wave, wave + 4, ... (16 experts each) over every K
+// chunk on MFMA, and the row-scaled logits go to zl[16][E] in LDS.  Every
+// workgroup runs the same operations in the same order, so all hold the
+// same logits.
+template <int WF>
+__device__ __forceinline__ void router_logits(const PassP& P, const Mat& Mr, const GemmIO& io, unsigned char* smem,
+                                              float* zl) {
+  Ctl* C = ctl(smem, (size_t)P.lds_bytes);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const Lin L = make_lin(Mr, 1, false);
+  stage_window<WF>(L, io, 0, 0, smem);
+  row_scales(P, io.ss_in, C->rs);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const uint4* aw = reinterpret_cast<const uint4*>(smem);
+  constexpr int NB = 32;   // fragments in flight per lane
+  constexpr int UPW = 4;   // units per wave at most (E <= 256: 16 units)
+  f32x4 acc[UPW];
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) {
+    acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int unit = wave + kWaves * j;
+    if (unit < Mr.n_units) {   // (wave-uniform)
+      const int sg = unit / kWaves, w = unit % kWaves;
+      const char* wb = static_cast<const char*>(Mr.w) + ((long long)sg * Mr.nkc * kWaves + w) * 1024 + lane * 16;
+      f32x4 a4 = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c0 = 0; c0 < Mr.nkc; c0 += NB) {
+        u4 wf[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+          wf[i] = c0 + i < Mr.nkc ? *(const gu4*)(wb + (long long)(c0 + i) * kWaves * 1024) : u4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          if (c0 + i < Mr.nkc) {
+            const u4 ah = __builtin_bit_cast(u4, aw[(c0 + i) * 128 + lane]);
+            const u4 al = __builtin_bit_cast(u4, aw[(c0 + i) * 128 + 64 + lane]);
+            a4 = mfma(ah, wf[i], a4);
+            a4 = mfma(al, wf[i], a4);
+          }
+        }
+      }
+      acc[j] = a4;
+    }
+  }
+  __syncthreads();   // every wave is done with the A window (zl lies inside it)
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) {
+    const int unit = wave + kWaves * j;
+    const int col = unit * kTileN + (lane & 15);
+    if (unit < Mr.n_units && col < P.E) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * (lane >> 4) + i;
+        zl[row * P.E + col] = C->rs[row] * acc[j][i];
+      }
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void route_block(const PassP& P, const float* bias, unsigned char* smem, int layer,
+                                            const float* zl) {
   Ctl* C = ctl(smem, (size_t)P.lds_bytes);
   int* used = reinterpret_cast<int*>(smem);            // [E] (scratch; A windows not live here)
   int* sel = used + 256;                              // [16][top_k]
@@ -1548,7 +1616,7 @@ __device__ __forceinline__ void route_block(const PassP& P, const float* bias, u
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       const int e = lane + 64 * i;
-      z[k][i] = (row < P.m && e < P.E) ? cld(P.rlog + row * P.ldr + e) : 0.f;
+      z[k][i] = (row < P.m && e < P.E) ? (zl ? zl[row * P.E + e] : cld(P.rlog + row * P.ldr + e)) : 0.f;
     }
   }
   float bz[EPL];
@@ -1768,7 +1836,14 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
       case PH_ROUTE_SWIGLU:
         sync([] {});
       {
-        route_block(P, d->bias, smem, d->layer);
+        float* zl = nullptr;
+        if constexpr (WF == W_BF16) {
+          if (d->Mr.w) {
+            zl = reinterpret_cast<float*>(smem + kRouteZl);
+            router_logits<WF>(P, d->Mr, io, smem, zl);
+          }
+        }
+        route_block(P, d->bias, smem, d->layer, zl);
         const SlotMap routed{C->ulist, C->uc, P.E, C->uc + P.n_shared};   // the union just built
         gemm_prefetch<WF, 2>(d->M, routed, false, ring);
         gemm_phase<WF, EPI_SWIGLU, 2>(P, d->M, io, routed, false, ring, smem, wst);

@@ -694,13 +694,19 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
       dn.a = act_l; dn.gain = next_gain; dn.a_out = a_site(2 * l + 2); dn.ss_out = ss_site(2 * l + 2); dn.trace = 1;
       add(dn, SPEC_K_DOWN, Lw.down.alg_bytes);
     } else {
-      Phase r = gemm_phase_desc(PH_STORE, l, Lw.router);
-      r.a = a_site(2 * l + 1); r.ss_in = ss_site(2 * l + 1); r.out = h->rlog; r.ldo = h->ldr; r.scale = 1;
-      add(r, SPEC_K_ROUTER, Lw.router.alg_bytes);
+      // bf16 routers with K in one A window are computed inside the routed
+      // phase by every workgroup (no router phase, no barrier before routing)
+      const bool fuse_router = h->wfmt == W_BF16 && Lw.router.m.n_win == 1;
+      if (!fuse_router) {
+        Phase r = gemm_phase_desc(PH_STORE, l, Lw.router);
+        r.a = a_site(2 * l + 1); r.ss_in = ss_site(2 * l + 1); r.out = h->rlog; r.ldo = h->ldr; r.scale = 1;
+        add(r, SPEC_K_ROUTER, Lw.router.alg_bytes);
+      }
       Phase g = gemm_phase_desc(PH_ROUTE_SWIGLU, l, Lw.ex_gateup);
       g.slot_mode = 1; g.a = a_site(2 * l + 1); g.ss_in = ss_site(2 * l + 1); g.a_out = act_l;
       g.a_out_slot = h->a_act_slot; g.bias = Lw.router_bias;
-      add(g, SPEC_K_EXPERT_GATEUP, Lw.ex_gateup.alg_bytes);
+      if (fuse_router) g.Mr = Lw.router.m;
+      add(g, SPEC_K_EXPERT_GATEUP, Lw.ex_gateup.alg_bytes + (fuse_router ? Lw.router.alg_bytes : 0.0));
       Phase dn = gemm_phase_desc(PH_STORE, l, Lw.ex_down);
       dn.slot_mode = 2; dn.a = act_l; dn.a_slot = h->a_act_slot; dn.out = h->ey; dn.ldo = h->ldx;
       dn.out_slot = h->ey_slot; dn.scale = 0;

@@ -80,6 +80,7 @@ struct Phase {
   uint4* a_out; long long a_out_slot;
   const float* bias;      // ROUTE: router bias
   void* kv;               // QKV / ATTN: the layer's KV pages
+  Mat Mr;                 // ROUTE: router matrix computed in the phase (Mr.w null: read the router phase's logits)
   int next_gemm;          // index of the next weight-streaming phase (n_prog if none)
   int dep;                // inputs: 0 after a grid barrier; else waits on this layer's
                           // ready counters (kDepHeads / kDepOWin)
