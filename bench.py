@@ -14,10 +14,13 @@ Timed region: `--steps` verification steps after `--warmup` untimed ones,
 bracketed by device synchronizations; inputs are resident in HBM (weights,
 KV cache); each step uploads its k+1 token ids and reads back the 12-byte
 result, as the C ABI defines.  Printed: one JSON line with accepted tokens/s
-(metric value), the HBM roofline of the dominant kernel (algorithmic bytes
-per launch over its mean launch time, from HIP events recorded on the
-library's stream while the same steps are replayed), and the CPU oracle
-timed on a bounded sample of the same workload as a baseline.
+(metric value), the HBM roofline of the dominant kernel (the pass kernel:
+algorithmic bytes per launch, spec_pass_bytes at each step's committed
+length, over its mean launch time from HIP events recorded around each
+launch on the library's stream during the timed steps), and the CPU oracle
+timed on a bounded sample of the same workload as a baseline.  The same
+steps are then replayed from the same state with per-phase stamps (stderr
+lines only).
 
 Flags: --gpus N (only 1 is supported), --steps K, --warmup W, --workload
 NAME, --k K, --k-sweep (extra per-k lines on stderr), --no-cpu-baseline,
@@ -153,16 +156,18 @@ class Session:
         from target_model_verification_amd import synth
         return [synth.draft_corruption(self.wl, first_round + r, k) for r in range(n)]
 
-    def run(self, k: int, corr, s: int, pending: int, profile: bool = False):
-        """Runs len(corr) rounds from sequence index s.  Returns per-round
-        (L, n_acc), the new s and pending token, and the elapsed seconds."""
+    def run(self, k: int, corr, s: int, pending: int, profile=0):
+        """Runs len(corr) rounds from sequence index s (profile: 0 off, 1
+        events + per-phase stamps, 2 events only).  Returns per-round
+        (L, n_acc), the new s and pending token, the elapsed seconds and the
+        profile counters."""
         import torch
         np, B = self.np, self.B
         h = self.h
         out = []
         tok = np.empty(k + 1, dtype=np.int32)
         if profile:
-            h.profile(True)
+            h.profile(profile)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for flags, ids in corr:
@@ -176,8 +181,9 @@ class Session:
         torch.cuda.synchronize()
         dt = time.perf_counter() - t0
         prof = h.profile_read() if profile else None
-        if profile:
+        if profile == 1:
             self.detail = h.profile_detail()
+        if profile:
             h.profile(False)
         return out, s, pending, dt, prof
 
@@ -222,16 +228,23 @@ def measure_k_stochastic(sess: Session, k: int, warmup: int, steps: int):
     h.rollback(sess.L0)
     pending, rec, inputs, dt = sess.pending0, [], [], 0.0
     L_start = None
+    ev_ms = ev_bytes = 0.0
     for r in range(warmup + steps):
         toks, q_dev, u_dev = draft_round(sess, r, pending, k, zbuf)
         torch.cuda.synchronize()
         L = h.kv_len
         if r == warmup:
             L_start = L
+        if r >= warmup:
+            h.profile(2)   # HIP events around the pass and acceptance kernels only
         t0 = time.perf_counter()
         res = h.step(toks, B.SPEC_ACCEPT_STOCHASTIC, q_dev.data_ptr(), u_dev.data_ptr())
         el = time.perf_counter() - t0
         if r >= warmup:
+            _, ms_p, by_p = h.profile_read()["pass"]
+            h.profile(0)
+            ev_ms += ms_p
+            ev_bytes += by_p
             dt += el
             rec.append((L, res.n_accepted))
             inputs.append((toks, q_dev, u_dev))
@@ -249,10 +262,12 @@ def measure_k_stochastic(sess: Session, k: int, warmup: int, steps: int):
         raise RuntimeError("replayed steps accepted different counts: the pass is not deterministic")
     accepted = sum(n + 1 for _, n in rec)
     bytes_total = sum(h.pass_bytes(L, k, B.SPEC_ACCEPT_STOCHASTIC) for L, _ in rec)
+    timed = dict(pass_launches=steps, pass_ms=ev_ms, pass_bytes=ev_bytes)
     return dict(k=k, steps=steps, seconds=dt, ms_per_step=dt / steps * 1e3, accepted=accepted,
                 acc_tok_s=accepted / dt, verified_tok_s=steps * (k + 1) / dt,
                 mean_accept=accepted / steps, pass_gb=bytes_total / steps / 1e9,
-                wall_gbs=bytes_total / dt / 1e9, L_start=L_start, prof=prof, profiled_seconds=None)
+                wall_gbs=bytes_total / dt / 1e9, L_start=L_start, prof=prof, timed=timed,
+                profiled_seconds=None)
 
 
 def measure_k(sess: Session, k: int, warmup: int, steps: int):
@@ -262,31 +277,34 @@ def measure_k(sess: Session, k: int, warmup: int, steps: int):
     sess.h.rollback(sess.L0)
     _, s, pending, _, _ = sess.run(k, corr[:warmup], 0, sess.pending0)
     L_start = sess.h.kv_len
-    rec, s_end, _, dt, _ = sess.run(k, corr[warmup:], s, pending)
-    # the same steps again from the same state, with HIP events around
-    # every kernel launch on the library's stream
+    # timed steps, with HIP events around the pass and acceptance kernels on
+    # the library's stream (events only: the pass runs as unprofiled)
+    rec, s_end, _, dt, tprof = sess.run(k, corr[warmup:], s, pending, profile=2)
+    # the same steps again from the same state, with per-phase stamps
     sess.h.rollback(L_start)
-    rec2, _, _, dt2, prof = sess.run(k, corr[warmup:], s, pending, profile=True)
+    rec2, _, _, dt2, prof = sess.run(k, corr[warmup:], s, pending, profile=1)
     if [r[1] for r in rec2] != [r[1] for r in rec]:
         raise RuntimeError("replayed steps accepted different counts: the pass is not deterministic")
     accepted = sum(n + 1 for _, n in rec)
-    if sess.spec.moe:   # the loaded experts per pass come from the profiled replay's union counts
-        n_p, _, by_p = prof["pass"]
-        bytes_total = by_p / n_p * len(rec)
-    else:
-        bytes_total = sum(sess.h.pass_bytes(L, k) for L, _ in rec)
+    n_p, ms_p, by_p = tprof["pass"]   # spec_pass_bytes per step (MoE: with its loaded experts)
+    bytes_total = by_p
+    timed = dict(pass_launches=n_p, pass_ms=ms_p, pass_bytes=by_p)
     return dict(k=k, steps=steps, seconds=dt, ms_per_step=dt / steps * 1e3, accepted=accepted,
                 acc_tok_s=accepted / dt, verified_tok_s=steps * (k + 1) / dt,
                 mean_accept=accepted / steps, pass_gb=bytes_total / steps / 1e9,
-                wall_gbs=bytes_total / dt / 1e9, L_start=L_start, prof=prof, profiled_seconds=dt2)
+                wall_gbs=bytes_total / dt / 1e9, L_start=L_start, prof=prof, timed=timed,
+                profiled_seconds=dt2)
 
 
-def dominant(prof):
-    """The persistent pass kernel (k_pass): one launch per step carrying every
-    phase of the block forward; (name, launches, ms, bytes)."""
-    name = "pass"
-    n, ms, by = prof[name]
-    return name, n, ms, by
+def expected_tokens(wl, k: int):
+    """E[n_acc + 1] per round for drafts corrupted independently with
+    probability c (per-draft agreement a = 1 - c (1 - 1/V)): (1 - a^(k+1)) /
+    (1 - a) (essay "Being right five times in a row is rare"); None for
+    drafts drawn from a noisy distribution (stochastic workloads)."""
+    if wl.accept != "greedy":
+        return None
+    a = 1.0 - wl.corruption * (1.0 - 1.0 / wl.spec.vocab)
+    return float(k + 1) if a == 1.0 else (1.0 - a ** (k + 1)) / (1.0 - a)
 
 
 def traffic_for(kernel_class: str):
@@ -310,11 +328,25 @@ def cpu_baseline(wl, W, k: int, L: int, seconds: float, mean_accept: float):
     from oracle import accept as oacc
     from oracle import model as om
     from target_model_verification_amd import synth
+    affinity = len(os.sched_getaffinity(0))
+    blas, blas_threads = "unknown", None
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                blas = f"{i.get('internal_api')} {i.get('version')} ({os.path.basename(i.get('filepath', ''))})"
+                blas_threads = i.get("num_threads")
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+        pass
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     t = time.time()
     M = om.OracleModel(wl.spec, W, np.float32)
     kv = om.KVCache.empty(wl.spec, L + k + 1, np.float32)
@@ -334,8 +366,9 @@ def cpu_baseline(wl, W, k: int, L: int, seconds: float, mean_accept: float):
         if el >= seconds or (n >= 2 and el + el / n > 2 * seconds):
             break
     step_s = el / n
-    return {"value": round(mean_accept / step_s, 3), "unit": "accepted tok/s", "cores": int(cores),
-            "kind": "oracle",
+    cores = int(blas_threads) if blas_threads else affinity
+    return {"value": round(mean_accept / step_s, 3), "unit": "accepted tok/s", "cores": cores,
+            "kind": "oracle", "affinity_cpus": affinity, "cpu_model": cpu_model, "blas": blas,
             "sample": (f"{n} verification steps (block pass over k+1={k + 1} tokens at committed length "
                        f"{L} + greedy acceptance) of the full {wl.spec.name} model in the NumPy oracle, "
                        f"weights as fp32 BLAS operands, {el:.1f} s; KV cache filled with seeded synthetic "
@@ -399,20 +432,24 @@ def main():
                                                                    mean[3], mx[3], ms / n * 1e3 - mx[3]))
                     log(line)
     r = results[k]
-    name, n, ms, by = dominant(r["prof"])
-    per_launch_bytes = by / n
-    per_launch_s = ms / n / 1e3
+    # the dominant kernel is the persistent pass kernel (k_pass), one launch
+    # per step carrying every phase of the block forward; its launches are
+    # timed with HIP events during the timed steps
+    t = r["timed"]
+    per_launch_bytes = t["pass_bytes"] / t["pass_launches"]
+    per_launch_s = t["pass_ms"] / t["pass_launches"] / 1e3
     achieved = per_launch_bytes / per_launch_s / 1e9
-    traffic = traffic_for(name)
+    traffic = traffic_for("pass")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "k_pass (persistent verification pass)", "bytes_per_launch": round(per_launch_bytes),
-                "us_per_launch": round(per_launch_s * 1e6, 2),
+                "us_per_launch": round(per_launch_s * 1e6, 2), "launches": t["pass_launches"],
                 "pass_wall_gbs": round(r["wall_gbs"], 1),
                 "pass_wall_frac": round(r["wall_gbs"] / HBM_PEAK_GBS, 4)}
     cpu = None
     if not args.no_cpu_baseline and wl.accept == "greedy":
         cpu = cpu_baseline(wl, W, k, r["L_start"], args.cpu_seconds, r["mean_accept"])
+    e_tok = expected_tokens(wl, k)
     line = {
         "metric": "accepted tok/s + verify-pass HBM GB/s vs peak, 7B bf16 k=8, single sequence",
         "value": round(r["acc_tok_s"], 2), "unit": "accepted tok/s", "n_gpus": 1, "steps": args.steps,
@@ -427,16 +464,27 @@ def main():
                                    else "stochastic acceptance at temperature 1") + ", single sequence"),
                    "k": k, "context": wl.context, "verified_tok_s": round(r["verified_tok_s"], 2),
                    "mean_tokens_per_step": round(r["mean_accept"], 4),
+                   "expected_tokens_per_step": None if e_tok is None else round(e_tok, 4),
+                   "expected_accepted_tok_s": None if e_tok is None else round(e_tok / r["ms_per_step"] * 1e3, 2),
                    "pass_bytes_gb": round(r["pass_gb"], 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     if args.k_sweep:
+        def frac(v):
+            t = v["timed"]
+            return round(t["pass_bytes"] / (t["pass_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4)
         line["k_sweep"] = {str(kk): {"ms_per_step": round(v["ms_per_step"], 4),
                                      "acc_tok_s": round(v["acc_tok_s"], 2),
                                      "verified_tok_s": round(v["verified_tok_s"], 2),
+                                     "us_per_pass": round(v["timed"]["pass_ms"] / v["timed"]["pass_launches"] * 1e3, 1),
+                                     "pass_hbm_frac": frac(v),
                                      "wall_gbs": round(v["wall_gbs"], 1)} for kk, v in results.items()}
+    # explicit teardown before the interpreter exits: the verifier's device
+    # memory is freed and the stream drained while the HIP runtime is whole
     sess.h.close()
+    del sess
+    torch.cuda.synchronize()
     print(json.dumps(line), flush=True)
 
 

@@ -15,8 +15,8 @@
  *   probability min(1, p/q), otherwise resample from the normalized positive
  *   part of p - q; a bonus token is drawn from the last row when all drafts
  *   pass.  Only accepted entries stay in the KV cache (essay "The loop",
- *   step 5; S2-MoE section 4.3, "only accepted tokens are committed to the
- *   shared cache").
+ *   step 5; S2-MoE section 4.3, where the cache shared by drafting and
+ *   verification keeps the entries of accepted tokens alone).
  *
  * Conventions
  *   - Every function returns a spec_status (0 = SPEC_OK) unless stated.
@@ -83,7 +83,11 @@ typedef struct {
   int32_t gemm_k_split;  /* K elements per staged activation window of the weight-streaming
                             phases (multiple of 128, at most 2048); 0 = 2048.  Smaller windows
                             split every output over more partial sums (a test knob). */
-  int32_t reserved[7];   /* must be zero */
+  int32_t kv_page_seed;  /* 0: cache page i holds positions 64i .. 64i+63 (identity page
+                            table); otherwise the logical pages are mapped to physical pages
+                            by a permutation drawn from this seed (results are identical;
+                            a test knob for the page indirection). */
+  int32_t reserved[6];   /* must be zero */
 } spec_config;
 
 /* Weight tensor kinds.  Matrices are row-major [K][N] with y = x . W. */
@@ -201,7 +205,7 @@ typedef enum {
   SPEC_K_NCLASSES = 15
 } spec_kernel_class;
 
-/* on != 0: every following step times the pass kernel and the acceptance
+/* on = 1: every following step times the pass kernel and the acceptance
  * kernel with HIP events recorded on the handle's stream, and each phase of
  * the pass with device wall-clock stamps taken by workgroup 0 after every
  * grid barrier (a phase's time includes its barrier); it accumulates per-
@@ -209,7 +213,11 @@ typedef enum {
  * activations each phase must move).  SPEC_K_ATTN_COMBINE is the merge of
  * the attention groups (no algorithmic bytes of its own: its partials are
  * an artefact of the split); SPEC_K_ROUTE stays zero (routing runs inside
- * SPEC_K_EXPERT_GATEUP).  Enabling resets the counters. */
+ * SPEC_K_EXPERT_GATEUP).  on = 2: only the HIP events around the pass and
+ * acceptance kernels (no per-phase stamps, so the pass runs exactly as
+ * unprofiled).  In both modes SPEC_K_PASS accumulates the bytes of
+ * spec_pass_bytes for each step (MoE: with the experts the step loaded).
+ * on = 0 turns profiling off.  Enabling resets the counters. */
 int spec_profile_enable(spec_verify_t* h, int32_t on);
 
 /* Reads the accumulated per-class figures since the last enable.
@@ -240,10 +248,21 @@ int spec_profile_raw(const spec_verify_t* h, uint64_t* out, int64_t n, int64_t* 
 /* Like spec_verify_step, and additionally copies the residual stream after
  * every layer into trace_dev (device fp32 [n_layers][k+1][d_model], may be
  * NULL) and, for MoE models, the number of routed experts loaded by each
- * layer into union_dev (device int32 [n_layers], may be NULL). */
+ * layer into union_dev (device int32 [n_layers], may be NULL) and the
+ * experts each block row selected into route_dev (device int32
+ * [n_layers][k+1][top_k], in rank order: probability descending, lower
+ * expert id first on ties; may be NULL; ignored for dense models). */
 int spec_verify_step_debug(spec_verify_t* h, const int32_t* tokens, int32_t k, int32_t mode,
                            const float* q_dev, const float* u_dev, spec_step_result* out,
-                           float* logits_dev, float* trace_dev, int32_t* union_dev);
+                           float* logits_dev, float* trace_dev, int32_t* union_dev,
+                           int32_t* route_dev);
+
+/* Debugging aid for the rollback rule (essay "The loop", step 5: entries
+ * of rejected drafts must never influence later steps): overwrites every
+ * cache entry at positions kv_len .. max_ctx-1 (keys and values of every
+ * layer and KV head) with NaN, on the handle's stream, and waits for it.
+ * A later step that read any of them would produce NaN logits. */
+int spec_kv_poison_dead(spec_verify_t* h);
 
 /* Algorithmic bytes one verification pass must move for this handle's
  * model at committed length L with block size k+1 and (MoE) `experts_loaded`

@@ -10,8 +10,6 @@ Test infrastructure only (see the package docstring).
 * Expected output tokens per round for per-token acceptance rate a and
   lookahead k: (1 - a^(k+1)) / (1 - a), rising to the ceiling 1/(1-a)
   (same essay, "Being right five times in a row is rare").
-* Throughput decomposition: tokens per iteration over bytes per iteration
-  times bandwidth (S2-MoE section 1, the Throughput equation).
 """
 from __future__ import annotations
 
@@ -52,6 +50,3 @@ def acceptance_rate_from_corruption(c: float, vocab: int) -> float:
     agrees with probability 1/V)."""
     return 1.0 - c * (1.0 - 1.0 / vocab)
 
-
-def throughput(tokens_per_iter: float, bytes_per_iter: float, bandwidth: float) -> float:
-    return tokens_per_iter / bytes_per_iter * bandwidth

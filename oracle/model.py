@@ -17,8 +17,8 @@ open is listed with its reading in the design notes):
   causal attention over cached entries; x += o Wo; h' = rmsnorm(x)*g2;
   dense: x += (silu(h' Wg) * (h' Wu)) Wd;
   MoE: x += sum_{e in top_k(pi)} pi_e FFN_e(h') + FFN_shared(h'),
-  pi = softmax(h' Wr + b) over all experts (S2-MoE section 2.1: a small
-  subset of experts is activated per token).
+  pi = softmax(h' Wr + b) over all experts (S2-MoE section 2.1: each token
+  runs only a few of the experts).
   Final: logits = (rmsnorm(x) * g_f) W_lm.
 * The KV cache here is an array with room for max_ctx positions plus a
   committed length; entries past the committed length are dead and never

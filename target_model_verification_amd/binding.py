@@ -33,7 +33,7 @@ class SpecConfig(ctypes.Structure):
                  "n_experts", "top_k", "n_shared", "d_ff_expert", "weight_dtype", "kv_dtype")] + \
                [("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("max_ctx", ctypes.c_int32), ("max_k", ctypes.c_int32), ("gemm_k_split", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 7)]
+                ("kv_page_seed", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6)]
 
 
 class SpecTensor(ctypes.Structure):
@@ -66,7 +66,7 @@ def _load():
         "spec_verify_step": (I, [P, ctypes.POINTER(ctypes.c_int32), I, I, P, P,
                                  ctypes.POINTER(SpecStepResult), P]),
         "spec_verify_step_debug": (I, [P, ctypes.POINTER(ctypes.c_int32), I, I, P, P,
-                                       ctypes.POINTER(SpecStepResult), P, P, P]),
+                                       ctypes.POINTER(SpecStepResult), P, P, P, P]),
         "spec_kv_commit_rollback": (I, [P, I]),
         "spec_kv_len": (I, [P]),
         "spec_last_error": (ctypes.c_char_p, [P]),
@@ -76,6 +76,7 @@ def _load():
         "spec_profile_detail": (I, [P, ctypes.POINTER(D)]),
         "spec_profile_raw": (I, [P, ctypes.POINTER(ctypes.c_uint64), ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
         "spec_pass_bytes": (D, [P, I, I, I, ctypes.c_int64]),
+        "spec_kv_poison_dead": (I, [P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -101,6 +102,7 @@ spec_profile_read = lib.spec_profile_read
 spec_profile_detail = lib.spec_profile_detail
 spec_profile_raw = lib.spec_profile_raw
 spec_pass_bytes = lib.spec_pass_bytes
+spec_kv_poison_dead = lib.spec_kv_poison_dead
 
 
 class SpecError(RuntimeError):
@@ -112,7 +114,7 @@ class SpecError(RuntimeError):
 _DT = {"f32": SPEC_DT_F32, "bf16": SPEC_DT_BF16, "int4g128": SPEC_DT_INT4G128}
 
 
-def make_config(spec, max_ctx: int, max_k: int, gemm_k_split: int = 0) -> SpecConfig:
+def make_config(spec, max_ctx: int, max_k: int, gemm_k_split: int = 0, kv_page_seed: int = 0) -> SpecConfig:
     c = SpecConfig()
     c.n_layers, c.d_model = spec.n_layers, spec.d_model
     c.n_q_heads, c.n_kv_heads, c.head_dim = spec.n_q_heads, spec.n_kv_heads, spec.head_dim
@@ -121,6 +123,7 @@ def make_config(spec, max_ctx: int, max_k: int, gemm_k_split: int = 0) -> SpecCo
     c.weight_dtype, c.kv_dtype = _DT[spec.weight_dtype], _DT[spec.kv_dtype]
     c.rope_theta, c.rms_eps = spec.rope_theta, spec.rms_eps
     c.max_ctx, c.max_k, c.gemm_k_split = max_ctx, max_k, gemm_k_split
+    c.kv_page_seed = kv_page_seed
     return c
 
 
@@ -169,9 +172,10 @@ class Verifier:
     """Owns one spec_verify_t handle."""
 
     def __init__(self, spec, W, prompt_k: Optional[np.ndarray], prompt_v: Optional[np.ndarray],
-                 prompt_len: int, max_ctx: int, max_k: int, stream: int = 0, gemm_k_split: int = 0):
+                 prompt_len: int, max_ctx: int, max_k: int, stream: int = 0, gemm_k_split: int = 0,
+                 kv_page_seed: int = 0):
         self.spec = spec
-        self.cfg = make_config(spec, max_ctx, max_k, gemm_k_split)
+        self.cfg = make_config(spec, max_ctx, max_k, gemm_k_split, kv_page_seed)
         tens, keep = make_tensors(W)
         pk = pv = None
         if prompt_len > 0:
@@ -188,14 +192,15 @@ class Verifier:
         self.h = h
 
     def step(self, tokens: Sequence[int], mode: int = SPEC_ACCEPT_GREEDY, q_ptr: int = 0, u_ptr: int = 0,
-             logits_ptr: int = 0, trace_ptr: int = 0, union_ptr: int = 0) -> SpecStepResult:
+             logits_ptr: int = 0, trace_ptr: int = 0, union_ptr: int = 0, route_ptr: int = 0) -> SpecStepResult:
         t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
         k = len(t) - 1
         res = SpecStepResult()
         tp = t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
-        if trace_ptr or union_ptr:
+        if trace_ptr or union_ptr or route_ptr:
             rc = spec_verify_step_debug(self.h, tp, k, mode, q_ptr or None, u_ptr or None, ctypes.byref(res),
-                                        logits_ptr or None, trace_ptr or None, union_ptr or None)
+                                        logits_ptr or None, trace_ptr or None, union_ptr or None,
+                                        route_ptr or None)
         else:
             rc = spec_verify_step(self.h, tp, k, mode, q_ptr or None, u_ptr or None, ctypes.byref(res),
                                   logits_ptr or None)
@@ -215,8 +220,16 @@ class Verifier:
     def last_error(self) -> str:
         return spec_last_error(self.h).decode(errors="replace")
 
-    def profile(self, on: bool) -> None:
-        spec_profile_enable(self.h, 1 if on else 0)
+    def profile(self, on) -> None:
+        """on: False/0 off, True/1 events + per-phase stamps, 2 events only."""
+        rc = spec_profile_enable(self.h, int(on))
+        if rc != SPEC_OK:
+            raise SpecError(rc, self.last_error())
+
+    def poison_dead(self) -> None:
+        rc = spec_kv_poison_dead(self.h)
+        if rc != SPEC_OK:
+            raise SpecError(rc, self.last_error())
 
     def profile_read(self):
         n = (ctypes.c_int64 * SPEC_K_NCLASSES)()

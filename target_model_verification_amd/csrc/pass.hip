@@ -1710,6 +1710,8 @@ __device__ __forceinline__ void route_block(const PassP& P, const float* bias, u
       cst(rec, C->uc);
       if (P.union_hist) P.union_hist[layer] = C->uc;
     }
+    if (P.route_hist)
+      for (int i = tid; i < P.m * K; i += kThreads) P.route_hist[(long long)layer * P.m * K + i] = sel[i];
     for (int e = tid; e < E; e += kThreads) {
       cst(rec + 1 + e, e < C->uc ? C->ulist[e] : -1);
       int s = -1;

@@ -150,4 +150,40 @@ hipError_t launch_kv_import(int kv_f32, const void* src, int P, int Hkv, int D, 
   return hipGetLastError();
 }
 
+// Every cache element at logical positions [from, to) of every layer and
+// KV head set to NaN (debugging aid: dead entries must never be read).
+template <typename T>
+__global__ void k_kv_poison(T* __restrict__ base, long long layer_elems, int n_layers, int Hkv, int D,
+                            const int* __restrict__ pt, int from, int to, T nan) {
+  const long long per_layer = 2LL * Hkv * (long long)(to - from) * D;
+  const long long total = per_layer * n_layers;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < total;
+       i += (long long)gridDim.x * blockDim.x) {
+    const int l = (int)(i / per_layer);
+    long long r = i - (long long)l * per_layer;
+    const int d = (int)(r % D);
+    r /= D;
+    const int t = from + (int)(r % (to - from));
+    r /= (to - from);
+    const int g = (int)(r % Hkv);
+    const int sel = (int)(r / Hkv);
+    const long long blk = (((long long)pt[t / kPage] * Hkv + g) * 2 + sel) * kPage * D;
+    base[(long long)l * layer_elems + blk + (sel == 0 ? (long long)(t % kPage) * D + d : (long long)d * kPage + (t % kPage))] =
+        nan;
+  }
+}
+
+hipError_t launch_kv_poison(int kv_f32, void* base, long long layer_elems, int n_layers, int Hkv, int D,
+                            const int* pt, int from, int to, hipStream_t s) {
+  if (to <= from) return hipSuccess;
+  const long long total = 2LL * Hkv * (long long)(to - from) * D * n_layers;
+  if (kv_f32)
+    hipLaunchKernelGGL(k_kv_poison<float>, grid_for(total), dim3(256), 0, s, static_cast<float*>(base), layer_elems,
+                       n_layers, Hkv, D, pt, from, to, __builtin_nanf(""));
+  else
+    hipLaunchKernelGGL(k_kv_poison<uint16_t>, grid_for(total), dim3(256), 0, s, static_cast<uint16_t*>(base),
+                       layer_elems, n_layers, Hkv, D, pt, from, to, (uint16_t)0x7FC0u);
+  return hipGetLastError();
+}
+
 }  // namespace sv

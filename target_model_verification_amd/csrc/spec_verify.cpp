@@ -98,7 +98,8 @@ struct spec_verify {
   int kv_len = 0;
   bool broken = false;
   std::string err;
-  // profiling
+  // profiling (0 off, 1 events + per-phase stamps, 2 events only)
+  int prof_mode = 0;
   bool profiling = false;
   hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
   unsigned long long* stamps_dev = nullptr;
@@ -185,7 +186,7 @@ bool check_cfg(const spec_config* c, std::string& msg) {
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return bad("rope_theta must be > 0 and rms_eps >= 0");
   if (c->gemm_k_split < 0 || c->gemm_k_split % 128 != 0 || c->gemm_k_split > 2048)
     return bad("gemm_k_split must be a multiple of 128 in [0, 2048]");
-  for (int i = 0; i < 7; ++i)
+  for (int i = 0; i < 6; ++i)
     if (c->reserved[i] != 0) return bad("reserved fields must be zero");
   const bool moe = c->n_experts > 0;
   if (moe) {
@@ -556,7 +557,7 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   if ((rc = up.alloc_mat(h->lm_head, plan.lm_head))) return rc;
   if ((rc = up.put(h->lm_head, SPEC_T_LM_HEAD, -1, -1, d, V, 0, 1, 0))) return rc;
 
-  // KV cache pages + identity page table
+  // KV cache pages and the page table (identity, or a seeded permutation)
   h->n_pages = cdiv(c.max_ctx, kPage);
   h->kv_layer_elems = (long long)h->n_pages * Hkv * 2 * kPage * D;
   if ((rc = dalloc_z(h, reinterpret_cast<char**>(&h->kv), (size_t)h->kv_layer_elems * c.n_layers * kv_elem)))
@@ -566,6 +567,17 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   {
     std::vector<int> pt(h->n_pages);
     for (int i = 0; i < h->n_pages; ++i) pt[i] = i;
+    if (c.kv_page_seed != 0) {
+      // Fisher-Yates with a splitmix64 stream seeded by kv_page_seed
+      unsigned long long st = (unsigned long long)(unsigned)c.kv_page_seed;
+      auto next = [&st]() {
+        unsigned long long z = (st += 0x9E3779B97F4A7C15ull);
+        z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+        z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+        return z ^ (z >> 31);
+      };
+      for (int i = h->n_pages - 1; i > 0; --i) std::swap(pt[i], pt[(int)(next() % (unsigned long long)(i + 1))]);
+    }
     if ((rc = dalloc_t(h, &h->page_table, h->n_pages))) return rc;
     HIPCHK(hipMemcpy(h->page_table, pt.data(), sizeof(int) * h->n_pages, hipMemcpyHostToDevice));
   }
@@ -757,6 +769,7 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   if ((rc = dalloc_z(h, &h->stamps_dev, (size_t)h->n_prog + 4))) return rc;
   h->stamps_host.assign((size_t)h->n_prog + 4, 0);
   if ((rc = dalloc_z(h, &h->wstamps_dev, (size_t)h->n_prog * h->n_wg * 4))) return rc;
+  if (moe && (rc = dalloc_z(h, &h->union_dev_prof, (size_t)c.n_layers))) return rc;
   h->wstamps_host.assign((size_t)h->n_prog * h->n_wg * 4, 0);
   for (auto& e : h->ev) HIPCHK(hipEventCreate(&e));
 
@@ -806,7 +819,7 @@ double phase_bytes(const spec_verify* h, int i, int m, int L, int experts_loaded
 
 int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, const float* q_dev,
               const float* u_dev, spec_step_result* out, float* logits_dev, float* trace_dev,
-              int32_t* union_dev) {
+              int32_t* union_dev, int32_t* route_dev) {
   if (!h) return SPEC_EINVAL;
   if (h->broken) return fail(h, SPEC_ESTATE, "handle unusable after an earlier GPU error");
   const spec_config& c = h->cfg;
@@ -822,15 +835,8 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   if ((long long)L + m > c.max_ctx) return fail(h, SPEC_ECAPACITY, "block exceeds max_ctx");
   const bool moe = c.n_experts > 0;
   int* union_rec = union_dev;
-  if (!union_rec && h->profiling && moe) {
-    if (!h->union_dev_prof) {
-      void* p = nullptr;
-      if (hipMalloc(&p, sizeof(int) * c.n_layers) != hipSuccess) return fail(h, SPEC_ENOMEM, "profiling buffer");
-      h->allocs.push_back(p);
-      h->union_dev_prof = static_cast<int*>(p);
-    }
-    union_rec = h->union_dev_prof;
-  }
+  if (!union_rec && h->profiling && moe) union_rec = h->union_dev_prof;   // allocated at create
+  const bool stamps = h->prof_mode == 1;
 
   std::memcpy(h->tokens_host, tokens, sizeof(int32_t) * m);
   hipError_t he = hipMemcpyAsync(h->tokens_dev, h->tokens_host, sizeof(int32_t) * m, hipMemcpyHostToDevice,
@@ -860,9 +866,9 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   p.rlog = h->rlog; p.ldr = h->ldr; p.ey = h->ey; p.ey_slot = h->ey_slot; p.ldy = h->ldx;
   p.route = h->route;
   p.bar = h->bar; p.bar_base = h->bar_gen; p.err = h->result_dev + 3;
-  p.trace = trace_dev; p.union_hist = union_rec;
-  p.stamps = h->profiling ? h->stamps_dev : nullptr;
-  p.wstamps = h->profiling ? h->wstamps_dev : nullptr;
+  p.trace = trace_dev; p.union_hist = union_rec; p.route_hist = moe ? route_dev : nullptr;
+  p.stamps = stamps ? h->stamps_dev : nullptr;
+  p.wstamps = stamps ? h->wstamps_dev : nullptr;
 
   if (he == hipSuccess && h->profiling) he = hipEventRecord(h->ev[0], h->stream);
   if (he == hipSuccess) he = launch_pass(h->wfmt, p, h->n_wg, h->lds, h->stream);
@@ -887,10 +893,10 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   if (he == hipSuccess && logits_dev)
     he = hipMemcpy2DAsync(logits_dev, (size_t)c.vocab * 4, h->logits, (size_t)h->ldl * 4, (size_t)c.vocab * 4, m,
                           hipMemcpyDeviceToDevice, h->stream);
-  if (he == hipSuccess && h->profiling)
+  if (he == hipSuccess && stamps)
     he = hipMemcpyAsync(h->stamps_host.data(), h->stamps_dev, sizeof(unsigned long long) * h->n_prog,
                         hipMemcpyDeviceToHost, h->stream);
-  if (he == hipSuccess && h->profiling)
+  if (he == hipSuccess && stamps)
     he = hipMemcpyAsync(h->wstamps_host.data(), h->wstamps_dev, sizeof(unsigned long long) * h->wstamps_host.size(),
                         hipMemcpyDeviceToHost, h->stream);
   std::vector<int> uh;
@@ -911,10 +917,12 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
     float pass_ms = 0.f, acc_ms = 0.f;
     (void)hipEventElapsedTime(&pass_ms, h->ev[0], h->ev[1]);
     (void)hipEventElapsedTime(&acc_ms, h->ev[1], h->ev[2]);
-    double total_bytes = 0;
+    long long experts_loaded = 0;
+    if (moe)
+      for (int l = 0; l < c.n_layers; ++l) experts_loaded += uh[l];
     const double tick_ms = 1.0 / h->wall_khz;
     double stamped = 0;
-    for (int i = 0; i < h->n_prog; ++i) {
+    for (int i = 0; i < h->n_prog && stamps; ++i) {
       double ms;
       if (i + 1 < h->n_prog) {
         ms = (double)(h->stamps_host[i + 1] - h->stamps_host[i]) * tick_ms;
@@ -952,11 +960,10 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
       h->prof_launches[k2] += 1;
       h->prof_ms[k2] += ms;
       h->prof_bytes[k2] += b;
-      total_bytes += b;
     }
     h->prof_launches[SPEC_K_PASS] += 1;
     h->prof_ms[SPEC_K_PASS] += pass_ms;
-    h->prof_bytes[SPEC_K_PASS] += total_bytes;
+    h->prof_bytes[SPEC_K_PASS] += spec_pass_bytes(h, L, k, mode, experts_loaded);
     h->prof_launches[SPEC_K_ACCEPT] += 1;
     h->prof_ms[SPEC_K_ACCEPT] += acc_ms;
     h->prof_bytes[SPEC_K_ACCEPT] +=
@@ -1028,13 +1035,13 @@ int spec_verify_create(const spec_config* cfg, const spec_tensor* tensors, int32
 
 int spec_verify_step(spec_verify_t* h, const int32_t* tokens, int32_t k, int32_t mode, const float* q_dev,
                      const float* u_dev, spec_step_result* out, float* logits_dev) {
-  return step_impl(h, tokens, k, mode, q_dev, u_dev, out, logits_dev, nullptr, nullptr);
+  return step_impl(h, tokens, k, mode, q_dev, u_dev, out, logits_dev, nullptr, nullptr, nullptr);
 }
 
 int spec_verify_step_debug(spec_verify_t* h, const int32_t* tokens, int32_t k, int32_t mode,
                            const float* q_dev, const float* u_dev, spec_step_result* out, float* logits_dev,
-                           float* trace_dev, int32_t* union_dev) {
-  return step_impl(h, tokens, k, mode, q_dev, u_dev, out, logits_dev, trace_dev, union_dev);
+                           float* trace_dev, int32_t* union_dev, int32_t* route_dev) {
+  return step_impl(h, tokens, k, mode, q_dev, u_dev, out, logits_dev, trace_dev, union_dev, route_dev);
 }
 
 int spec_kv_commit_rollback(spec_verify_t* h, int32_t new_kv_len) {
@@ -1049,6 +1056,17 @@ int spec_kv_commit_rollback(spec_verify_t* h, int32_t new_kv_len) {
 
 int32_t spec_kv_len(const spec_verify_t* h) { return h ? h->kv_len : -1; }
 
+int spec_kv_poison_dead(spec_verify_t* h) {
+  if (!h) return SPEC_EINVAL;
+  if (h->broken) return fail(h, SPEC_ESTATE, "handle unusable after an earlier GPU error");
+  const spec_config& c = h->cfg;
+  HIPCHK(launch_kv_poison(c.kv_dtype == SPEC_DT_F32, h->kv, h->kv_layer_elems, c.n_layers, c.n_kv_heads,
+                          c.head_dim, h->page_table, h->kv_len, c.max_ctx, h->stream));
+  HIPCHK(hipStreamSynchronize(h->stream));
+  h->err.clear();
+  return SPEC_OK;
+}
+
 const char* spec_last_error(const spec_verify_t* h) { return h ? h->err.c_str() : kNullMsg; }
 
 void spec_verify_destroy(spec_verify_t* h) {
@@ -1059,6 +1077,8 @@ void spec_verify_destroy(spec_verify_t* h) {
 
 int spec_profile_enable(spec_verify_t* h, int32_t on) {
   if (!h) return SPEC_EINVAL;
+  if (on < 0 || on > 2) return fail(h, SPEC_EINVAL, "profiling mode must be 0, 1 or 2");
+  h->prof_mode = on;
   h->profiling = on != 0;
   for (int i = 0; i < SPEC_K_NCLASSES; ++i) {
     h->prof_launches[i] = 0;

@@ -131,6 +131,7 @@ struct PassP {
   // debug / profiling (nullable)
   float* trace;              // [n_layers][m][d]
   int* union_hist;           // [n_layers]
+  int* route_hist;           // [n_layers][m][top_k] experts selected by each row, in rank order
   unsigned long long* stamps;   // [n_phases + 1] wall clock at phase ends (workgroup 0)
   unsigned long long* wstamps;  // [n_phases][n_wg][4] per-workgroup phase stamps (nullable)
 };
@@ -164,5 +165,7 @@ hipError_t launch_retile(int wfmt, const void* src, const void* src_scales, int 
                          void* dst2, int nkc, int tpu, int tile_off, int tile_stride, int pair_dim, hipStream_t s);
 hipError_t launch_kv_import(int kv_f32, const void* src, int P, int Hkv, int D, void* layer_base,
                             const int* page_table, hipStream_t s);
+hipError_t launch_kv_poison(int kv_f32, void* base, long long layer_elems, int n_layers, int Hkv, int D,
+                            const int* page_table, int from, int to, hipStream_t s);
 
 }  // namespace sv

@@ -2,12 +2,15 @@
 seeded inputs as the oracle and compares element by element."""
 from __future__ import annotations
 
+import json
+import os
 import sys
 from typing import Optional
 
 import numpy as np
 import torch
 
+from oracle import accept as oacc
 from oracle import model as om
 from spec_harness import (PreparedWorkload, RoundInputs, greedy_round_inputs, kv_to_host_arrays,
                           oracle_step, stochastic_round_inputs)
@@ -64,17 +67,47 @@ def layer_errors(pw: PreparedWorkload, h: B.Verifier, kv: om.KVCache, ri: RoundI
     return errs
 
 
+ACC_TOL = 1e-5   # fp32 (device) against fp64 (oracle) acceptance arithmetic on the same logits
+
+
+def record(entry: dict) -> None:
+    """Appends one JSON line of parity statistics to the file named by the
+    SPEC_PARITY_RECORD environment variable (if set)."""
+    path = os.environ.get("SPEC_PARITY_RECORD")
+    if not path:
+        return
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "a") as f:
+        f.write(json.dumps(entry, sort_keys=True) + "\n")
+
+
+def _valid(res, L: int, k: int, V: int) -> bool:
+    return 0 <= res.n_accepted <= k and 0 <= res.next_token < V and res.kv_len == L + 1 + res.n_accepted
+
+
 def run_parity_rounds(pw: PreparedWorkload, h: B.Verifier, k: int, rounds: int, mode: str,
-                      greedy_ref: Optional[np.ndarray] = None, c=None):
-    """Runs `rounds` verification steps on both sides from the same state and
-    checks: logits within tolerance; n_accepted / next / kv_len identical
-    unless the oracle flags a near-tie (then both resync to the oracle)."""
+                      greedy_ref: Optional[np.ndarray] = None, c=None, tag: str = ""):
+    """Runs `rounds` verification steps on both sides from the same state.
+
+    Every round checks:
+      - logits against the oracle's, element by element, within the logit
+        tolerance (1e-4 fp32, 2e-2 bf16 / int4);
+      - the GPU's (n_accepted, next, kv_len) against the acceptance rule
+        applied to the GPU's own logits (oracle.accept_*): greedy exactly,
+        stochastic exactly unless a decision lies within a relative 1e-5 of
+        flipping (fp32 on the device against fp64), then only validity;
+      - the GPU's outcome against the oracle's: identical unless the oracle
+        flags a near-tie at the logit tolerance (top-2 gap of a deciding row,
+        |u q - p| of a test, the margin of a draw); after a flagged
+        divergence both sides resync to the oracle's outcome.
+    Returns the statistics (also appended to SPEC_PARITY_RECORD)."""
     spec = pw.wl.spec
     tol = logit_tol(spec)
     kv = pw.kv0.copy()
     pending = pw.pending0
     s = 0
-    st = dict(max_err=0.0, flagged=0, flagged_mismatch=0, accepted=0, rounds=0)
+    st = dict(max_err=0.0, flagged=0, flagged_mismatch=0, self_flagged=0, self_flagged_mismatch=0,
+              accepted=0, rounds=0, tie_where={})
     for r in range(rounds):
         L = kv.length
         assert h.kv_len == L
@@ -93,9 +126,27 @@ def run_parity_rounds(pw: PreparedWorkload, h: B.Verifier, k: int, rounds: int, 
             raise AssertionError(f"{spec.name} round {r}: logits max err {err:.3e} > {tol}; "
                                  f"per-layer residual errors {['%.2e' % e for e in errs]}")
         got = (res_g.n_accepted, res_g.next_token, res_g.kv_len)
+        # the acceptance rule on the GPU's own logits
+        if mode == "greedy":
+            own = oacc.accept_greedy(lg, ri.tokens[1:], L, 0.0)
+            assert got == (own.n_accepted, own.next_token, own.kv_len), \
+                f"{spec.name} round {r}: GPU {got} != greedy rule on its own logits {own}"
+        else:
+            own = oacc.accept_stochastic(lg, ri.q, ri.tokens[1:], ri.u, L, ACC_TOL)
+            if own.near_tie:
+                st["self_flagged"] += 1
+            if got != (own.n_accepted, own.next_token, own.kv_len):
+                assert own.near_tie, \
+                    f"{spec.name} round {r}: GPU {got} != stochastic rule on its own logits {own} (no flag)"
+                assert _valid(res_g, L, k, spec.vocab)
+                st["self_flagged_mismatch"] += 1
+        # against the oracle's outcome
         want = (out_o.n_accepted, out_o.next_token, out_o.kv_len)
         if out_o.near_tie:
             st["flagged"] += 1
+            for w in out_o.tie_where:
+                key = w if not w.startswith("row") else "row"
+                st["tie_where"][key] = st["tie_where"].get(key, 0) + 1
         if got != want:
             assert out_o.near_tie, f"{spec.name} round {r}: GPU {got} != oracle {want} (no near-tie)"
             st["flagged_mismatch"] += 1
@@ -106,4 +157,5 @@ def run_parity_rounds(pw: PreparedWorkload, h: B.Verifier, k: int, rounds: int, 
         st["rounds"] += 1
         pending = out_o.next_token
         s += out_o.n_accepted + 1
+    record(dict(workload=spec.name, k=k, mode=mode, tag=tag, tol=tol, **st))
     return st

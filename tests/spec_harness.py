@@ -32,9 +32,11 @@ class PreparedWorkload:
 
 
 def prepare(wl: synth.Workload, dtype=np.float64, prefill_dtype=None, max_ctx=None,
-            context: Optional[int] = None) -> PreparedWorkload:
+            context: Optional[int] = None, weights: Optional[dict] = None) -> PreparedWorkload:
+    """Weights of the workload (or the given ones), the oracle model, the
+    prompt prefilled by the oracle and the first pending token."""
     spec = wl.spec
-    W = synth.make_weights(spec, wl.seed)
+    W = synth.make_weights(spec, wl.seed) if weights is None else weights
     prompt = synth.prompt_ids(wl, context)
     max_ctx = max_ctx or (len(prompt) + wl.rounds * 17 + 64)
     if prefill_dtype is not None and prefill_dtype != dtype:

@@ -5,7 +5,8 @@ Speculative Decoding", "The four sentences are already inside one
 sentence"), runs are bitwise repeatable, speculative rounds on the GPU emit
 the GPU's own greedy decode ("The output does not change"), rollback leaves
 no trace (step 5 of "The loop"), and bad calls leave the handle's state
-unchanged.
+unchanged, dead cache entries are never read (NaN-filled), and the page
+indirection is transparent (a permuted page table).
 
 Dense models: nesting and spec == autoregressive hold bitwise (every
 phase's work split is independent of the block's row count).  MoE models:
@@ -22,7 +23,7 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 from gpu_common import log, make_verifier  # noqa: E402
-from spec_harness import prepare  # noqa: E402
+from spec_harness import kv_to_host_arrays, prepare  # noqa: E402
 from target_model_verification_amd import binding as B  # noqa: E402
 from target_model_verification_amd import synth  # noqa: E402
 
@@ -125,6 +126,51 @@ def test_rollback_leaves_no_trace(verifier):
     _, again = _logits(h, toks)
     h.rollback(L)
     assert np.array_equal(ref, again)
+
+
+def test_dead_entries_never_read(verifier):
+    """Entries past the committed length are dead (essay "The loop", step 5):
+    after a step that rejects part of its block, filling every dead cache
+    entry with NaN must not change the next step's logits by a single bit."""
+    pw, h = verifier
+    L = h.kv_len
+    a = [pw.pending0, 11, 12, 13, 14, 15, 16]
+    r1 = h.step(a, B.SPEC_ACCEPT_GREEDY)
+    b = [r1.next_token, 21, 22, 23, 24]
+    _, ref = _logits(h, b)
+    h.rollback(L)
+    r2 = h.step(a, B.SPEC_ACCEPT_GREEDY)
+    assert (r1.n_accepted, r1.next_token, r1.kv_len) == (r2.n_accepted, r2.next_token, r2.kv_len)
+    h.poison_dead()
+    _, got = _logits(h, b)
+    h.rollback(L)
+    assert np.all(np.isfinite(got))
+    assert np.array_equal(ref, got)
+
+
+def test_permuted_page_table():
+    """The cache is paged (64 positions per page) through a page table: a
+    handle whose logical pages map to a seeded permutation of the physical
+    pages (prompt import, appends and attention all go through the table)
+    gives bitwise the same logits and outcomes as the identity table."""
+    pw = prepare(synth.ALL_WORKLOADS["small_gqa"])
+    hi = make_verifier(pw, max_k=15)
+    K, V = kv_to_host_arrays(pw)
+    hp = B.Verifier(pw.wl.spec, pw.W, K, V, pw.kv0.length, pw.max_ctx, 15,
+                    torch.cuda.current_stream().cuda_stream, 0, kv_page_seed=12345)
+    try:
+        tok = pw.pending0
+        for r in range(6):
+            toks = [tok] + [int(t) for t in synth.prompt_ids(pw.wl, 40 + 8 * r)[-8:]]
+            ri, li = _logits(hi, toks)
+            rp, lp = _logits(hp, toks)
+            assert np.array_equal(li, lp)
+            assert (ri.n_accepted, ri.next_token, ri.kv_len) == (rp.n_accepted, rp.next_token, rp.kv_len)
+            tok = ri.next_token
+        log(f"[invariants] permuted page table: 6 steps bitwise equal, kv_len {hi.kv_len}")
+    finally:
+        hi.close()
+        hp.close()
 
 
 def test_bad_calls_leave_state_unchanged(verifier):

@@ -111,3 +111,19 @@ def test_noisy_target_drafts(verifier):
         q = onx.softmax(z[:K] + g.standard_normal((K, V)), axis=-1).astype(np.float32)
         u = g.uniform(0.0, 1.0, K + 1)
         _check(pw, h, toks, q, u)
+
+
+def test_zero_residual_draws_from_p(verifier):
+    """q >= p at every id (q_i = 1.5 p_{i-1}, rows summing to 1.5) and u_1
+    close to 1: d_1 is rejected (u_1 q > p) and max(0, p - q) is zero
+    everywhere, so the resample falls back to p_0 itself (the degenerate
+    residual case)."""
+    pw, h = verifier
+    for seed in range(3):
+        toks = _tokens(pw, 30 + seed)
+        p = onx.softmax(_block_logits(h, toks), axis=-1)
+        q = (1.5 * p[:K]).astype(np.float32)
+        u = np.random.default_rng([pw.wl.seed, 89, seed]).uniform(0.0, 1.0, K + 1)
+        u[0] = 0.999
+        res = _check(pw, h, toks, q, u)
+        assert res.n_accepted == 0
