@@ -172,6 +172,21 @@ int spec_verify_step(spec_verify_t* h, const int32_t* tokens, int32_t k, int32_t
                      const float* q_dev, const float* u_dev, spec_step_result* out,
                      float* logits_dev);
 
+/* For callers that cannot allocate device memory while stepping (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same step as spec_verify_step, with the same arguments and results,
+ * and it allocates nothing.  The pass kernel's split-K partial tiles and
+ * their arrival tickets go to a fixed device scratch array of the library
+ * (64 MiB, reserved on every device the library runs on until the process
+ * ends) instead of the handle's workspace; the tickets are cleared by a
+ * small kernel on the handle's stream before the pass.  SPEC_ECAPACITY if
+ * this model's workspace (two banks of partials plus tickets) exceeds the
+ * scratch.  All calls on one device share that device's scratch: calls
+ * that overlap in time on one device (several handles or streams) race. */
+int spec_verify_step_noalloc(spec_verify_t* h, const int32_t* tokens, int32_t k, int32_t mode,
+                             const float* q_dev, const float* u_dev, spec_step_result* out,
+                             float* logits_dev);
+
 /* Truncates the committed cache to new_kv_len (0 <= new_kv_len <= kv_len):
  * entries at or beyond it become dead and are overwritten by later blocks.
  * Metadata only; no device work. */

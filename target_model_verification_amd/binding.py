@@ -77,6 +77,8 @@ def _load():
         "spec_profile_raw": (I, [P, ctypes.POINTER(ctypes.c_uint64), ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
         "spec_pass_bytes": (D, [P, I, I, I, ctypes.c_int64]),
         "spec_kv_poison_dead": (I, [P]),
+        "spec_verify_step_noalloc": (I, [P, ctypes.POINTER(ctypes.c_int32), I, I, P, P,
+                                         ctypes.POINTER(SpecStepResult), P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -103,6 +105,7 @@ spec_profile_detail = lib.spec_profile_detail
 spec_profile_raw = lib.spec_profile_raw
 spec_pass_bytes = lib.spec_pass_bytes
 spec_kv_poison_dead = lib.spec_kv_poison_dead
+spec_verify_step_noalloc = lib.spec_verify_step_noalloc
 
 
 class SpecError(RuntimeError):
@@ -192,12 +195,16 @@ class Verifier:
         self.h = h
 
     def step(self, tokens: Sequence[int], mode: int = SPEC_ACCEPT_GREEDY, q_ptr: int = 0, u_ptr: int = 0,
-             logits_ptr: int = 0, trace_ptr: int = 0, union_ptr: int = 0, route_ptr: int = 0) -> SpecStepResult:
+             logits_ptr: int = 0, trace_ptr: int = 0, union_ptr: int = 0, route_ptr: int = 0,
+             noalloc: bool = False) -> SpecStepResult:
         t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
         k = len(t) - 1
         res = SpecStepResult()
         tp = t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
-        if trace_ptr or union_ptr or route_ptr:
+        if noalloc:
+            rc = spec_verify_step_noalloc(self.h, tp, k, mode, q_ptr or None, u_ptr or None, ctypes.byref(res),
+                                          logits_ptr or None)
+        elif trace_ptr or union_ptr or route_ptr:
             rc = spec_verify_step_debug(self.h, tp, k, mode, q_ptr or None, u_ptr or None, ctypes.byref(res),
                                         logits_ptr or None, trace_ptr or None, union_ptr or None,
                                         route_ptr or None)

@@ -14,7 +14,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspecverify.so")
-SOURCES = ["pass.hip", "retile.hip", "misc.hip", "plan_check.cpp", "spec_verify.cpp"]
+SOURCES = ["pass.hip", "retile.hip", "misc.hip", "noalloc.hip", "plan_check.cpp", "spec_verify.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # packed fp32 VALU forms are disabled for all device code
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -1792,7 +1792,8 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
     io.trace = (d->trace && P.trace) ? P.trace + (long long)d->layer * P.m * P.d : nullptr;
     io.ready = P.ready + (long long)max(d->layer, 0) * kReadyStride;
     io.ss_in = d->ss_in; io.ss_out = d->ss_out;
-    io.ws = d->ws; io.tickets = d->tickets;
+    io.ws = P.ws_alt ? P.ws_alt + (long long)d->ws_bank * P.ws_bank_floats : d->ws;
+    io.tickets = P.tickets_alt ? P.tickets_alt + (long long)d->ws_bank * P.tickets_bank : d->tickets;
     io.dep = d->dep;
     io.notify = d->notify;
     // the O projection waits on merged heads only when attention merges

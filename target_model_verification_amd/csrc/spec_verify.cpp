@@ -74,6 +74,9 @@ struct spec_verify {
   int* route = nullptr;
   float* ws = nullptr;
   unsigned* tickets = nullptr;
+  size_t ws_bank_floats = 0, tickets_bank = 0;   // per split-K bank
+  void* scratch = nullptr;      // the fixed device scratch of this device (no-alloc steps)
+  bool scratch_fits = false;    // both split-K banks and their tickets fit in it
   unsigned* attn_tickets = nullptr;
   unsigned long long* bar = nullptr;
   unsigned long long bar_gen = 0;
@@ -106,6 +109,7 @@ struct spec_verify {
   std::vector<unsigned long long> stamps_host;
   unsigned long long* wstamps_dev = nullptr;    // [n_prog][n_wg][4]
   std::vector<unsigned long long> wstamps_host;
+  std::vector<int> union_host;                  // MoE: union sizes of the last profiled step
   double prof_detail[SPEC_K_NCLASSES][8] = {};
   int* union_dev_prof = nullptr;
   int64_t prof_launches[SPEC_K_NCLASSES] = {};
@@ -151,12 +155,15 @@ int dalloc_t(spec_verify* h, T** p, size_t count) {
   return rc;
 }
 
-// zero-filled allocation
+// zero-filled allocation (at least 16 bytes, all of them zeroed)
 template <typename T>
 int dalloc_z(spec_verify* h, T** p, size_t count) {
-  int rc = dalloc_t(h, p, count);
+  const size_t bytes = std::max<size_t>(count * sizeof(T), 16);
+  void* q = nullptr;
+  int rc = dalloc(h, &q, bytes);
+  *p = static_cast<T*>(q);
   if (rc) return rc;
-  hipError_t e = hipMemsetAsync(*p, 0, std::max<size_t>(count * sizeof(T), 16), h->stream);
+  hipError_t e = hipMemsetAsync(*p, 0, bytes, h->stream);
   if (e != hipSuccess) return fail(h, SPEC_EHIP, std::string("memset: ") + hipGetErrorString(e));
   return SPEC_OK;
 }
@@ -649,6 +656,12 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   // predecessor's reductions still run)
   if ((rc = dalloc_z(h, &h->ws, 2 * plan.ws_floats))) return rc;
   if ((rc = dalloc_z(h, &h->tickets, 2 * plan.n_tickets))) return rc;
+  h->ws_bank_floats = plan.ws_floats;
+  h->tickets_bank = plan.n_tickets;
+  // the fixed scratch that spec_verify_step_noalloc uses in place of ws and
+  // tickets: two banks of partials, then two banks of tickets
+  if (scratch_setup(h->device, &h->scratch) != hipSuccess) h->scratch = nullptr;   // no-alloc steps then refuse
+  h->scratch_fits = (2 * plan.ws_floats * 4 + 255) / 256 * 256 + 2 * plan.n_tickets * 4 <= kScratchBytes;
   if ((rc = dalloc_z(h, &h->attn_tickets, (size_t)Hkv + 16))) return rc;
   if ((rc = dalloc_z(h, &h->bar, 512))) return rc;
   if ((rc = dalloc_z(h, &h->tokens_dev, 16))) return rc;
@@ -741,6 +754,7 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
     const int bank = ng++ & 1;
     prog[i].ws = h->ws + (size_t)bank * plan.ws_floats;
     prog[i].tickets = h->tickets + (size_t)bank * plan.n_tickets;
+    prog[i].ws_bank = bank;
   }
   // grid barriers per pass (every phase but the first, except those fed by
   // ready counters and, with the inline merge, the merge phases)
@@ -770,6 +784,7 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   h->stamps_host.assign((size_t)h->n_prog + 4, 0);
   if ((rc = dalloc_z(h, &h->wstamps_dev, (size_t)h->n_prog * h->n_wg * 4))) return rc;
   if (moe && (rc = dalloc_z(h, &h->union_dev_prof, (size_t)c.n_layers))) return rc;
+  h->union_host.assign((size_t)std::max(c.n_layers, 1), 0);
   h->wstamps_host.assign((size_t)h->n_prog * h->n_wg * 4, 0);
   for (auto& e : h->ev) HIPCHK(hipEventCreate(&e));
 
@@ -819,7 +834,7 @@ double phase_bytes(const spec_verify* h, int i, int m, int L, int experts_loaded
 
 int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, const float* q_dev,
               const float* u_dev, spec_step_result* out, float* logits_dev, float* trace_dev,
-              int32_t* union_dev, int32_t* route_dev) {
+              int32_t* union_dev, int32_t* route_dev, bool noalloc = false) {
   if (!h) return SPEC_EINVAL;
   if (h->broken) return fail(h, SPEC_ESTATE, "handle unusable after an earlier GPU error");
   const spec_config& c = h->cfg;
@@ -833,6 +848,9 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   const int m = k + 1;
   const int L = h->kv_len;
   if ((long long)L + m > c.max_ctx) return fail(h, SPEC_ECAPACITY, "block exceeds max_ctx");
+  if (noalloc && (!h->scratch || !h->scratch_fits))
+    return fail(h, SPEC_ECAPACITY, "the split-K workspace of this model exceeds the fixed scratch (" +
+                                       std::to_string(kScratchBytes >> 20) + " MiB)");
   const bool moe = c.n_experts > 0;
   int* union_rec = union_dev;
   if (!union_rec && h->profiling && moe) union_rec = h->union_dev_prof;   // allocated at create
@@ -866,6 +884,15 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   p.rlog = h->rlog; p.ldr = h->ldr; p.ey = h->ey; p.ey_slot = h->ey_slot; p.ldy = h->ldx;
   p.route = h->route;
   p.bar = h->bar; p.bar_base = h->bar_gen; p.err = h->result_dev + 3;
+  if (noalloc) {
+    // partials in the fixed scratch; its tickets start at zero
+    p.ws_alt = static_cast<float*>(h->scratch);
+    p.ws_bank_floats = (long long)h->ws_bank_floats;
+    p.tickets_alt = reinterpret_cast<unsigned*>(static_cast<char*>(h->scratch) +
+                                                (2 * h->ws_bank_floats * 4 + 255) / 256 * 256);
+    p.tickets_bank = (long long)h->tickets_bank;
+    if (he == hipSuccess) he = launch_zero_u32(p.tickets_alt, 2 * (long long)h->tickets_bank, h->stream);
+  }
   p.trace = trace_dev; p.union_hist = union_rec; p.route_hist = moe ? route_dev : nullptr;
   p.stamps = stamps ? h->stamps_dev : nullptr;
   p.wstamps = stamps ? h->wstamps_dev : nullptr;
@@ -899,11 +926,9 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   if (he == hipSuccess && stamps)
     he = hipMemcpyAsync(h->wstamps_host.data(), h->wstamps_dev, sizeof(unsigned long long) * h->wstamps_host.size(),
                         hipMemcpyDeviceToHost, h->stream);
-  std::vector<int> uh;
-  if (he == hipSuccess && h->profiling && moe) {
-    uh.resize(c.n_layers);
+  std::vector<int>& uh = h->union_host;
+  if (he == hipSuccess && h->profiling && moe)
     he = hipMemcpyAsync(uh.data(), union_rec, sizeof(int) * c.n_layers, hipMemcpyDeviceToHost, h->stream);
-  }
   if (he == hipSuccess) he = hipStreamSynchronize(h->stream);
   if (he != hipSuccess) {
     h->broken = true;
@@ -1036,6 +1061,11 @@ int spec_verify_create(const spec_config* cfg, const spec_tensor* tensors, int32
 int spec_verify_step(spec_verify_t* h, const int32_t* tokens, int32_t k, int32_t mode, const float* q_dev,
                      const float* u_dev, spec_step_result* out, float* logits_dev) {
   return step_impl(h, tokens, k, mode, q_dev, u_dev, out, logits_dev, nullptr, nullptr, nullptr);
+}
+
+int spec_verify_step_noalloc(spec_verify_t* h, const int32_t* tokens, int32_t k, int32_t mode,
+                             const float* q_dev, const float* u_dev, spec_step_result* out, float* logits_dev) {
+  return step_impl(h, tokens, k, mode, q_dev, u_dev, out, logits_dev, nullptr, nullptr, nullptr, true);
 }
 
 int spec_verify_step_debug(spec_verify_t* h, const int32_t* tokens, int32_t k, int32_t mode,

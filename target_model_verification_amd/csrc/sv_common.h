@@ -89,6 +89,7 @@ struct Phase {
   float* ss_out;          // EMBED / RESID / COMBINE: partials of the next norm
   float* ws;              // split-K workspace bank (GEMM phases; a phase that may
   unsigned* tickets;      // overlap its predecessor's reductions uses the other bank)
+  int ws_bank;            // which of the two banks (0 / 1) ws and tickets are
 };
 // Ready counters per layer (64-bit, monotonic: pass e waits for e times the
 // expected count): KV heads' query / key / value blocks, and windows of the
@@ -125,6 +126,9 @@ struct PassP {
   int o_wcols;                // input columns per window of the O projection
   int qf_rt;                  // row tiles per KV head in the query fragments
   int attn_inline;           // 1: attention's last arrivers merge, the merge phase is skipped
+  // split-K banks replacing the program's own (null: use the program's):
+  // bank b at ws_alt + b * ws_bank_floats, tickets_alt + b * tickets_bank
+  float* ws_alt; unsigned* tickets_alt; long long ws_bank_floats, tickets_bank;
   // grid barrier
   unsigned long long* bar; unsigned long long bar_base;
   int* err;                  // set to 1 by a grid-barrier wait that ran out
@@ -161,6 +165,12 @@ hipError_t pass_occupancy(int wfmt, size_t lds, int* blocks_per_cu);
 // split units one workgroup may flush per phase (control-area capacity)
 constexpr int kMaxPending = 512;
 hipError_t launch_accept(const AcceptParams& p, hipStream_t s);
+// Fixed device scratch (file-scope array) for steps that allocate nothing:
+// its device address on `device` (which must be current); looked up once per
+// device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t scratch_setup(int device, void** out);
+hipError_t launch_zero_u32(unsigned* p, long long n, hipStream_t s);
 hipError_t launch_retile(int wfmt, const void* src, const void* src_scales, int K, int N, void* dst,
                          void* dst2, int nkc, int tpu, int tile_off, int tile_stride, int pair_dim, hipStream_t s);
 hipError_t launch_kv_import(int kv_f32, const void* src, int P, int Hkv, int D, void* layer_base,
