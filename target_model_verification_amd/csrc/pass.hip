@@ -148,6 +148,31 @@ __device__ __forceinline__ void afrag_put(uint4* a, int row, int col, float v) {
   cst16(base + (64 + ln) * 8 + e, (uint16_t)l);
 }
 
+// Eight consecutive elements (row, col .. col+7; col a multiple of 8) of an
+// A operand: one 16-byte word of the hi fragment and one of the lo fragment,
+// each stored through to the device-coherent level as two 64-bit stores.
+__device__ __forceinline__ void afrag_put8(uint4* a, int row, int col, const float (&v)[8]) {
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t h0 = f2bf(v[2 * e]), h1 = f2bf(v[2 * e + 1]);
+    const uint32_t l0 = f2bf(v[2 * e] - bf2f(h0)), l1 = f2bf(v[2 * e + 1] - bf2f(h1));
+    hw[e] = h0 | h1 << 16;
+    lw[e] = l0 | l1 << 16;
+  }
+  const int ch = col >> 5, ln = row + 16 * ((col & 31) >> 3);
+  unsigned long long* ph = reinterpret_cast<unsigned long long*>(a + (long long)ch * 128 + ln);
+  unsigned long long* pl = reinterpret_cast<unsigned long long*>(a + (long long)ch * 128 + 64 + ln);
+  __hip_atomic_store(glb(ph), (unsigned long long)hw[0] | (unsigned long long)hw[1] << 32, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(glb(ph + 1), (unsigned long long)hw[2] | (unsigned long long)hw[3] << 32, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(glb(pl), (unsigned long long)lw[0] | (unsigned long long)lw[1] << 32, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(glb(pl + 1), (unsigned long long)lw[2] | (unsigned long long)lw[3] << 32, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // raw workgroup barrier: execution only; the compiler may not move memory
 // operations across it
 __device__ __forceinline__ void raw_barrier() {
@@ -1085,12 +1110,22 @@ __device__ __forceinline__ void attn_merge_head(const PassP& P, uint4* a_o, int 
     Sr[r] = S;
   }
   __syncthreads();
-  for (int e = tid; e < R * D; e += kThreads) {
-    const int r = e / D, d = e - r * D;
-    float A = 0.f;
-    for (int c = 0; c < NG; ++c) A += fv[c * R + r] * pa[(c * R + r) * D + d];
+  // eight consecutive dims of one row per thread (one 16-byte word of each
+  // A fragment)
+  for (int e = tid; e < R * (D / 8); e += kThreads) {
+    const int r = e / (D / 8), d0 = (e - r * (D / 8)) * 8;
+    float A[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NG; ++c) {
+      const float f = fv[c * R + r];
+      const float* src = pa + (c * R + r) * D + d0;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) A[q] += f * src[q];
+    }
+    const float inv = Sr[r];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) A[q] = A[q] / inv;
     const int j = r / P.G, h = g * P.G + r % P.G;
-    afrag_put(a_o, j, h * D + d, A / Sr[r]);
+    afrag_put8(a_o, j, h * D + d0, A);
   }
 }
 
@@ -1772,8 +1807,9 @@ __device__ __forceinline__ void stamp(const PassP& P, int ph) {
 // The pass interprets a program of phases prepared by the host (one entry
 // per phase, a grid barrier between consecutive phases).  Each phase kind
 // is inlined once, and the weight ring lives in registers for the whole
-// pass.
-template <int WF>
+// pass.  Dense and MoE models get separate instances, each holding only the
+// phase kinds its programs use (the kernel's code size shows in its speed).
+template <int WF, bool MOE>
 __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
   extern __shared__ __align__(16) unsigned char smem[];
   Ctl* C = ctl(smem, (size_t)P.lds_bytes);
@@ -1822,6 +1858,7 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
         embed_phase(P, WF == W_F32, d->a_out, d->ss_out);
         break;
       case PH_STORE: {
+        if constexpr (!MOE) break;
         const SlotMap sm = d->slot_mode ? slots : dense;
         sync([&] { gemm_prefetch<WF, 1>(d->M, sm, d->slot_mode == 2, ring); });
         gemm_phase<WF, EPI_STORE, 1>(P, d->M, io, sm, d->slot_mode == 2, ring, smem, wst);
@@ -1837,6 +1874,7 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
         gemm_phase<WF, EPI_RESID, 1>(P, d->M, io, dense, false, ring, smem, wst);
         break;
       case PH_ROUTE_SWIGLU:
+        if constexpr (!MOE) break;
         sync([] {});
       {
         float* zl = nullptr;
@@ -1853,6 +1891,7 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
         break;
       }
       case PH_SWIGLU:
+        if constexpr (MOE) break;
         sync([&] { gemm_prefetch<WF, 2>(d->M, dense, false, ring); });
         gemm_phase<WF, EPI_SWIGLU, 2>(P, d->M, io, dense, false, ring, smem, wst);
         break;
@@ -1880,6 +1919,7 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
         attn_merge_phase(P, d->a_out, io.ready);
         break;
       case PH_COMBINE:
+        if constexpr (!MOE) break;
         sync([] {});
         moe_combine_phase(P, d->gain, io.trace, d->a_out, d->ss_out);
         break;
@@ -1900,23 +1940,26 @@ size_t pass_lds_bytes(int wfmt, int max_rows_attn, int D) {
   return b + kCtlBytes;
 }
 
-static const void* pick(int wfmt) {
-  if (wfmt == W_F32) return reinterpret_cast<const void*>(&k_pass<W_F32>);
-  if (wfmt == W_BF16) return reinterpret_cast<const void*>(&k_pass<W_BF16>);
-  if (wfmt == W_INT4) return reinterpret_cast<const void*>(&k_pass<W_INT4>);
+static const void* pick(int wfmt, bool moe) {
+  if (wfmt == W_F32) return moe ? reinterpret_cast<const void*>(&k_pass<W_F32, true>)
+                                : reinterpret_cast<const void*>(&k_pass<W_F32, false>);
+  if (wfmt == W_BF16) return moe ? reinterpret_cast<const void*>(&k_pass<W_BF16, true>)
+                                 : reinterpret_cast<const void*>(&k_pass<W_BF16, false>);
+  if (wfmt == W_INT4) return moe ? reinterpret_cast<const void*>(&k_pass<W_INT4, true>)
+                                 : reinterpret_cast<const void*>(&k_pass<W_INT4, false>);
   return nullptr;
 }
 
-hipError_t pass_occupancy(int wfmt, size_t lds, int* blocks_per_cu) {
-  const void* f = pick(wfmt);
+hipError_t pass_occupancy(int wfmt, bool moe, size_t lds, int* blocks_per_cu) {
+  const void* f = pick(wfmt, moe);
   if (!f) return hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, kThreads, lds);
 }
 
-hipError_t launch_pass(int wfmt, const PassP& p, int n_wg, size_t lds, hipStream_t s) {
-  const void* f = pick(wfmt);
+hipError_t launch_pass(int wfmt, bool moe, const PassP& p, int n_wg, size_t lds, hipStream_t s) {
+  const void* f = pick(wfmt, moe);
   if (!f) return hipErrorInvalidValue;
   PassP q = p;
   void* args[] = {&q};

@@ -496,7 +496,7 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   h->wall_khz = wclk > 0 ? (double)wclk : 100000.0;
   h->lds = pass_lds_bytes(h->wfmt, max_rows_attn(&c), D);
   int per_cu = 0;
-  HIPCHK(pass_occupancy(h->wfmt, h->lds, &per_cu));
+  HIPCHK(pass_occupancy(h->wfmt, c.n_experts > 0, h->lds, &per_cu));
   if (per_cu < 1) return fail(h, SPEC_EHIP, "the pass kernel does not fit on a compute unit");
   PassPlan plan;
   {
@@ -898,7 +898,7 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   p.wstamps = stamps ? h->wstamps_dev : nullptr;
 
   if (he == hipSuccess && h->profiling) he = hipEventRecord(h->ev[0], h->stream);
-  if (he == hipSuccess) he = launch_pass(h->wfmt, p, h->n_wg, h->lds, h->stream);
+  if (he == hipSuccess) he = launch_pass(h->wfmt, moe, p, h->n_wg, h->lds, h->stream);
   if (he != hipSuccess) {
     h->broken = true;
     return fail(h, SPEC_EHIP, std::string("pass launch: ") + hipGetErrorString(he));

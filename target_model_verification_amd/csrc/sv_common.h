@@ -159,9 +159,9 @@ __host__ __device__ inline int route_words(int E, int top_k) { return 1 + 2 * E 
 // One pass executes n_prog - 1 grid barriers (the host advances the barrier
 // generation by that much per launch).  fp32 weights imply an fp32 KV cache;
 // bf16 / int4 weights a bf16 cache.
-hipError_t launch_pass(int wfmt, const PassP& p, int n_wg, size_t lds, hipStream_t s);
+hipError_t launch_pass(int wfmt, bool moe, const PassP& p, int n_wg, size_t lds, hipStream_t s);
 size_t pass_lds_bytes(int wfmt, int max_rows_attn, int D);
-hipError_t pass_occupancy(int wfmt, size_t lds, int* blocks_per_cu);
+hipError_t pass_occupancy(int wfmt, bool moe, size_t lds, int* blocks_per_cu);
 // split units one workgroup may flush per phase (control-area capacity)
 constexpr int kMaxPending = 512;
 hipError_t launch_accept(const AcceptParams& p, hipStream_t s);
