@@ -71,6 +71,10 @@ def parse():
     ap.add_argument("--k-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--draft", default="synthetic", choices=("synthetic", "self"),
+                    help="drafts: the workload's corrupted greedy continuation, or (MoE) the model's own "
+                         "expert-sparse self-speculative draft (spec_draft)")
+    ap.add_argument("--draft-top-k", type=int, default=1, help="routed experts per draft token (--draft self)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device copy (the HBM counter calibration for --traffic-from)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -270,6 +274,50 @@ def measure_k_stochastic(sess: Session, k: int, warmup: int, steps: int):
                 profiled_seconds=None)
 
 
+def measure_self_draft(sess: Session, k: int, kd: int, warmup: int, steps: int):
+    """Self-speculative rounds (MoE): k draft tokens from the model itself
+    with kd routed experts per token (spec_draft, chained on the device),
+    then the verification step of the block, greedy acceptance.  Both calls
+    are timed per round (each returns after its result reached the host);
+    the verification pass is also timed with HIP events."""
+    import torch
+    B, h = sess.B, sess.h
+    h.rollback(sess.L0)
+    pending, rec, t_draft, t_verify = sess.pending0, [], 0.0, 0.0
+    L_start = None
+    for r in range(warmup + steps):
+        if r == warmup:
+            L_start = h.kv_len
+            h.profile(2)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        drafts = h.draft(pending, k, kd)
+        t1 = time.perf_counter()
+        L = h.kv_len
+        res = h.step([pending] + drafts, B.SPEC_ACCEPT_GREEDY)
+        t2 = time.perf_counter()
+        if r >= warmup:
+            t_draft += t1 - t0
+            t_verify += t2 - t1
+            rec.append((L, res.n_accepted))
+        pending = res.next_token
+    tprof = h.profile_read()
+    h.profile(0)
+    accepted = sum(n + 1 for _, n in rec)
+    n_p, ms_p, by_p = tprof["pass"]
+    dt = t_draft + t_verify
+    return dict(k=k, steps=steps, seconds=t_verify, ms_per_step=t_verify / steps * 1e3, accepted=accepted,
+                acc_tok_s=accepted / t_verify, verified_tok_s=steps * (k + 1) / t_verify,
+                mean_accept=accepted / steps, pass_gb=by_p / steps / 1e9, wall_gbs=by_p / t_verify / 1e9,
+                L_start=L_start, prof=tprof, timed=dict(pass_launches=n_p, pass_ms=ms_p, pass_bytes=by_p),
+                profiled_seconds=None,
+                self_draft=dict(draft_top_k=kd, draft_ms_per_round=t_draft / steps * 1e3,
+                                draft_ms_per_token=t_draft / steps / k * 1e3,
+                                verify_ms_per_round=t_verify / steps * 1e3,
+                                e2e_accepted_tok_s=accepted / dt,
+                                mean_accepted_drafts=accepted / steps - 1.0))
+
+
 def measure_k(sess: Session, k: int, warmup: int, steps: int):
     if sess.wl.accept == "stochastic":
         return measure_k_stochastic(sess, k, warmup, steps)
@@ -413,8 +461,13 @@ def main():
             log("[bench] calibration copy: 1 GiB read + 1 GiB written")
             del a, b
         results = {}
+        if args.draft == "self" and not wl.spec.moe:
+            raise SystemExit("--draft self drafts by expert sparsity: it needs a MoE workload")
         for kk in ks:
-            results[kk] = measure_k(sess, kk, args.warmup, args.steps)
+            if args.draft == "self":
+                results[kk] = measure_self_draft(sess, kk, args.draft_top_k, args.warmup, args.steps)
+            else:
+                results[kk] = measure_k(sess, kk, args.warmup, args.steps)
             r = results[kk]
             log(f"[bench] k={kk}: {r['ms_per_step']:.3f} ms/step, {r['acc_tok_s']:.1f} accepted tok/s, "
                 f"{r['verified_tok_s']:.1f} verified tok/s, mean accepted+1 {r['mean_accept']:.3f}, "
@@ -449,7 +502,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and wl.accept == "greedy":
         cpu = cpu_baseline(wl, W, k, r["L_start"], args.cpu_seconds, r["mean_accept"])
-    e_tok = expected_tokens(wl, k)
+    e_tok = expected_tokens(wl, k) if args.draft == "synthetic" else None
     line = {
         "metric": "accepted tok/s + verify-pass HBM GB/s vs peak, 7B bf16 k=8, single sequence",
         "value": round(r["acc_tok_s"], 2), "unit": "accepted tok/s", "n_gpus": 1, "steps": args.steps,
@@ -470,6 +523,12 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if args.draft == "self":
+        line["data"] = ("synthetic: random-init weights N(0,0.02), uniform random prompt ids, drafts = the model's own "
+                        f"greedy decode with {args.draft_top_k} routed expert(s) per token (self-speculative)")
+        line["config"]["workload"] = line["config"]["workload"].replace(
+            f"draft corruption {wl.corruption}", f"self-speculative draft with {args.draft_top_k} routed expert(s)")
+        line["self_draft"] = {kk: round(v, 4) if isinstance(v, float) else v for kk, v in r["self_draft"].items()}
     if args.k_sweep:
         def frac(v):
             t = v["timed"]

@@ -187,6 +187,33 @@ int spec_verify_step_noalloc(spec_verify_t* h, const int32_t* tokens, int32_t k,
                              const float* q_dev, const float* u_dev, spec_step_result* out,
                              float* logits_dev);
 
+/* Self-speculative draft of a MoE target by expert sparsity (S2-MoE,
+ * section 2.3 and section 5 "Draft configuration", Table 1: the draft is
+ * the target itself with fewer routed experts per token; section 4.3: the
+ * draft reads the target's cache, its own cache writes are temporary and
+ * only verified tokens are kept).  Runs n autoregressive single-token passes
+ * of this handle's model with draft_top_k routed experts per token (the
+ * router's top draft_top_k by probability, weights the unrenormalized
+ * probabilities, shared experts as in the target): pass i at position
+ * kv_len + i takes token pending (i = 0) or d_i, attends to the committed
+ * cache and the draft's own earlier entries, and d_{i+1} is the argmax of
+ * its logits (lowest id on ties).  The passes are chained on the device (no
+ * host round trip between tokens); the call returns after the n ids have
+ * reached the host.
+ *   pending:     the pending token (host), in [0, vocab).
+ *   n:           1..16 draft tokens.
+ *   draft_top_k: 1..top_k routed experts per draft token (MoE models only;
+ *                SPEC_EINVAL for dense models).
+ *   drafts:      host int32 [n] receiving d_1..d_n.
+ *   logits_dev:  NULL or device fp32 [n][vocab] receiving each draft pass's
+ *                logits (the draft distributions for stochastic acceptance
+ *                are their softmax).
+ * Requires kv_len + n <= max_ctx (else SPEC_ECAPACITY).  The committed
+ * length does not change: the draft's cache entries at kv_len .. kv_len+n-1
+ * are dead, and the verification step that follows overwrites them. */
+int spec_draft(spec_verify_t* h, int32_t pending, int32_t n, int32_t draft_top_k, int32_t* drafts,
+               float* logits_dev);
+
 /* Truncates the committed cache to new_kv_len (0 <= new_kv_len <= kv_len):
  * entries at or beyond it become dead and are overwritten by later blocks.
  * Metadata only; no device work. */

@@ -102,16 +102,18 @@ class BlockResult:
     trace: Optional[List[np.ndarray]] = None  # residual stream after each layer
 
 
-def route(M: OracleModel, layer: int, h: np.ndarray):
+def route(M: OracleModel, layer: int, h: np.ndarray, top_k: Optional[int] = None):
     """MoE router for a block: pi = softmax(h Wr + b) over all experts; each
-    token keeps its top_k experts by probability, ties to the lower expert
+    token keeps its top_k experts by probability (the model's top_k unless
+    given: a self-speculative draft keeps fewer), ties to the lower expert
     id; weights are the (unrenormalized) probabilities.  Returns
     (pi [m,E], sel [m,top_k] expert ids in rank order, r [m,E] logits)."""
     spec = M.spec
+    top_k = spec.top_k if top_k is None else top_k
     r = h @ M[f"l{layer}.router"] + M[f"l{layer}.router_bias"].astype(h.dtype)
     pi = nx.softmax(r, axis=-1)
     order = np.argsort(-pi, axis=-1, kind="stable")    # descending, ties -> lower id
-    sel = order[:, :spec.top_k]
+    sel = order[:, :top_k]
     return pi, sel, r
 
 
@@ -120,7 +122,7 @@ def expert_ffn(M: OracleModel, layer: int, e: int, h: np.ndarray) -> np.ndarray:
     return (nx.silu(h @ M[p + "w_gate"]) * (h @ M[p + "w_up"])) @ M[p + "w_down"]
 
 
-def moe_ffn(M: OracleModel, layer: int, h: np.ndarray):
+def moe_ffn(M: OracleModel, layer: int, h: np.ndarray, top_k: Optional[int] = None):
     """x-update of a MoE layer for a block of tokens h [m, d].
 
     For each token j, y_j = sum over its selected experts e of
@@ -130,8 +132,9 @@ def moe_ffn(M: OracleModel, layer: int, h: np.ndarray):
     in rank order, then the shared experts.
     """
     spec = M.spec
+    top_k = spec.top_k if top_k is None else top_k
     m = h.shape[0]
-    pi, sel, r = route(M, layer, h)
+    pi, sel, r = route(M, layer, h, top_k)
     out = {}
     union = sorted(set(int(e) for e in sel.reshape(-1)))
     for e in union:
@@ -147,16 +150,18 @@ def moe_ffn(M: OracleModel, layer: int, h: np.ndarray):
         y += expert_ffn(M, layer, spec.n_experts + s, h)
     # routing facts for near-tie flags and byte accounting
     srt = np.sort(r, axis=-1)[:, ::-1]
-    gap = srt[:, spec.top_k - 1] - srt[:, spec.top_k]
+    gap = srt[:, top_k - 1] - srt[:, top_k] if top_k < spec.n_experts else np.full(m, np.inf)
     info = dict(sel=sel, union=union, topk_gap=gap)
     return y, info
 
 
-def forward_block(M: OracleModel, kv: KVCache, tokens, L: int, trace: bool = False) -> BlockResult:
+def forward_block(M: OracleModel, kv: KVCache, tokens, L: int, trace: bool = False,
+                  top_k: Optional[int] = None) -> BlockResult:
     """One target pass over `tokens` at positions L..L+m-1 against the
     committed cache entries [0, L).  Writes the block's rounded k,v at
     positions L..L+m-1 of `kv` (dead until committed) and returns the m rows
-    of logits.  kv.length is not changed."""
+    of logits.  kv.length is not changed.  top_k (MoE): routed experts per
+    token, the model's own unless given."""
     spec = M.spec
     dt = M.dtype
     tokens = np.asarray(tokens, dtype=np.int64)
@@ -185,7 +190,7 @@ def forward_block(M: OracleModel, kv: KVCache, tokens, L: int, trace: bool = Fal
         x = x + o.reshape(m, H * D) @ M[p + "wo"]
         h2 = nx.rmsnorm(x, M[p + "ffn_norm"], spec.rms_eps)
         if spec.n_experts > 0:
-            y, info = moe_ffn(M, l, h2)
+            y, info = moe_ffn(M, l, h2, top_k)
             routing.append(info)
             x = x + y
         else:
@@ -205,6 +210,28 @@ def prefill(M: OracleModel, prompt, max_ctx: int, kv_dtype=None) -> (KVCache, np
     res = forward_block(M, kv, prompt, 0)
     kv.length = len(prompt)
     return kv, res.logits[-1]
+
+
+def draft_greedy(M: OracleModel, kv: KVCache, pending: int, n: int, top_k: int):
+    """Self-speculative draft of a MoE target by expert sparsity (S2-MoE
+    section 2.3 and section 5 "Draft configuration": the same model with
+    fewer routed experts per token; section 4.3: the draft reads the
+    target's cache and its own writes are temporary).  n single-token passes
+    with top_k routed experts, pass i at position kv.length + i on a copy of
+    the cache (the draft's entries never reach `kv`), each draft token the
+    argmax of the previous pass (lowest id on ties).  Returns (tokens [n],
+    logits [n, V], per-pass routing facts)."""
+    scratch = kv.copy()
+    L = kv.length
+    toks, rows, routing = [], [], []
+    tok = int(pending)
+    for i in range(n):
+        res = forward_block(M, scratch, [tok], L + i, top_k=top_k)
+        tok = int(np.argmax(res.logits[0]))
+        toks.append(tok)
+        rows.append(res.logits[0])
+        routing.append(res.routing)
+    return np.asarray(toks, dtype=np.int32), np.stack(rows), routing
 
 
 def ar_decode(M: OracleModel, kv: KVCache, pending: int, n: int) -> np.ndarray:

@@ -77,6 +77,7 @@ def _load():
         "spec_profile_raw": (I, [P, ctypes.POINTER(ctypes.c_uint64), ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
         "spec_pass_bytes": (D, [P, I, I, I, ctypes.c_int64]),
         "spec_kv_poison_dead": (I, [P]),
+        "spec_draft": (I, [P, I, I, I, ctypes.POINTER(ctypes.c_int32), P]),
         "spec_verify_step_noalloc": (I, [P, ctypes.POINTER(ctypes.c_int32), I, I, P, P,
                                          ctypes.POINTER(SpecStepResult), P]),
     }
@@ -105,6 +106,7 @@ spec_profile_detail = lib.spec_profile_detail
 spec_profile_raw = lib.spec_profile_raw
 spec_pass_bytes = lib.spec_pass_bytes
 spec_kv_poison_dead = lib.spec_kv_poison_dead
+spec_draft = lib.spec_draft
 spec_verify_step_noalloc = lib.spec_verify_step_noalloc
 
 
@@ -214,6 +216,14 @@ class Verifier:
         if rc != SPEC_OK:
             raise SpecError(rc, self.last_error())
         return res
+
+    def draft(self, pending: int, n: int, draft_top_k: int, logits_ptr: int = 0) -> List[int]:
+        """Self-speculative draft tokens d_1..d_n (spec_draft)."""
+        out = (ctypes.c_int32 * n)()
+        rc = spec_draft(self.h, int(pending), int(n), int(draft_top_k), out, logits_ptr or None)
+        if rc != SPEC_OK:
+            raise SpecError(rc, self.last_error())
+        return [int(x) for x in out]
 
     def rollback(self, new_len: int) -> None:
         rc = spec_kv_commit_rollback(self.h, new_len)

@@ -89,6 +89,8 @@ struct spec_verify {
   int* result_dev = nullptr;
   int* tokens_host = nullptr;   // pinned
   int* result_host = nullptr;   // pinned
+  int* draft_res = nullptr;     // self-speculative draft: [kMaxRows][4] acceptance records (device)
+  int* draft_host = nullptr;    // pinned copy of draft_res and the error flag
   // the pass program
   Phase* prog = nullptr;
   int n_prog = 0;
@@ -674,6 +676,9 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   }
   HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->tokens_host), 16 * sizeof(int), hipHostMallocDefault));
   HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->result_host), 4 * sizeof(int), hipHostMallocDefault));
+  if ((rc = dalloc_z(h, &h->draft_res, (size_t)kMaxRows * 4))) return rc;
+  HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->draft_host), (kMaxRows * 4 + 4) * sizeof(int),
+                       hipHostMallocDefault));
 
   // ---- the pass program
   std::vector<Phase> prog;
@@ -804,6 +809,7 @@ void free_all(spec_verify* h) {
   h->allocs.clear();
   if (h->tokens_host) (void)hipHostFree(h->tokens_host);
   if (h->result_host) (void)hipHostFree(h->result_host);
+  if (h->draft_host) (void)hipHostFree(h->draft_host);
   for (auto& e : h->ev)
     if (e) (void)hipEventDestroy(e);
 }
@@ -830,6 +836,50 @@ double phase_bytes(const spec_verify* h, int i, int m, int L, int experts_loaded
     case SPEC_K_LMHEAD: return w + (double)m * d * 4 + (double)m * c.vocab * 4;
     default: return 0;
   }
+}
+
+// Parameters of one pass over m block rows at committed length L, reading
+// the block's token ids from tokens_dev, with top_k routed experts per token
+// (MoE).
+PassP pass_params(const spec_verify* h, int m, int L, const int* tokens_dev, int top_k) {
+  const spec_config& c = h->cfg;
+  const bool moe = c.n_experts > 0;
+  PassP p{};
+  p.m = m; p.L = L; p.n_layers = c.n_layers; p.d = c.d_model; p.Hq = c.n_q_heads; p.Hkv = c.n_kv_heads;
+  p.D = c.head_dim; p.V = c.vocab; p.G = c.n_q_heads / c.n_kv_heads; p.E = c.n_experts; p.top_k = top_k;
+  p.n_shared = c.n_shared; p.F = moe ? c.d_ff_expert : c.d_ff;
+  p.n_groups = cdiv(L + m, kGroupPos);
+  // heads whose merge is small are merged by their last attention item;
+  // the merge phases (one per layer) then run without a barrier
+  p.attn_inline = (long long)m * p.G * c.head_dim * p.n_groups <= kInlineMergeElems ? 1 : 0;
+  p.attn_tickets = h->attn_tickets;
+  p.n_ss = h->n_ss;
+  p.lds_bytes = (int)h->lds;
+  p.eps = c.rms_eps;
+  p.inv_d = 1.0f / (float)c.d_model;
+  p.attn_scale = 1.0f / std::sqrt((float)c.head_dim);
+  p.prog = h->prog; p.n_prog = h->n_prog;
+  p.embed = h->embed; p.gain0 = h->layers[0].attn_norm;
+  p.tokens = tokens_dev; p.page_table = h->page_table; p.rope_cs = h->rope_cs;
+  p.x = h->x; p.ldx = h->ldx;
+  p.logits = h->logits; p.ldl = h->ldl;
+  p.ready = h->ready; p.epoch = h->epoch + 1; p.qf_rt = h->qf_rt; p.o_wcols = h->o_wcols;
+  p.st_max = h->st_max; p.st_sum = h->st_sum; p.st_idx = h->st_idx; p.n_stat = h->n_stat;
+  p.pm = h->pm; p.ps = h->ps; p.pacc = h->pacc;
+  p.rlog = h->rlog; p.ldr = h->ldr; p.ey = h->ey; p.ey_slot = h->ey_slot; p.ldy = h->ldx;
+  p.route = h->route;
+  p.bar = h->bar; p.bar_base = h->bar_gen; p.err = h->result_dev + 3;
+  return p;
+}
+
+// Launches one pass and advances the handle's barrier generation and pass
+// count (the device counters are monotonic over the handle's lifetime).
+hipError_t launch_counted(spec_verify* h, const PassP& p) {
+  const hipError_t he = launch_pass(h->wfmt, h->cfg.n_experts > 0, p, h->n_wg, h->lds, h->stream);
+  if (he != hipSuccess) return he;
+  h->bar_gen += (unsigned long long)(p.attn_inline ? h->n_barriers_inline : h->n_barriers_merge);
+  h->epoch = p.epoch;
+  return hipSuccess;
 }
 
 int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, const float* q_dev,
@@ -859,31 +909,7 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   std::memcpy(h->tokens_host, tokens, sizeof(int32_t) * m);
   hipError_t he = hipMemcpyAsync(h->tokens_dev, h->tokens_host, sizeof(int32_t) * m, hipMemcpyHostToDevice,
                                  h->stream);
-  PassP p{};
-  p.m = m; p.L = L; p.n_layers = c.n_layers; p.d = c.d_model; p.Hq = c.n_q_heads; p.Hkv = c.n_kv_heads;
-  p.D = c.head_dim; p.V = c.vocab; p.G = c.n_q_heads / c.n_kv_heads; p.E = c.n_experts; p.top_k = c.top_k;
-  p.n_shared = c.n_shared; p.F = moe ? c.d_ff_expert : c.d_ff;
-  p.n_groups = cdiv(L + m, kGroupPos);
-  // heads whose merge is small are merged by their last attention item;
-  // the merge phases (one per layer) then run without a barrier
-  p.attn_inline = (long long)m * p.G * c.head_dim * p.n_groups <= kInlineMergeElems ? 1 : 0;
-  p.attn_tickets = h->attn_tickets;
-  p.n_ss = h->n_ss;
-  p.lds_bytes = (int)h->lds;
-  p.eps = c.rms_eps;
-  p.inv_d = 1.0f / (float)c.d_model;
-  p.attn_scale = 1.0f / std::sqrt((float)c.head_dim);
-  p.prog = h->prog; p.n_prog = h->n_prog;
-  p.embed = h->embed; p.gain0 = h->layers[0].attn_norm;
-  p.tokens = h->tokens_dev; p.page_table = h->page_table; p.rope_cs = h->rope_cs;
-  p.x = h->x; p.ldx = h->ldx;
-  p.logits = h->logits; p.ldl = h->ldl;
-  p.ready = h->ready; p.epoch = h->epoch + 1; p.qf_rt = h->qf_rt; p.o_wcols = h->o_wcols;
-  p.st_max = h->st_max; p.st_sum = h->st_sum; p.st_idx = h->st_idx; p.n_stat = h->n_stat;
-  p.pm = h->pm; p.ps = h->ps; p.pacc = h->pacc;
-  p.rlog = h->rlog; p.ldr = h->ldr; p.ey = h->ey; p.ey_slot = h->ey_slot; p.ldy = h->ldx;
-  p.route = h->route;
-  p.bar = h->bar; p.bar_base = h->bar_gen; p.err = h->result_dev + 3;
+  PassP p = pass_params(h, m, L, h->tokens_dev, c.top_k);
   if (noalloc) {
     // partials in the fixed scratch; its tickets start at zero
     p.ws_alt = static_cast<float*>(h->scratch);
@@ -898,13 +924,11 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   p.wstamps = stamps ? h->wstamps_dev : nullptr;
 
   if (he == hipSuccess && h->profiling) he = hipEventRecord(h->ev[0], h->stream);
-  if (he == hipSuccess) he = launch_pass(h->wfmt, moe, p, h->n_wg, h->lds, h->stream);
+  if (he == hipSuccess) he = launch_counted(h, p);
   if (he != hipSuccess) {
     h->broken = true;
     return fail(h, SPEC_EHIP, std::string("pass launch: ") + hipGetErrorString(he));
   }
-  h->bar_gen += (unsigned long long)(p.attn_inline ? h->n_barriers_inline : h->n_barriers_merge);
-  h->epoch = p.epoch;
   if (h->profiling) he = hipEventRecord(h->ev[1], h->stream);
   AcceptParams a{};
   a.k = k; a.V = c.vocab; a.L = L; a.mode = mode; a.n_stat = h->n_stat;
@@ -1072,6 +1096,57 @@ int spec_verify_step_debug(spec_verify_t* h, const int32_t* tokens, int32_t k, i
                            const float* q_dev, const float* u_dev, spec_step_result* out, float* logits_dev,
                            float* trace_dev, int32_t* union_dev, int32_t* route_dev) {
   return step_impl(h, tokens, k, mode, q_dev, u_dev, out, logits_dev, trace_dev, union_dev, route_dev);
+}
+
+int spec_draft(spec_verify_t* h, int32_t pending, int32_t n, int32_t draft_top_k, int32_t* drafts,
+               float* logits_dev) {
+  if (!h) return SPEC_EINVAL;
+  if (h->broken) return fail(h, SPEC_ESTATE, "handle unusable after an earlier GPU error");
+  const spec_config& c = h->cfg;
+  if (c.n_experts <= 0) return fail(h, SPEC_EINVAL, "drafting by expert sparsity needs a MoE model");
+  if (draft_top_k < 1 || draft_top_k > c.top_k) return fail(h, SPEC_EINVAL, "draft_top_k must be in [1, top_k]");
+  if (n < 1 || n > kMaxRows) return fail(h, SPEC_EINVAL, "n must be in [1, 16]");
+  if (!drafts) return fail(h, SPEC_EINVAL, "drafts must not be NULL");
+  if (pending < 0 || pending >= c.vocab) return fail(h, SPEC_EINVAL, "token id out of range");
+  const int L0 = h->kv_len;
+  if ((long long)L0 + n > c.max_ctx) return fail(h, SPEC_ECAPACITY, "draft exceeds max_ctx");
+  h->tokens_host[0] = pending;
+  hipError_t he = hipMemcpyAsync(h->tokens_dev, h->tokens_host, sizeof(int32_t), hipMemcpyHostToDevice, h->stream);
+  // pass i reads its token from pass i-1's acceptance record (device-side
+  // chaining: no host round trip between draft tokens)
+  for (int i = 0; i < n && he == hipSuccess; ++i) {
+    const int* tok = i == 0 ? h->tokens_dev : h->draft_res + 4 * (i - 1) + 1;
+    const PassP p = pass_params(h, 1, L0 + i, tok, draft_top_k);
+    he = launch_counted(h, p);
+    AcceptParams a{};
+    a.k = 0; a.V = c.vocab; a.L = L0 + i; a.mode = SPEC_ACCEPT_NONE; a.n_stat = h->n_stat;
+    a.tokens = tok;
+    a.st_max = h->st_max; a.st_sum = h->st_sum; a.st_idx = h->st_idx;
+    a.logits = h->logits; a.ldl = h->ldl;
+    a.result = h->draft_res + 4 * i;
+    if (he == hipSuccess) he = launch_accept(a, h->stream);
+    if (he == hipSuccess && logits_dev)
+      he = hipMemcpyAsync(logits_dev + (long long)i * c.vocab, h->logits, (size_t)c.vocab * 4, hipMemcpyDeviceToDevice,
+                          h->stream);
+  }
+  if (he == hipSuccess)
+    he = hipMemcpyAsync(h->draft_host, h->draft_res, sizeof(int) * 4 * n, hipMemcpyDeviceToHost, h->stream);
+  if (he == hipSuccess)
+    he = hipMemcpyAsync(h->draft_host + kMaxRows * 4, h->result_dev, sizeof(int) * 4, hipMemcpyDeviceToHost,
+                        h->stream);
+  if (he == hipSuccess) he = hipStreamSynchronize(h->stream);
+  if (he != hipSuccess) {
+    h->broken = true;
+    return fail(h, SPEC_EHIP, std::string("draft: ") + hipGetErrorString(he));
+  }
+  if (h->draft_host[kMaxRows * 4 + 3] != 0) {
+    h->broken = true;
+    return fail(h, SPEC_EHIP, "grid barrier wait timed out inside a draft pass");
+  }
+  for (int i = 0; i < n; ++i) drafts[i] = h->draft_host[4 * i + 1];
+  // the committed length is unchanged: the draft's cache entries are dead
+  h->err.clear();
+  return SPEC_OK;
 }
 
 int spec_kv_commit_rollback(spec_verify_t* h, int32_t new_kv_len) {

@@ -108,3 +108,58 @@ def test_router_bias_prior_is_zipf():
     z /= z.sum()
     assert np.allclose(np.sort(p)[::-1], z, rtol=1e-6)
     assert len(set(ranks.tolist())) == 64
+
+
+def test_moe_fewer_experts_equals_per_token_loop():
+    """Routing with fewer experts per token (the self-speculative draft's
+    expert sparsity): per-token brute force with the router's top k' by
+    probability (ties to the lower id), unrenormalized weights, plus the
+    shared expert."""
+    wl, W, M = _model("small_moe")
+    spec = wl.spec
+    rng = np.random.default_rng(11)
+    h = rng.standard_normal((9, spec.d_model))
+    for kd in (1, 2, 3):
+        y, info = om.moe_ffn(M, 1, h, top_k=kd)
+        for j in range(9):
+            r = h[j] @ M["l1.router"] + M["l1.router_bias"]
+            pi = np.exp(r - r.max())
+            pi /= pi.sum()
+            top = sorted(range(spec.n_experts), key=lambda e: (-pi[e], e))[:kd]
+            ref = sum(pi[e] * om.expert_ffn(M, 1, e, h[j:j + 1])[0] for e in top)
+            ref = ref + om.expert_ffn(M, 1, spec.n_experts, h[j:j + 1])[0]
+            assert np.max(np.abs(y[j] - ref)) < 1e-12
+            assert [int(e) for e in info["sel"][j]] == top
+
+
+def test_draft_with_all_experts_is_the_greedy_decode():
+    """A draft that keeps the target's own expert count is the target: its
+    tokens are the greedy autoregressive decode, bitwise (same operations),
+    and the committed cache is left untouched."""
+    wl, W, M = _model("small_moe")
+    kv, last = om.prefill(M, synth.prompt_ids(wl, 40), 80)
+    pending = int(np.argmax(last))
+    before = [k.copy() for k in kv.K]
+    toks, logits, _ = om.draft_greedy(M, kv, pending, 8, wl.spec.top_k)
+    assert list(toks) == list(om.ar_decode(M, kv, pending, 8))
+    assert kv.length == 40 and all(np.array_equal(a, b) for a, b in zip(before, kv.K))
+    # each draft token is the argmax of a fresh pass over the drafted prefix
+    scratch = kv.copy()
+    seq = [pending] + list(toks[:-1])
+    res = om.forward_block(M, scratch, seq, kv.length)
+    assert list(np.argmax(res.logits, axis=-1)) == list(toks)
+
+
+def test_sparse_draft_is_its_own_model():
+    """A draft with one routed expert is a different (cheaper) model: its
+    tokens are the greedy decode of the same weights routed top-1, i.e. the
+    argmax rows of one block pass with top_k = 1 over the drafted prefix
+    (the nesting invariant of that model)."""
+    wl, W, M = _model("small_moe")
+    kv, last = om.prefill(M, synth.prompt_ids(wl, 40), 80)
+    pending = int(np.argmax(last))
+    toks, logits, _ = om.draft_greedy(M, kv, pending, 8, 1)
+    scratch = kv.copy()
+    res = om.forward_block(M, scratch, [pending] + list(toks[:-1]), kv.length, top_k=1)
+    assert list(np.argmax(res.logits, axis=-1)) == list(toks)
+    assert np.max(np.abs(res.logits - logits)) < 1e-9
