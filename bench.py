@@ -75,6 +75,12 @@ def parse():
                     help="drafts: the workload's corrupted greedy continuation, or (MoE) the model's own "
                          "expert-sparse self-speculative draft (spec_draft)")
     ap.add_argument("--draft-top-k", type=int, default=1, help="routed experts per draft token (--draft self)")
+    ap.add_argument("--reuse-cap", type=int, default=0,
+                    help="MoE: verify with reuse-aware expert gating (lossy) over this many preferred experts")
+    ap.add_argument("--reuse-alpha", type=float, default=0.5, help="bias scale of reuse-aware gating")
+    ap.add_argument("--adaptive-k", action="store_true",
+                    help="also time rounds whose lookahead follows spec_adaptive_k (start 5, +2 after a full "
+                         "accept, -1 otherwise)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a 1 GiB device copy (the HBM counter calibration for --traffic-from)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -125,6 +131,7 @@ class Session:
         from target_model_verification_amd import binding as B
         from target_model_verification_amd import synth
         self.B, self.np = B, np
+        self.reuse = None   # (cap, alpha): verify with reuse-aware gating
         self.wl = wl
         self.spec = wl.spec
         self.max_k = max_k
@@ -178,7 +185,10 @@ class Session:
             tok[0] = pending
             tok[1:] = np.where(flags, ids, self.ref[s + 1:s + 1 + k])
             L = h.kv_len
-            res = h.step(tok, B.SPEC_ACCEPT_GREEDY)
+            if self.reuse:
+                res = h.step_reuse(tok, self.reuse[0], self.reuse[1], B.SPEC_ACCEPT_GREEDY)
+            else:
+                res = h.step(tok, B.SPEC_ACCEPT_GREEDY)
             out.append((L, res.n_accepted))
             s += res.n_accepted + 1
             pending = res.next_token
@@ -318,6 +328,78 @@ def measure_self_draft(sess: Session, k: int, kd: int, warmup: int, steps: int):
                                 mean_accepted_drafts=accepted / steps - 1.0))
 
 
+def reuse_quality(sess: Session, k: int, cap: int, alpha: float, n_blocks: int = 8):
+    """Reuse-aware gating against the exact pass on the same blocks (untimed):
+    experts loaded per layer and the output consistency metrics of S2-MoE
+    section 6.2.2 (mean KL, RMS probability shift, top-1 agreement,
+    perplexity ratio of the blocks' next tokens)."""
+    import torch
+    np, B, h = sess.np, sess.B, sess.h
+    spec = sess.spec
+    h.rollback(sess.L0)
+    ex_u, re_u, kl, dp, top1, dnll = [], [], [], [], [], []
+    for r in range(n_blocks):
+        flags, ids = sess.rounds(k, 1, first_round=20000 + r)[0]
+        s = r * (k + 1)
+        tok = np.concatenate([[sess.ref[s]], np.where(flags, ids, sess.ref[s + 1:s + 1 + k])]).astype(np.int32)
+        out = {}
+        for name, reuse in (("exact", None), ("reuse", (cap, alpha))):
+            lg = torch.empty((k + 1, spec.vocab), dtype=torch.float32, device="cuda")
+            un = torch.zeros(spec.n_layers, dtype=torch.int32, device="cuda")
+            if reuse:
+                h.step_reuse(tok, cap, alpha, B.SPEC_ACCEPT_NONE, logits_ptr=lg.data_ptr(), union_ptr=un.data_ptr())
+            else:
+                h.step(tok, B.SPEC_ACCEPT_NONE, 0, 0, lg.data_ptr(), union_ptr=un.data_ptr())
+            h.rollback(sess.L0)
+            out[name] = (lg[:k].double(), float(un.float().mean()))
+        p = torch.softmax(out["exact"][0], -1)
+        q = torch.softmax(out["reuse"][0], -1)
+        nxt = torch.from_numpy(tok[1:].astype(np.int64)).to(p.device)
+        kl.append(float((p * (torch.log(p.clamp_min(1e-300)) - torch.log(q.clamp_min(1e-300)))).sum(-1).mean()))
+        dp.append(float(((q - p) ** 2).mean(-1).sqrt().mean()))
+        top1.append(float((p.argmax(-1) == q.argmax(-1)).double().mean()))
+        ar = torch.arange(k, device=p.device)
+        dnll.append(float((-torch.log(q[ar, nxt]) + torch.log(p[ar, nxt])).mean()))
+        ex_u.append(out["exact"][1])
+        re_u.append(out["reuse"][1])
+    import math
+    return dict(cap=cap, alpha=alpha, blocks=n_blocks, experts_per_layer_exact=round(sum(ex_u) / n_blocks, 3),
+                experts_per_layer_reuse=round(sum(re_u) / n_blocks, 3),
+                reuse_ratio_exact=round(sum(ex_u) / n_blocks / ((k + 1) * spec.top_k), 4),
+                reuse_ratio_reuse=round(sum(re_u) / n_blocks / ((k + 1) * spec.top_k), 4),
+                mean_kl=sum(kl) / n_blocks, rms_dp=sum(dp) / n_blocks, top1_agreement=sum(top1) / n_blocks,
+                ppl_ratio=math.exp(sum(dnll) / n_blocks))
+
+
+def measure_adaptive(sess: Session, k0: int, warmup: int, steps: int):
+    """Greedy rounds whose lookahead follows the adaptive schedule
+    (spec_adaptive_k), drafts drawn as for the fixed-k runs.  Returns
+    accepted tok/s over the timed rounds and the lookahead histogram."""
+    import torch
+    np, B, h = sess.np, sess.B, sess.h
+    h.rollback(sess.L0)
+    s, pending, k = 0, sess.pending0, k0
+    ks, acc, dt = [], 0, 0.0
+    for r in range(warmup + steps):
+        flags, ids = sess.rounds(k, 1, first_round=10000 + r)[0]
+        tok = np.concatenate([[pending], np.where(flags, ids, sess.ref[s + 1:s + 1 + k])]).astype(np.int32)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        res = h.step(tok, B.SPEC_ACCEPT_GREEDY)
+        el = time.perf_counter() - t0
+        if r >= warmup:
+            dt += el
+            acc += res.n_accepted + 1
+            ks.append(k)
+        s += res.n_accepted + 1
+        pending = res.next_token
+        k = B.spec_adaptive_k(k, res.n_accepted, sess.max_k)
+    hist = {str(v): ks.count(v) for v in sorted(set(ks))}
+    return dict(k0=k0, max_k=sess.max_k, steps=steps, accepted_tok_s=round(acc / dt, 2),
+                ms_per_step=round(dt / steps * 1e3, 4), mean_k=round(sum(ks) / steps, 3),
+                mean_tokens_per_step=round(acc / steps, 4), k_histogram=hist)
+
+
 def measure_k(sess: Session, k: int, warmup: int, steps: int):
     if sess.wl.accept == "stochastic":
         return measure_k_stochastic(sess, k, warmup, steps)
@@ -452,7 +534,7 @@ def main():
         f"{time.time() - t:.1f} s")
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        sess = Session(wl, W, max(ks), args.warmup + args.steps, stream.cuda_stream)
+        sess = Session(wl, W, 15 if args.adaptive_k else max(ks), args.warmup + args.steps, stream.cuda_stream)
         if args.calib_copy:
             a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
             b = torch.empty_like(a)
@@ -461,6 +543,10 @@ def main():
             log("[bench] calibration copy: 1 GiB read + 1 GiB written")
             del a, b
         results = {}
+        if args.reuse_cap:
+            if not wl.spec.moe or args.draft != "synthetic":
+                raise SystemExit("--reuse-cap needs a MoE workload with synthetic drafts")
+            sess.reuse = (args.reuse_cap, args.reuse_alpha)
         if args.draft == "self" and not wl.spec.moe:
             raise SystemExit("--draft self drafts by expert sparsity: it needs a MoE workload")
         for kk in ks:
@@ -523,6 +609,18 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if args.reuse_cap:
+        with torch.cuda.stream(stream):
+            line["reuse_gating"] = reuse_quality(sess, k, args.reuse_cap, args.reuse_alpha)
+        line["config"]["workload"] += (f", reuse-aware expert gating (lossy) cap {args.reuse_cap} "
+                                       f"alpha {args.reuse_alpha}")
+        log(f"[bench] reuse-aware gating: {line['reuse_gating']}")
+    if args.adaptive_k:
+        if wl.accept != "greedy" or args.draft != "synthetic":
+            raise SystemExit("--adaptive-k runs greedy rounds with the workload's synthetic drafts")
+        with torch.cuda.stream(stream):
+            line["adaptive_k"] = measure_adaptive(sess, 5, args.warmup, args.steps)
+        log(f"[bench] adaptive k: {line['adaptive_k']}")
     if args.draft == "self":
         line["data"] = ("synthetic: random-init weights N(0,0.02), uniform random prompt ids, drafts = the model's own "
                         f"greedy decode with {args.draft_top_k} routed expert(s) per token (self-speculative)")

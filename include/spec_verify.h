@@ -214,6 +214,35 @@ int spec_verify_step_noalloc(spec_verify_t* h, const int32_t* tokens, int32_t k,
 int spec_draft(spec_verify_t* h, int32_t pending, int32_t n, int32_t draft_top_k, int32_t* drafts,
                float* logits_dev);
 
+/* Lossy variant of spec_verify_step with reuse-aware expert gating (S2-MoE
+ * section 4.2): in every MoE layer the block's rows steer their routing
+ * towards shared experts, so the union of experts the pass loads shrinks.
+ * For block rows b with gating logits l_b (router logits plus bias):
+ * importance g_e = sum_b w_b l_{b,e} with w_b = conf_dev[b] (device fp32
+ * [k+1], non-negative; NULL: all 1); the `cap` experts of largest importance
+ * (ties to the lower id) are preferred; row b adds alpha * (l_b(1) -
+ * l_b(top_k+1)) -- its first minus its (top_k+1)-th logit -- to the preferred
+ * experts' logits, and top_k routing (selection and weights) runs on the
+ * biased logits.  alpha = 0, or cap = n_experts (the same shift for every
+ * expert of a row), gives the exact target.  The outputs are those of the
+ * modified model: acceptance no longer reproduces the target's own decode.
+ * MoE models with top_k < n_experts only; cap in [top_k, n_experts],
+ * alpha >= 0.  union_dev / route_dev as in spec_verify_step_debug (may be
+ * NULL).  Other arguments, results and errors as in spec_verify_step. */
+int spec_verify_step_reuse(spec_verify_t* h, const int32_t* tokens, int32_t k, int32_t mode,
+                           const float* q_dev, const float* u_dev, const float* conf_dev, int32_t cap,
+                           float alpha, spec_step_result* out, float* logits_dev, int32_t* union_dev,
+                           int32_t* route_dev);
+
+/* Lookahead schedule for the next round (host policy, no device work): the
+ * adaptive schedule the essay "LLM Inference: Speculative Decoding"
+ * attributes to HuggingFace in "And the checking stops being free" -- raise
+ * the lookahead by 2 after a round whose whole block was accepted, back off
+ * otherwise.  Returns min(k + 2, max_k) if n_accepted == k, else
+ * max(1, k - 1); -1 if k is outside [1, max_k], max_k < 1 or n_accepted is
+ * outside [0, k]. */
+int32_t spec_adaptive_k(int32_t k, int32_t n_accepted, int32_t max_k);
+
 /* Truncates the committed cache to new_kv_len (0 <= new_kv_len <= kv_len):
  * entries at or beyond it become dead and are overwritten by later blocks.
  * Metadata only; no device work. */

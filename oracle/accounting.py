@@ -10,10 +10,14 @@ Test infrastructure only (see the package docstring).
 * Expected output tokens per round for per-token acceptance rate a and
   lookahead k: (1 - a^(k+1)) / (1 - a), rising to the ceiling 1/(1-a)
   (same essay, "Being right five times in a row is rare").
+* The adaptive lookahead schedule the essay attributes to HuggingFace
+  ("And the checking stops being free"): +2 after a fully accepted block,
+  back off otherwise (read as -1, never below 1, never above the largest
+  lookahead the verifier takes).
 """
 from __future__ import annotations
 
-from typing import Dict, Sequence
+from typing import Dict, List, Sequence
 
 
 def run_counters(k: int, n_accepted: Sequence[int], n_tokens: int) -> Dict[str, int]:
@@ -32,6 +36,20 @@ def run_counters(k: int, n_accepted: Sequence[int], n_tokens: int) -> Dict[str, 
         tokens=min(emitted, n_tokens),
         target_passes_saved=min(emitted, n_tokens) - rounds,
     )
+
+
+def adaptive_k_schedule(k0: int, n_accepted_seq: Sequence[int], max_k: int) -> List[int]:
+    """Lookahead of every round: round 0 uses k0; after a round with
+    lookahead k and n accepted drafts, the next uses k + 2 (at most max_k)
+    when n == k, else k - 1 (at least 1).  Returns one k per round plus the
+    k the next round would use."""
+    ks = [k0]
+    for n in n_accepted_seq:
+        k = ks[-1]
+        if not 0 <= n <= k:
+            raise ValueError("accepted count outside [0, k]")
+        ks.append(min(k + 2, max_k) if n == k else max(1, k - 1))
+    return ks
 
 
 def expected_tokens_per_round(a: float, k: int) -> float:

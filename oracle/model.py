@@ -102,15 +102,44 @@ class BlockResult:
     trace: Optional[List[np.ndarray]] = None  # residual stream after each layer
 
 
-def route(M: OracleModel, layer: int, h: np.ndarray, top_k: Optional[int] = None):
+def reuse_gating_logits(r: np.ndarray, w: np.ndarray, top_k: int, cap: int, alpha: float):
+    """Reuse-aware expert gating (S2-MoE section 4.2), step by step on a
+    block's gating logits r [m, E]:
+      1. importance of expert e: g_e = sum_b w_b r_{b,e} (w: row confidences);
+      2. preferred experts: the `cap` experts of largest importance, ties to
+         the lower id;
+      3. each row b adds lambda_b = alpha (r_b(1) - r_b(top_k+1)), its first
+         minus its (top_k+1)-th logit, to the preferred experts' logits.
+    Returns (biased logits [m, E], preferred mask [E], gap between the cap-th
+    and the (cap+1)-th importance)."""
+    r = np.asarray(r, dtype=np.float64)
+    m, E = r.shape
+    g = np.zeros(E)
+    for b in range(m):
+        g = g + float(w[b]) * r[b]
+    order = np.argsort(-g, kind="stable")
+    pref = np.zeros(E, dtype=bool)
+    pref[order[:cap]] = True
+    cap_gap = float(g[order[cap - 1]] - g[order[cap]]) if cap < E else np.inf
+    srt = np.sort(r, axis=-1)[:, ::-1]
+    lam = alpha * (srt[:, 0] - srt[:, top_k])
+    return r + lam[:, None] * pref[None, :], pref, cap_gap
+
+
+def route(M: OracleModel, layer: int, h: np.ndarray, top_k: Optional[int] = None, reuse=None):
     """MoE router for a block: pi = softmax(h Wr + b) over all experts; each
     token keeps its top_k experts by probability (the model's top_k unless
     given: a self-speculative draft keeps fewer), ties to the lower expert
-    id; weights are the (unrenormalized) probabilities.  Returns
+    id; weights are the (unrenormalized) probabilities.  reuse = (w, cap,
+    alpha) first biases the gating logits (reuse_gating_logits).  Returns
     (pi [m,E], sel [m,top_k] expert ids in rank order, r [m,E] logits)."""
     spec = M.spec
     top_k = spec.top_k if top_k is None else top_k
     r = h @ M[f"l{layer}.router"] + M[f"l{layer}.router_bias"].astype(h.dtype)
+    if reuse is not None:
+        w, cap, alpha = reuse
+        r, _, _ = reuse_gating_logits(r, w, top_k, cap, alpha)
+        r = r.astype(h.dtype)
     pi = nx.softmax(r, axis=-1)
     order = np.argsort(-pi, axis=-1, kind="stable")    # descending, ties -> lower id
     sel = order[:, :top_k]
@@ -122,7 +151,7 @@ def expert_ffn(M: OracleModel, layer: int, e: int, h: np.ndarray) -> np.ndarray:
     return (nx.silu(h @ M[p + "w_gate"]) * (h @ M[p + "w_up"])) @ M[p + "w_down"]
 
 
-def moe_ffn(M: OracleModel, layer: int, h: np.ndarray, top_k: Optional[int] = None):
+def moe_ffn(M: OracleModel, layer: int, h: np.ndarray, top_k: Optional[int] = None, reuse=None):
     """x-update of a MoE layer for a block of tokens h [m, d].
 
     For each token j, y_j = sum over its selected experts e of
@@ -134,7 +163,7 @@ def moe_ffn(M: OracleModel, layer: int, h: np.ndarray, top_k: Optional[int] = No
     spec = M.spec
     top_k = spec.top_k if top_k is None else top_k
     m = h.shape[0]
-    pi, sel, r = route(M, layer, h, top_k)
+    pi, sel, r = route(M, layer, h, top_k, reuse)
     out = {}
     union = sorted(set(int(e) for e in sel.reshape(-1)))
     for e in union:
@@ -152,16 +181,20 @@ def moe_ffn(M: OracleModel, layer: int, h: np.ndarray, top_k: Optional[int] = No
     srt = np.sort(r, axis=-1)[:, ::-1]
     gap = srt[:, top_k - 1] - srt[:, top_k] if top_k < spec.n_experts else np.full(m, np.inf)
     info = dict(sel=sel, union=union, topk_gap=gap)
+    if reuse is not None:
+        r0 = h @ M[f"l{layer}.router"] + M[f"l{layer}.router_bias"].astype(h.dtype)
+        info["cap_gap"] = reuse_gating_logits(r0, reuse[0], top_k, reuse[1], reuse[2])[2]
     return y, info
 
 
 def forward_block(M: OracleModel, kv: KVCache, tokens, L: int, trace: bool = False,
-                  top_k: Optional[int] = None) -> BlockResult:
+                  top_k: Optional[int] = None, reuse=None) -> BlockResult:
     """One target pass over `tokens` at positions L..L+m-1 against the
     committed cache entries [0, L).  Writes the block's rounded k,v at
     positions L..L+m-1 of `kv` (dead until committed) and returns the m rows
     of logits.  kv.length is not changed.  top_k (MoE): routed experts per
-    token, the model's own unless given."""
+    token, the model's own unless given; reuse = (w [m], cap, alpha): the
+    lossy reuse-aware gating of every MoE layer (reuse_gating_logits)."""
     spec = M.spec
     dt = M.dtype
     tokens = np.asarray(tokens, dtype=np.int64)
@@ -190,7 +223,7 @@ def forward_block(M: OracleModel, kv: KVCache, tokens, L: int, trace: bool = Fal
         x = x + o.reshape(m, H * D) @ M[p + "wo"]
         h2 = nx.rmsnorm(x, M[p + "ffn_norm"], spec.rms_eps)
         if spec.n_experts > 0:
-            y, info = moe_ffn(M, l, h2, top_k)
+            y, info = moe_ffn(M, l, h2, top_k, reuse)
             routing.append(info)
             x = x + y
         else:

@@ -78,6 +78,9 @@ def _load():
         "spec_pass_bytes": (D, [P, I, I, I, ctypes.c_int64]),
         "spec_kv_poison_dead": (I, [P]),
         "spec_draft": (I, [P, I, I, I, ctypes.POINTER(ctypes.c_int32), P]),
+        "spec_adaptive_k": (I, [I, I, I]),
+        "spec_verify_step_reuse": (I, [P, ctypes.POINTER(ctypes.c_int32), I, I, P, P, P, I, F,
+                                       ctypes.POINTER(SpecStepResult), P, P, P]),
         "spec_verify_step_noalloc": (I, [P, ctypes.POINTER(ctypes.c_int32), I, I, P, P,
                                          ctypes.POINTER(SpecStepResult), P]),
     }
@@ -107,6 +110,8 @@ spec_profile_raw = lib.spec_profile_raw
 spec_pass_bytes = lib.spec_pass_bytes
 spec_kv_poison_dead = lib.spec_kv_poison_dead
 spec_draft = lib.spec_draft
+spec_adaptive_k = lib.spec_adaptive_k
+spec_verify_step_reuse = lib.spec_verify_step_reuse
 spec_verify_step_noalloc = lib.spec_verify_step_noalloc
 
 
@@ -224,6 +229,19 @@ class Verifier:
         if rc != SPEC_OK:
             raise SpecError(rc, self.last_error())
         return [int(x) for x in out]
+
+    def step_reuse(self, tokens: Sequence[int], cap: int, alpha: float, mode: int = SPEC_ACCEPT_GREEDY,
+                   q_ptr: int = 0, u_ptr: int = 0, conf_ptr: int = 0, logits_ptr: int = 0, union_ptr: int = 0,
+                   route_ptr: int = 0) -> SpecStepResult:
+        """Verification step with reuse-aware expert gating (lossy)."""
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        res = SpecStepResult()
+        rc = spec_verify_step_reuse(self.h, t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(t) - 1, mode,
+                                    q_ptr or None, u_ptr or None, conf_ptr or None, cap, alpha,
+                                    ctypes.byref(res), logits_ptr or None, union_ptr or None, route_ptr or None)
+        if rc != SPEC_OK:
+            raise SpecError(rc, self.last_error())
+        return res
 
     def rollback(self, new_len: int) -> None:
         rc = spec_kv_commit_rollback(self.h, new_len)

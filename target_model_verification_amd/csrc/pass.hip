@@ -1632,6 +1632,74 @@ __device__ __forceinline__ void router_logits(const PassP& P, const Mat& Mr, con
   __syncthreads();
 }
 
+// Reuse-aware gating (S2-MoE section 4.2; a lossy variant, off unless
+// asked for): the block's gating logits l_b (router logits with bias) give
+// each expert an importance g_e = sum_b w_b l_{b,e} (w_b the row's
+// confidence, rows in order); the cap experts of largest importance (ties to
+// the lower id) are preferred; every row b adds lambda_b = alpha (l_b(1) -
+// l_b(top_k+1)) -- the gap between its first and (top_k+1)-th logit -- to
+// the preferred experts' logits, and routing proceeds on the biased logits.
+// z holds this wave's rows (row = wave + kWaves k), experts lane + 64 i.
+template <int RPW, int EPL>
+__device__ __forceinline__ void reuse_bias(const PassP& P, float* zs, float* gs, int* pref, float* lam,
+                                           float (&z)[RPW][EPL]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = P.E;
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    const int row = wave + kWaves * k;
+    if (row < P.m) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + 64 * i < E) zs[row * E + lane + 64 * i] = z[k][i];
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) {
+    float g = 0.f;
+    for (int b = 0; b < P.m; ++b) g += (P.reuse_w ? P.reuse_w[b] : 1.f) * zs[b * E + e];
+    gs[e] = g;
+  }
+  // each row's first and (top_k+1)-th logit, by rank (lower id first on ties)
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    const int row = wave + kWaves * k;
+    if (row < P.m) {
+      const float* zr = zs + row * E;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E) {
+          const float ze = z[k][i];
+          int rank = 0;
+          for (int j = 0; j < E; ++j) rank += (zr[j] > ze || (zr[j] == ze && j < e)) ? 1 : 0;
+          if (rank == 0) lam[2 * row] = ze;
+          if (rank == P.top_k) lam[2 * row + 1] = ze;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += kThreads) {
+    const float ge = gs[e];
+    int rank = 0;
+    for (int j = 0; j < E; ++j) rank += (gs[j] > ge || (gs[j] == ge && j < e)) ? 1 : 0;
+    pref[e] = rank < P.reuse_cap ? 1 : 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    const int row = wave + kWaves * k;
+    if (row < P.m) {
+      const float lb = P.reuse_alpha * (lam[2 * row] - lam[2 * row + 1]);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + 64 * i < E && pref[lane + 64 * i]) z[k][i] += lb;
+    }
+  }
+  __syncthreads();   // zs / gs / pref / lam are dead (the probabilities reuse the space)
+}
+
 __device__ __forceinline__ void route_block(const PassP& P, const float* bias, unsigned char* smem, int layer,
                                             const float* zl) {
   Ctl* C = ctl(smem, (size_t)P.lds_bytes);
@@ -1657,16 +1725,25 @@ __device__ __forceinline__ void route_block(const PassP& P, const float* bias, u
   float bz[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) bz[i] = lane + 64 * i < P.E ? *glb(bias + lane + 64 * i) : 0.f;
+  // the gating logits (router logits with bias)
+#pragma unroll
+  for (int k = 0; k < RPW; ++k)
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) z[k][i] = lane + 64 * i < P.E ? z[k][i] + bz[i] : -INFINITY;
+  if (P.reuse_cap > 0) {
+    float* zs = prs;                          // [16][E] (before the probabilities are written)
+    float* gs = prs + 16 * 256;               // [E]
+    int* pref = reinterpret_cast<int*>(gs + 256);   // [E]
+    float* lam = gs + 512;                    // [16][2]
+    reuse_bias<RPW, EPL>(P, zs, gs, pref, lam, z);
+  }
   // softmax of every row, the rows' reductions side by side
   float mx[RPW], sum[RPW];
 #pragma unroll
   for (int k = 0; k < RPW; ++k) {
     mx[k] = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      z[k][i] = lane + 64 * i < P.E ? z[k][i] + bz[i] : -INFINITY;
-      mx[k] = fmaxf(mx[k], z[k][i]);
-    }
+    for (int i = 0; i < EPL; ++i) mx[k] = fmaxf(mx[k], z[k][i]);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1)
@@ -1934,7 +2011,7 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
 size_t pass_lds_bytes(int wfmt, int max_rows_attn, int D) {
   const size_t gemm = (size_t)kAWindowBytes + (wfmt == W_INT4 ? 16 * 16 * 4 : 0);   // + int4 row sums
   const size_t attn = attn_lds_bytes((max_rows_attn + 15) / 16, D);
-  const size_t route = 4 * (256 + 16 * 16 * 2 + 16 * 256);   // used, sel, selw, probabilities
+  const size_t route = 4 * (256 + 16 * 16 * 2 + 16 * 256 + 256 * 2 + 32);   // used, sel, selw, probabilities, reuse
   size_t b = gemm > attn ? gemm : attn;
   if (route > b) b = route;
   return b + kCtlBytes;

@@ -884,7 +884,8 @@ hipError_t launch_counted(spec_verify* h, const PassP& p) {
 
 int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, const float* q_dev,
               const float* u_dev, spec_step_result* out, float* logits_dev, float* trace_dev,
-              int32_t* union_dev, int32_t* route_dev, bool noalloc = false) {
+              int32_t* union_dev, int32_t* route_dev, bool noalloc = false, int reuse_cap = 0,
+              float reuse_alpha = 0.f, const float* reuse_w = nullptr) {
   if (!h) return SPEC_EINVAL;
   if (h->broken) return fail(h, SPEC_ESTATE, "handle unusable after an earlier GPU error");
   const spec_config& c = h->cfg;
@@ -910,6 +911,9 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   hipError_t he = hipMemcpyAsync(h->tokens_dev, h->tokens_host, sizeof(int32_t) * m, hipMemcpyHostToDevice,
                                  h->stream);
   PassP p = pass_params(h, m, L, h->tokens_dev, c.top_k);
+  p.reuse_cap = reuse_cap;
+  p.reuse_alpha = reuse_alpha;
+  p.reuse_w = reuse_w;
   if (noalloc) {
     // partials in the fixed scratch; its tickets start at zero
     p.ws_alt = static_cast<float*>(h->scratch);
@@ -1092,6 +1096,19 @@ int spec_verify_step_noalloc(spec_verify_t* h, const int32_t* tokens, int32_t k,
   return step_impl(h, tokens, k, mode, q_dev, u_dev, out, logits_dev, nullptr, nullptr, nullptr, true);
 }
 
+int spec_verify_step_reuse(spec_verify_t* h, const int32_t* tokens, int32_t k, int32_t mode, const float* q_dev,
+                           const float* u_dev, const float* conf_dev, int32_t cap, float alpha,
+                           spec_step_result* out, float* logits_dev, int32_t* union_dev, int32_t* route_dev) {
+  if (!h) return SPEC_EINVAL;
+  const spec_config& c = h->cfg;
+  if (c.n_experts <= 0) return fail(h, SPEC_EINVAL, "reuse-aware gating needs a MoE model");
+  if (c.top_k >= c.n_experts) return fail(h, SPEC_EINVAL, "reuse-aware gating needs top_k < n_experts");
+  if (cap < c.top_k || cap > c.n_experts) return fail(h, SPEC_EINVAL, "cap must be in [top_k, n_experts]");
+  if (!(alpha >= 0.f) || !(alpha <= 1e6f)) return fail(h, SPEC_EINVAL, "alpha must be finite and >= 0");
+  return step_impl(h, tokens, k, mode, q_dev, u_dev, out, logits_dev, nullptr, union_dev, route_dev, false, cap,
+                   alpha, conf_dev);
+}
+
 int spec_verify_step_debug(spec_verify_t* h, const int32_t* tokens, int32_t k, int32_t mode,
                            const float* q_dev, const float* u_dev, spec_step_result* out, float* logits_dev,
                            float* trace_dev, int32_t* union_dev, int32_t* route_dev) {
@@ -1160,6 +1177,12 @@ int spec_kv_commit_rollback(spec_verify_t* h, int32_t new_kv_len) {
 }
 
 int32_t spec_kv_len(const spec_verify_t* h) { return h ? h->kv_len : -1; }
+
+int32_t spec_adaptive_k(int32_t k, int32_t n_accepted, int32_t max_k) {
+  if (max_k < 1 || k < 1 || k > max_k || n_accepted < 0 || n_accepted > k) return -1;
+  if (n_accepted == k) return k + 2 < max_k ? k + 2 : max_k;   // the whole block passed: look further
+  return k - 1 > 1 ? k - 1 : 1;                               // a draft failed: back off by one
+}
 
 int spec_kv_poison_dead(spec_verify_t* h) {
   if (!h) return SPEC_EINVAL;

@@ -136,6 +136,11 @@ struct PassP {
   float* trace;              // [n_layers][m][d]
   int* union_hist;           // [n_layers]
   int* route_hist;           // [n_layers][m][top_k] experts selected by each row, in rank order
+  // reuse-aware gating (lossy; reuse_cap 0 = off): per layer the cap experts
+  // with the largest confidence-weighted sum of the block's gating logits
+  // get a per-row bias reuse_alpha * (top-1 logit - (top_k+1)-th logit)
+  int reuse_cap; float reuse_alpha;
+  const float* reuse_w;      // [m] row confidences (null: 1)
   unsigned long long* stamps;   // [n_phases + 1] wall clock at phase ends (workgroup 0)
   unsigned long long* wstamps;  // [n_phases][n_wg][4] per-workgroup phase stamps (nullable)
 };

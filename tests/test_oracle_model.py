@@ -163,3 +163,57 @@ def test_sparse_draft_is_its_own_model():
     res = om.forward_block(M, scratch, [pending] + list(toks[:-1]), kv.length, top_k=1)
     assert list(np.argmax(res.logits, axis=-1)) == list(toks)
     assert np.max(np.abs(res.logits - logits)) < 1e-9
+
+
+def test_reuse_gating_hand_worked():
+    """Reuse-aware gating (S2-MoE section 4.2) on a 3-token, 6-expert block,
+    top_k = 2, cap = 3, alpha = 0.5, unit confidences, worked by hand:
+    importances g = (4, 3, 4, 3.6, -0.5, 1.5) prefer experts {0, 2, 3} (the
+    tie 0/2 to the lower id first); the rows' first-minus-third logit gaps
+    (2, 1, 2) give biases (1, 0.5, 1); row 2's second expert moves from 5 to
+    the preferred 0 (a tie 2.0/2.0 broken to the lower id), so the block's
+    union shrinks from five experts to four."""
+    r = np.array([[3, 1, 0, 2, -1, 0.5], [0, 2, 1, 1.5, 0.2, -1], [1, 0, 3, 0.1, 0.3, 2]], float)
+    rb, pref, cap_gap = om.reuse_gating_logits(r, np.ones(3), 2, 3, 0.5)
+    assert list(pref) == [True, False, True, True, False, False]
+    assert cap_gap == pytest.approx(3.6 - 3.0)
+    want = np.array([[4, 1, 1, 3, -1, 0.5], [0.5, 2, 1.5, 2.0, 0.2, -1], [2, 0, 4, 1.1, 0.3, 2]])
+    assert np.allclose(rb, want, atol=1e-12)
+    top2 = lambda x: [int(e) for e in np.argsort(-x, kind="stable")[:2]]
+    assert [top2(x) for x in r] == [[0, 3], [1, 3], [2, 5]]
+    assert [top2(x) for x in rb] == [[0, 3], [1, 3], [2, 0]]
+
+
+@pytest.mark.parametrize("alpha,cap", [(0.0, 10), (0.7, 16)])
+def test_reuse_gating_special_cases_are_exact(alpha, cap):
+    """alpha = 0 adds nothing (bitwise the exact target); cap = every expert
+    shifts a row's logits uniformly, which leaves softmax and top-k routing
+    unchanged (the exact target up to rounding)."""
+    wl, W, M = _model("small_moe")
+    kv, last = om.prefill(M, synth.prompt_ids(wl, 30), 60)
+    toks = [int(np.argmax(last))] + list(synth.prompt_ids(wl, 39)[30:])
+    ref = om.forward_block(M, kv.copy(), toks, 30)
+    w = np.linspace(0.2, 1.0, len(toks))
+    got = om.forward_block(M, kv.copy(), toks, 30, reuse=(w, cap, alpha))
+    if alpha == 0.0:
+        assert np.array_equal(got.logits, ref.logits)
+    else:
+        assert np.max(np.abs(got.logits - ref.logits)) < 1e-10
+    for a, b in zip(got.routing, ref.routing):
+        assert np.array_equal(a["sel"], b["sel"])
+
+
+def test_reuse_gating_shrinks_the_union():
+    """With a strong bias the block's experts concentrate on the preferred
+    set: over random blocks the mean union is smaller than the exact one,
+    and never larger than cap plus the rows' unbiased picks allow."""
+    wl, W, M = _model("small_moe")
+    rng = np.random.default_rng(5)
+    exact, reuse = [], []
+    for t in range(6):
+        h = rng.standard_normal((9, wl.spec.d_model))
+        _, a = om.moe_ffn(M, 0, h)
+        _, b = om.moe_ffn(M, 0, h, reuse=(np.ones(9), 8, 1.0))
+        exact.append(len(a["union"]))
+        reuse.append(len(b["union"]))
+    assert np.mean(reuse) < np.mean(exact)

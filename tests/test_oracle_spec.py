@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 from oracle import accept as oa
+from oracle import accounting as oacc_k
 from oracle import model as om
 from spec_harness import (greedy_round_inputs, oracle_greedy_rounds, oracle_step, prepare,
                           stochastic_round_inputs)
@@ -90,3 +91,35 @@ def test_stochastic_rounds_bookkeeping_and_noiseless_draft():
     u = np.full(k + 1, 0.5)
     o = oa.accept_stochastic(res.logits, np.stack(qs), toks[1:], u, L)
     assert o.n_accepted == k
+
+
+def test_adaptive_k_schedule_hand_worked():
+    """The essay's description worked by hand: start at 5; full accept -> 7;
+    full accept -> 9; 3 of 9 accepted -> 8; none -> 7; full accept -> 9;
+    full accept -> 11, capped at the verifier's 10; partial -> 9.  Back-off
+    never goes below 1."""
+    ks = oacc_k.adaptive_k_schedule(5, [5, 7, 3, 0, 7, 9, 4], 10)
+    assert ks == [5, 7, 9, 8, 7, 9, 10, 9]
+    assert oacc_k.adaptive_k_schedule(1, [0, 0, 1], 15) == [1, 1, 1, 3]
+    with pytest.raises(ValueError):
+        oacc_k.adaptive_k_schedule(3, [4], 15)
+
+
+def test_library_adaptive_k_matches_the_schedule():
+    """spec_adaptive_k (host code of the library) follows the same rule on
+    random accept sequences, and rejects arguments outside its domain."""
+    import random
+    from target_model_verification_amd import binding as b
+    rng = random.Random(3)
+    for _ in range(200):
+        max_k = rng.randint(1, 15)
+        k = rng.randint(1, max_k)
+        seq = []
+        ks = [k]
+        for _ in range(20):
+            n = rng.choice([ks[-1], rng.randint(0, ks[-1])])
+            seq.append(n)
+            ks.append(b.spec_adaptive_k(ks[-1], n, max_k))
+        assert ks == oacc_k.adaptive_k_schedule(k, seq, max_k)
+    assert b.spec_adaptive_k(0, 0, 5) == -1 and b.spec_adaptive_k(6, 0, 5) == -1
+    assert b.spec_adaptive_k(3, 4, 5) == -1 and b.spec_adaptive_k(1, 0, 0) == -1
