@@ -187,6 +187,30 @@ int spec_verify_step_noalloc(spec_verify_t* h, const int32_t* tokens, int32_t k,
                              const float* q_dev, const float* u_dev, spec_step_result* out,
                              float* logits_dev);
 
+/* Verification of a token tree (S2-MoE section 4.1: drafts expanded as a
+ * tree, each candidate verified in the same pass).  Row 0 is the pending
+ * token (the root, parents[0] = -1); row i > 0 is a draft token whose parent
+ * row parents[i] precedes it (0 <= parents[i] < i).  One target pass scores
+ * every row: row i sits at position kv_len + depth(i) and attends to the
+ * committed cache and to its ancestors (and itself) only, so its logits are
+ * those the target writes after the path root..i.  Greedy acceptance walks
+ * down from the root: while the argmax of the current row (lowest id on
+ * ties) is the token of one of its children (the lowest-numbered such child
+ * if several), that child is accepted and becomes current; next_token is
+ * the argmax of the last current row (a correction, or the bonus token at a
+ * leaf).  The cache keeps the pending token and the accepted path at
+ * positions kv_len .. kv_len + n_accepted (their entries are moved there
+ * from the rows' block slots); everything after is dead.
+ *   tokens, parents: host int32 [m], 1 <= m <= max_k + 1.
+ *   out:   n_accepted = length of the accepted path, next_token, kv_len =
+ *          old kv_len + 1 + n_accepted.
+ *   path:  host int32 [m] receiving the accepted rows in order (root
+ *          excluded; n_accepted entries).
+ *   logits_dev: NULL or device fp32 [m][vocab].
+ * Errors as in spec_verify_step (SPEC_EINVAL for a malformed tree). */
+int spec_verify_tree(spec_verify_t* h, const int32_t* tokens, const int32_t* parents, int32_t m,
+                     spec_step_result* out, int32_t* path, float* logits_dev);
+
 /* Self-speculative draft of a MoE target by expert sparsity (S2-MoE,
  * section 2.3 and section 5 "Draft configuration", Table 1: the draft is
  * the target itself with fewer routed experts per token; section 4.3: the
@@ -208,11 +232,40 @@ int spec_verify_step_noalloc(spec_verify_t* h, const int32_t* tokens, int32_t k,
  *   logits_dev:  NULL or device fp32 [n][vocab] receiving each draft pass's
  *                logits (the draft distributions for stochastic acceptance
  *                are their softmax).
+ *   route_dev:   NULL or device int32 [n][n_layers][draft_top_k] receiving
+ *                the experts each draft pass routed its token to, per
+ *                layer, in rank order (probability descending, lower id
+ *                first on ties).
  * Requires kv_len + n <= max_ctx (else SPEC_ECAPACITY).  The committed
  * length does not change: the draft's cache entries at kv_len .. kv_len+n-1
  * are dead, and the verification step that follows overwrites them. */
 int spec_draft(spec_verify_t* h, int32_t pending, int32_t n, int32_t draft_top_k, int32_t* drafts,
-               float* logits_dev);
+               float* logits_dev, int32_t* route_dev);
+
+/* Routing-aware adaptive expansion of a draft tree (S2-MoE section 4.1;
+ * host policy, no device work).  Candidate i (0 <= i < n) has a parent
+ * parents[i] (-1: a child of the root, else an earlier candidate), the draft
+ * probability p[i] in [0, 1] of its token given its parent, a drafting cost
+ * c_draft[i] >= 0, and the experts verifying it would activate: ids
+ * exp_ids[exp_offsets[i] .. exp_offsets[i+1]) (any non-negative ids, e.g.
+ * layer * n_experts + expert; duplicates count once).  Its prefix
+ * confidence P_i is the product of p along its path from the root, its
+ * expected benefit P_i * t_ar (t_ar: one target decoding step), its cost
+ * the number of its experts not yet active times t_exp (one expert's
+ * verification cost) plus c_draft[i], and its utility U_i = benefit / cost
+ * (infinite for a zero cost and positive benefit, 0 for a zero benefit).
+ * Starting from the active set base_ids [n_base], each round admits the
+ * candidate of highest U_i (lowest index on ties) among those whose parent
+ * is the root or already admitted, provided U_i >= 1, and adds its experts
+ * to the active set; it stops when the best U_i < 1 or max_nodes are
+ * admitted.  Writes the admitted candidates in admission order to order
+ * [max_nodes] and, when row_parents [max_nodes + 1] is not NULL, the parent
+ * rows of the verification tree whose row 0 is the root and row r the
+ * candidate admitted r-th (ready for spec_verify_tree).  Returns the
+ * number admitted, or -1 for invalid arguments. */
+int32_t spec_tree_expand(int32_t n, const int32_t* parents, const double* p, const int32_t* exp_offsets,
+                         const int32_t* exp_ids, int32_t n_base, const int32_t* base_ids, double t_ar, double t_exp,
+                         const double* c_draft, int32_t max_nodes, int32_t* order, int32_t* row_parents);
 
 /* Lossy variant of spec_verify_step with reuse-aware expert gating (S2-MoE
  * section 4.2): in every MoE layer the block's rows steer their routing

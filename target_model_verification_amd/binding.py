@@ -77,8 +77,14 @@ def _load():
         "spec_profile_raw": (I, [P, ctypes.POINTER(ctypes.c_uint64), ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]),
         "spec_pass_bytes": (D, [P, I, I, I, ctypes.c_int64]),
         "spec_kv_poison_dead": (I, [P]),
-        "spec_draft": (I, [P, I, I, I, ctypes.POINTER(ctypes.c_int32), P]),
+        "spec_draft": (I, [P, I, I, I, ctypes.POINTER(ctypes.c_int32), P, P]),
+        "spec_tree_expand": (I, [I, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(D), ctypes.POINTER(ctypes.c_int32),
+                                 ctypes.POINTER(ctypes.c_int32), I, ctypes.POINTER(ctypes.c_int32), D, D,
+                                 ctypes.POINTER(D), I, ctypes.POINTER(ctypes.c_int32),
+                                 ctypes.POINTER(ctypes.c_int32)]),
         "spec_adaptive_k": (I, [I, I, I]),
+        "spec_verify_tree": (I, [P, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), I,
+                                 ctypes.POINTER(SpecStepResult), ctypes.POINTER(ctypes.c_int32), P]),
         "spec_verify_step_reuse": (I, [P, ctypes.POINTER(ctypes.c_int32), I, I, P, P, P, I, F,
                                        ctypes.POINTER(SpecStepResult), P, P, P]),
         "spec_verify_step_noalloc": (I, [P, ctypes.POINTER(ctypes.c_int32), I, I, P, P,
@@ -111,6 +117,8 @@ spec_pass_bytes = lib.spec_pass_bytes
 spec_kv_poison_dead = lib.spec_kv_poison_dead
 spec_draft = lib.spec_draft
 spec_adaptive_k = lib.spec_adaptive_k
+spec_verify_tree = lib.spec_verify_tree
+spec_tree_expand = lib.spec_tree_expand
 spec_verify_step_reuse = lib.spec_verify_step_reuse
 spec_verify_step_noalloc = lib.spec_verify_step_noalloc
 
@@ -222,10 +230,10 @@ class Verifier:
             raise SpecError(rc, self.last_error())
         return res
 
-    def draft(self, pending: int, n: int, draft_top_k: int, logits_ptr: int = 0) -> List[int]:
+    def draft(self, pending: int, n: int, draft_top_k: int, logits_ptr: int = 0, route_ptr: int = 0) -> List[int]:
         """Self-speculative draft tokens d_1..d_n (spec_draft)."""
         out = (ctypes.c_int32 * n)()
-        rc = spec_draft(self.h, int(pending), int(n), int(draft_top_k), out, logits_ptr or None)
+        rc = spec_draft(self.h, int(pending), int(n), int(draft_top_k), out, logits_ptr or None, route_ptr or None)
         if rc != SPEC_OK:
             raise SpecError(rc, self.last_error())
         return [int(x) for x in out]
@@ -242,6 +250,19 @@ class Verifier:
         if rc != SPEC_OK:
             raise SpecError(rc, self.last_error())
         return res
+
+    def step_tree(self, tokens: Sequence[int], parents: Sequence[int], logits_ptr: int = 0):
+        """Token-tree verification (greedy): (result, accepted rows)."""
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        pa = np.ascontiguousarray(np.asarray(parents, dtype=np.int32))
+        res = SpecStepResult()
+        path = (ctypes.c_int32 * len(t))()
+        rc = spec_verify_tree(self.h, t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                              pa.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), len(t), ctypes.byref(res), path,
+                              logits_ptr or None)
+        if rc != SPEC_OK:
+            raise SpecError(rc, self.last_error())
+        return res, [int(path[i]) for i in range(res.n_accepted)]
 
     def rollback(self, new_len: int) -> None:
         rc = spec_kv_commit_rollback(self.h, new_len)
@@ -306,3 +327,24 @@ class Verifier:
             self.close()
         except Exception:
             pass
+
+
+def tree_expand(parents, p, experts, base, t_ar: float, t_exp: float, c_draft, max_nodes: int):
+    """spec_tree_expand on Python lists: (admitted candidates in order,
+    parent rows of the verification tree)."""
+    n = len(parents)
+    i32 = lambda a: np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    f64 = lambda a: np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    off = i32(np.concatenate([[0], np.cumsum([len(e) for e in experts])]) if n else [0])
+    ids = i32([e for ex in experts for e in ex] or [0])
+    pa, pp, cd, bs = i32(parents if n else [0]), f64(p if n else [0]), f64(c_draft if n else [0]), i32(list(base) or [0])
+    order = (ctypes.c_int32 * max(max_nodes, 1))()
+    rows = (ctypes.c_int32 * (max_nodes + 1))()
+    P32 = ctypes.POINTER(ctypes.c_int32)
+    PD = ctypes.POINTER(ctypes.c_double)
+    cnt = spec_tree_expand(n, pa.ctypes.data_as(P32), pp.ctypes.data_as(PD), off.ctypes.data_as(P32),
+                           ids.ctypes.data_as(P32), len(base), bs.ctypes.data_as(P32), float(t_ar), float(t_exp),
+                           cd.ctypes.data_as(PD), int(max_nodes), order, rows)
+    if cnt < 0:
+        raise ValueError("spec_tree_expand: invalid arguments")
+    return [int(order[i]) for i in range(cnt)], [int(rows[i]) for i in range(cnt + 1)]

@@ -65,6 +65,24 @@ __global__ __launch_bounds__(1024) void k_accept(AcceptParams p) {
     if (lane == 0) { amax[w] = I; rowM[w] = M; rowS[w] = S; }
   }
   __syncthreads();
+  if (p.mode == kAcceptTree) {     // greedy walk down a token tree
+    if (tid == 0) {
+      int cur = 0, n = 0;
+      for (;;) {
+        const int a = amax[cur];
+        int c = -1;
+        for (int i = cur + 1; i < m; ++i)
+          if (p.parents[i] == cur && p.tokens[i] == a) { c = i; break; }   // lowest-numbered matching child
+        if (c < 0) break;
+        p.path[n++] = c;
+        cur = c;
+      }
+      p.result[0] = n;
+      p.result[1] = amax[cur];
+      p.result[2] = p.L + 1 + n;
+    }
+    return;
+  }
   if (p.mode != 1) {               // greedy / none
     if (tid == 0) {
       int n = 0;

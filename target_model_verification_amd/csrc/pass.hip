@@ -418,10 +418,12 @@ __device__ __forceinline__ void qkv_pre(const PassP& P, int unit, QkvPre& q) {
   const int ii = (c2 % D) >> 1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int t = P.L + min(4 * rg + i, P.m - 1);
+    const int row = min(4 * rg + i, P.m - 1);
+    const int t = P.L + row;                                           // cache slot
+    const int tp = P.tree_pos ? P.L + P.tree_pos[row] : t;             // rotary position
     q.pg[i] = (long long)P.page_table[t / kPage] * P.Hkv;
-    q.cs[i] = rot_col ? P.rope_cs[((long long)t * H + ii) * 2 + 0] : 0.f;
-    q.sn[i] = rot_col ? P.rope_cs[((long long)t * H + ii) * 2 + 1] : 0.f;
+    q.cs[i] = rot_col ? P.rope_cs[((long long)tp * H + ii) * 2 + 0] : 0.f;
+    q.sn[i] = rot_col ? P.rope_cs[((long long)tp * H + ii) * 2 + 1] : 0.f;
   }
 }
 
@@ -1305,7 +1307,12 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = rb + rt * 16 + 4 * (lane >> 4) + i;
-        const bool vis = r < R && key < nkeys && tk <= P.L + r / P.G;
+        // causal: block row j sees positions up to L + j; a token tree: the
+        // committed cache and the rows of its ancestor mask
+        bool seen = tk <= P.L + r / P.G;
+        if (P.tree_anc && tk >= P.L && tk - P.L < kMaxRows && r < R)
+          seen = ((P.tree_anc[r / P.G] >> (tk - P.L)) & 1u) != 0u;
+        const bool vis = r < R && key < nkeys && seen;
         s4[i] = vis ? s4[i] : -INFINITY;
       }
       return s4;

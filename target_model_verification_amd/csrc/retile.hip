@@ -173,6 +173,49 @@ __global__ void k_kv_poison(T* __restrict__ base, long long layer_elems, int n_l
   }
 }
 
+// Cache entries of the accepted token-tree rows moved to consecutive slots:
+// row path[j] (slot L + path[j]) -> slot L + 1 + j, keys and values of one
+// (layer, KV head) per workgroup.  The path increases, so a destination can
+// be the source of an earlier move only; every source element is read into
+// registers before any write (at most 15 rows x 2 x 128 elements per 256
+// threads).
+template <typename T>
+__global__ void k_tree_commit(T* __restrict__ base, long long layer_elems, int Hkv, int D,
+                              const int* __restrict__ pt, int L, const int* __restrict__ result,
+                              const int* __restrict__ path) {
+  const int l = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
+  const int n = result[0];
+  T* lb = base + (long long)l * layer_elems;
+  constexpr int kMaxEl = 16 * 2 * 128 / 256;   // rows x (key + value) x head_dim per thread
+  T v[kMaxEl];
+  long long dst[kMaxEl];
+  int cnt = 0;
+  for (int e = threadIdx.x; e < n * 2 * D; e += blockDim.x) {
+    const int j = e / (2 * D), r = e % (2 * D), sel = r / D, d = r % D;
+    const int ts = L + path[j], td = L + 1 + j;
+    const long long bs = (((long long)pt[ts / kPage] * Hkv + g) * 2 + sel) * kPage * D;
+    const long long bd = (((long long)pt[td / kPage] * Hkv + g) * 2 + sel) * kPage * D;
+    const long long os = sel == 0 ? (long long)(ts % kPage) * D + d : (long long)d * kPage + (ts % kPage);
+    const long long od = sel == 0 ? (long long)(td % kPage) * D + d : (long long)d * kPage + (td % kPage);
+    v[cnt] = lb[bs + os];
+    dst[cnt] = bd + od;
+    ++cnt;
+  }
+  __syncthreads();
+  for (int i = 0; i < cnt; ++i) lb[dst[i]] = v[i];
+}
+
+hipError_t launch_tree_commit(int kv_f32, void* base, long long layer_elems, int n_layers, int Hkv, int D,
+                              const int* pt, int L, const int* result, const int* path, hipStream_t s) {
+  if (kv_f32)
+    hipLaunchKernelGGL(k_tree_commit<float>, dim3(n_layers * Hkv), dim3(256), 0, s, static_cast<float*>(base),
+                       layer_elems, Hkv, D, pt, L, result, path);
+  else
+    hipLaunchKernelGGL(k_tree_commit<uint16_t>, dim3(n_layers * Hkv), dim3(256), 0, s,
+                       static_cast<uint16_t*>(base), layer_elems, Hkv, D, pt, L, result, path);
+  return hipGetLastError();
+}
+
 hipError_t launch_kv_poison(int kv_f32, void* base, long long layer_elems, int n_layers, int Hkv, int D,
                             const int* pt, int from, int to, hipStream_t s) {
   if (to <= from) return hipSuccess;

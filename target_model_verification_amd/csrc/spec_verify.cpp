@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <iterator>
 #include <map>
 #include <string>
 #include <tuple>
@@ -90,6 +91,8 @@ struct spec_verify {
   int* tokens_host = nullptr;   // pinned
   int* result_host = nullptr;   // pinned
   int* draft_res = nullptr;     // self-speculative draft: [kMaxRows][4] acceptance records (device)
+  int* tree_dev = nullptr;      // token tree: parents [16], depths [16], ancestor masks [16], path [16]
+  int* tree_host = nullptr;     // pinned staging of the tree arrays and the returned path
   int* draft_host = nullptr;    // pinned copy of draft_res and the error flag
   // the pass program
   Phase* prog = nullptr;
@@ -677,6 +680,8 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->tokens_host), 16 * sizeof(int), hipHostMallocDefault));
   HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->result_host), 4 * sizeof(int), hipHostMallocDefault));
   if ((rc = dalloc_z(h, &h->draft_res, (size_t)kMaxRows * 4))) return rc;
+  if ((rc = dalloc_z(h, &h->tree_dev, (size_t)kMaxRows * 4))) return rc;
+  HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->tree_host), kMaxRows * 4 * sizeof(int), hipHostMallocDefault));
   HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->draft_host), (kMaxRows * 4 + 4) * sizeof(int),
                        hipHostMallocDefault));
 
@@ -810,6 +815,7 @@ void free_all(spec_verify* h) {
   if (h->tokens_host) (void)hipHostFree(h->tokens_host);
   if (h->result_host) (void)hipHostFree(h->result_host);
   if (h->draft_host) (void)hipHostFree(h->draft_host);
+  if (h->tree_host) (void)hipHostFree(h->tree_host);
   for (auto& e : h->ev)
     if (e) (void)hipEventDestroy(e);
 }
@@ -1115,8 +1121,74 @@ int spec_verify_step_debug(spec_verify_t* h, const int32_t* tokens, int32_t k, i
   return step_impl(h, tokens, k, mode, q_dev, u_dev, out, logits_dev, trace_dev, union_dev, route_dev);
 }
 
+int spec_verify_tree(spec_verify_t* h, const int32_t* tokens, const int32_t* parents, int32_t m,
+                     spec_step_result* out, int32_t* path, float* logits_dev) {
+  if (!h) return SPEC_EINVAL;
+  if (h->broken) return fail(h, SPEC_ESTATE, "handle unusable after an earlier GPU error");
+  const spec_config& c = h->cfg;
+  if (!tokens || !parents || !out || !path) return fail(h, SPEC_EINVAL, "tokens, parents, out and path are required");
+  if (m < 1 || m > c.max_k + 1) return fail(h, SPEC_EINVAL, "m must be in [1, max_k + 1]");
+  for (int i = 0; i < m; ++i)
+    if (tokens[i] < 0 || tokens[i] >= c.vocab) return fail(h, SPEC_EINVAL, "token id out of range");
+  if (parents[0] != -1) return fail(h, SPEC_EINVAL, "row 0 (the pending token) is the root: parents[0] must be -1");
+  int* depth = h->tree_host + kMaxRows;
+  unsigned* anc = reinterpret_cast<unsigned*>(h->tree_host + 2 * kMaxRows);
+  depth[0] = 0;
+  anc[0] = 1u;
+  for (int i = 1; i < m; ++i) {
+    if (parents[i] < 0 || parents[i] >= i) return fail(h, SPEC_EINVAL, "every parent must precede its row");
+    depth[i] = depth[parents[i]] + 1;
+    anc[i] = anc[parents[i]] | (1u << i);
+  }
+  const int L = h->kv_len;
+  if ((long long)L + m > c.max_ctx) return fail(h, SPEC_ECAPACITY, "block exceeds max_ctx");
+  std::memcpy(h->tree_host, parents, sizeof(int32_t) * m);
+  std::memcpy(h->tokens_host, tokens, sizeof(int32_t) * m);
+  hipError_t he = hipMemcpyAsync(h->tokens_dev, h->tokens_host, sizeof(int32_t) * m, hipMemcpyHostToDevice, h->stream);
+  if (he == hipSuccess)
+    he = hipMemcpyAsync(h->tree_dev, h->tree_host, sizeof(int) * 3 * kMaxRows, hipMemcpyHostToDevice, h->stream);
+  PassP p = pass_params(h, m, L, h->tokens_dev, c.top_k);
+  p.tree_pos = h->tree_dev + kMaxRows;
+  p.tree_anc = reinterpret_cast<const unsigned*>(h->tree_dev + 2 * kMaxRows);
+  if (he == hipSuccess) he = launch_counted(h, p);
+  AcceptParams a{};
+  a.k = m - 1; a.V = c.vocab; a.L = L; a.mode = kAcceptTree; a.n_stat = h->n_stat;
+  a.tokens = h->tokens_dev; a.parents = h->tree_dev; a.path = h->tree_dev + 3 * kMaxRows;
+  a.st_max = h->st_max; a.st_sum = h->st_sum; a.st_idx = h->st_idx;
+  a.logits = h->logits; a.ldl = h->ldl;
+  a.result = h->result_dev;
+  if (he == hipSuccess) he = launch_accept(a, h->stream);
+  // the accepted rows' cache entries to consecutive slots after the pending token's
+  if (he == hipSuccess)
+    he = launch_tree_commit(c.kv_dtype == SPEC_DT_F32, h->kv, h->kv_layer_elems, c.n_layers, c.n_kv_heads, c.head_dim,
+                            h->page_table, L, h->result_dev, a.path, h->stream);
+  if (he == hipSuccess)
+    he = hipMemcpyAsync(h->result_host, h->result_dev, 4 * sizeof(int), hipMemcpyDeviceToHost, h->stream);
+  if (he == hipSuccess)
+    he = hipMemcpyAsync(h->tree_host + 3 * kMaxRows, a.path, kMaxRows * sizeof(int), hipMemcpyDeviceToHost, h->stream);
+  if (he == hipSuccess && logits_dev)
+    he = hipMemcpy2DAsync(logits_dev, (size_t)c.vocab * 4, h->logits, (size_t)h->ldl * 4, (size_t)c.vocab * 4, m,
+                          hipMemcpyDeviceToDevice, h->stream);
+  if (he == hipSuccess) he = hipStreamSynchronize(h->stream);
+  if (he != hipSuccess) {
+    h->broken = true;
+    return fail(h, SPEC_EHIP, std::string("tree step: ") + hipGetErrorString(he));
+  }
+  if (h->result_host[3] != 0) {
+    h->broken = true;
+    return fail(h, SPEC_EHIP, "grid barrier wait timed out inside the pass");
+  }
+  out->n_accepted = h->result_host[0];
+  out->next_token = h->result_host[1];
+  out->kv_len = h->result_host[2];
+  for (int i = 0; i < out->n_accepted; ++i) path[i] = h->tree_host[3 * kMaxRows + i];
+  h->kv_len = out->kv_len;
+  h->err.clear();
+  return SPEC_OK;
+}
+
 int spec_draft(spec_verify_t* h, int32_t pending, int32_t n, int32_t draft_top_k, int32_t* drafts,
-               float* logits_dev) {
+               float* logits_dev, int32_t* route_dev) {
   if (!h) return SPEC_EINVAL;
   if (h->broken) return fail(h, SPEC_ESTATE, "handle unusable after an earlier GPU error");
   const spec_config& c = h->cfg;
@@ -1133,7 +1205,8 @@ int spec_draft(spec_verify_t* h, int32_t pending, int32_t n, int32_t draft_top_k
   // chaining: no host round trip between draft tokens)
   for (int i = 0; i < n && he == hipSuccess; ++i) {
     const int* tok = i == 0 ? h->tokens_dev : h->draft_res + 4 * (i - 1) + 1;
-    const PassP p = pass_params(h, 1, L0 + i, tok, draft_top_k);
+    PassP p = pass_params(h, 1, L0 + i, tok, draft_top_k);
+    if (route_dev) p.route_hist = route_dev + (long long)i * c.n_layers * draft_top_k;
     he = launch_counted(h, p);
     AcceptParams a{};
     a.k = 0; a.V = c.vocab; a.L = L0 + i; a.mode = SPEC_ACCEPT_NONE; a.n_stat = h->n_stat;
@@ -1177,6 +1250,66 @@ int spec_kv_commit_rollback(spec_verify_t* h, int32_t new_kv_len) {
 }
 
 int32_t spec_kv_len(const spec_verify_t* h) { return h ? h->kv_len : -1; }
+
+int32_t spec_tree_expand(int32_t n, const int32_t* parents, const double* p, const int32_t* exp_offsets,
+                         const int32_t* exp_ids, int32_t n_base, const int32_t* base_ids, double t_ar, double t_exp,
+                         const double* c_draft, int32_t max_nodes, int32_t* order, int32_t* row_parents) {
+#pragma clang fp contract(off)   // the utilities are compared exactly: plain products and sums
+  if (n < 0 || n_base < 0 || max_nodes < 0) return -1;
+  if (n > 0 && (!parents || !p || !exp_offsets || !c_draft)) return -1;
+  if (n_base > 0 && !base_ids) return -1;
+  if (max_nodes > 0 && !order) return -1;
+  if (!(t_ar >= 0.0) || !(t_exp >= 0.0) || !std::isfinite(t_ar) || !std::isfinite(t_exp)) return -1;
+  if (n > 0 && exp_offsets[0] != 0) return -1;
+  std::vector<std::vector<int32_t>> ex(n);
+  std::vector<double> conf(n);
+  for (int i = 0; i < n; ++i) {
+    if (parents[i] < -1 || parents[i] >= i) return -1;
+    if (!(p[i] >= 0.0 && p[i] <= 1.0) || !(c_draft[i] >= 0.0) || !std::isfinite(c_draft[i])) return -1;
+    if (exp_offsets[i + 1] < exp_offsets[i] || (exp_offsets[i + 1] > exp_offsets[i] && !exp_ids)) return -1;
+    for (int j = exp_offsets[i]; j < exp_offsets[i + 1]; ++j) {
+      if (exp_ids[j] < 0) return -1;
+      ex[i].push_back(exp_ids[j]);
+    }
+    std::sort(ex[i].begin(), ex[i].end());
+    ex[i].erase(std::unique(ex[i].begin(), ex[i].end()), ex[i].end());
+    // prefix confidence: the product of the draft probabilities root..i
+    conf[i] = parents[i] < 0 ? p[i] : conf[parents[i]] * p[i];
+  }
+  std::vector<int32_t> active;
+  for (int j = 0; j < n_base; ++j) {
+    if (base_ids[j] < 0) return -1;
+    active.push_back(base_ids[j]);
+  }
+  std::sort(active.begin(), active.end());
+  active.erase(std::unique(active.begin(), active.end()), active.end());
+  std::vector<char> taken(n, 0);
+  std::vector<int32_t> row(n, -1);
+  int cnt = 0;
+  while (cnt < max_nodes) {
+    int best = -1;
+    double best_u = -1.0;
+    for (int i = 0; i < n; ++i) {
+      if (taken[i] || (parents[i] >= 0 && !taken[parents[i]])) continue;
+      int fresh = 0;   // experts verifying i would activate beyond the admitted set's
+      for (int32_t e : ex[i]) fresh += !std::binary_search(active.begin(), active.end(), e);
+      const double benefit = conf[i] * t_ar;
+      const double cost = (double)fresh * t_exp + c_draft[i];
+      const double u = benefit <= 0.0 ? 0.0 : (cost <= 0.0 ? INFINITY : benefit / cost);
+      if (u > best_u) { best = i; best_u = u; }
+    }
+    if (best < 0 || best_u < 1.0) break;
+    taken[best] = 1;
+    row[best] = cnt + 1;
+    if (row_parents) row_parents[cnt + 1] = parents[best] < 0 ? 0 : row[parents[best]];
+    order[cnt++] = best;
+    std::vector<int32_t> merged;
+    std::set_union(active.begin(), active.end(), ex[best].begin(), ex[best].end(), std::back_inserter(merged));
+    active.swap(merged);
+  }
+  if (row_parents) row_parents[0] = -1;
+  return cnt;
+}
 
 int32_t spec_adaptive_k(int32_t k, int32_t n_accepted, int32_t max_k) {
   if (max_k < 1 || k < 1 || k > max_k || n_accepted < 0 || n_accepted > k) return -1;

@@ -141,6 +141,12 @@ struct PassP {
   // get a per-row bias reuse_alpha * (top-1 logit - (top_k+1)-th logit)
   int reuse_cap; float reuse_alpha;
   const float* reuse_w;      // [m] row confidences (null: 1)
+  // token tree (null: the block is a chain): row j sits at position L +
+  // tree_pos[j] (its depth) for the rotary embedding, while its cache entry
+  // is written at slot L + j; it attends to the committed cache and to the
+  // block rows whose bits are set in tree_anc[j] (its ancestors and itself)
+  const int* tree_pos;
+  const unsigned* tree_anc;
   unsigned long long* stamps;   // [n_phases + 1] wall clock at phase ends (workgroup 0)
   unsigned long long* wstamps;  // [n_phases][n_wg][4] per-workgroup phase stamps (nullable)
 };
@@ -148,11 +154,17 @@ struct PassP {
 struct AcceptParams {
   int k, V, L, mode, n_stat;
   const int* tokens;
+  const int* parents;   // token tree: parent row of every row (mode kAcceptTree)
+  int* path;            // token tree: accepted rows, root excluded
   const float* st_max; const float* st_sum; const int* st_idx;
   const float* logits; int ldl;
   const float* q; const float* u;
   int* result;          // [3]
 };
+
+// Acceptance kernel mode for a token tree (greedy; the C ABI's modes are
+// 0..2).
+constexpr int kAcceptTree = 3;
 
 // MoE routing record in global memory (int32 words):
 //   [0] union size U; [1 .. E] union list (ascending expert id);
@@ -182,5 +194,9 @@ hipError_t launch_kv_import(int kv_f32, const void* src, int P, int Hkv, int D, 
                             const int* page_table, hipStream_t s);
 hipError_t launch_kv_poison(int kv_f32, void* base, long long layer_elems, int n_layers, int Hkv, int D,
                             const int* page_table, int from, int to, hipStream_t s);
+// After a token-tree step: moves the cache entries of the accepted rows
+// (path, count in result[0]) from slots L + path[j] to L + 1 + j.
+hipError_t launch_tree_commit(int kv_f32, void* base, long long layer_elems, int n_layers, int Hkv, int D,
+                              const int* page_table, int L, const int* result, const int* path, hipStream_t s);
 
 }  // namespace sv

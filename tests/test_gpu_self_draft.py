@@ -73,6 +73,28 @@ def test_draft_matches_oracle(moe, kd):
     log(f"[self draft] small_moe top-{kd}: {agree}/{N_DRAFT} draft tokens identical, drafts {toks}")
 
 
+def test_draft_routes_match_oracle(moe):
+    """The experts each draft pass routed its token to (route_dev of
+    spec_draft) against the oracle's selection, per layer as sets, for every
+    pass whose input token agrees; a difference must sit on a router near-tie
+    at the draft's top-k boundary."""
+    pw, h = moe
+    spec = pw.wl.spec
+    kd = 2
+    lg = torch.empty((N_DRAFT, spec.vocab), dtype=torch.float32, device="cuda")
+    rt = torch.full((N_DRAFT, spec.n_layers, kd), -1, dtype=torch.int32, device="cuda")
+    toks = h.draft(pw.pending0, N_DRAFT, kd, lg.data_ptr(), rt.data_ptr())
+    ref_toks, ref_logits, ref_routing = om.draft_greedy(pw.M, pw.kv0, pw.pending0, N_DRAFT, kd)
+    agree = _compare_draft(pw, toks, lg.cpu().numpy(), list(ref_toks), ref_logits, ref_routing, kd)
+    routes = rt.cpu().numpy()
+    for i in range(min(agree + 1, N_DRAFT)):
+        for l in range(spec.n_layers):
+            want = sorted(int(e) for e in ref_routing[i][l]["sel"][0])
+            got = sorted(int(e) for e in routes[i, l])
+            if got != want:
+                assert float(ref_routing[i][l]["topk_gap"][0]) < 1e-3, f"pass {i} layer {l}: {got} != {want}"
+
+
 def test_full_expert_draft_is_the_gpu_greedy_decode(moe):
     pw, h = moe
     L = h.kv_len
