@@ -78,6 +78,8 @@ def parse():
     ap.add_argument("--reuse-cap", type=int, default=0,
                     help="MoE: verify with reuse-aware expert gating (lossy) over this many preferred experts")
     ap.add_argument("--reuse-alpha", type=float, default=0.5, help="bias scale of reuse-aware gating")
+    ap.add_argument("--tree", action="store_true",
+                    help="also run self-drafted token trees with routing-aware expansion (--draft self)")
     ap.add_argument("--adaptive-k", action="store_true",
                     help="also time rounds whose lookahead follows spec_adaptive_k (start 5, +2 after a full "
                          "accept, -1 otherwise)")
@@ -326,6 +328,96 @@ def measure_self_draft(sess: Session, k: int, kd: int, warmup: int, steps: int):
                                 verify_ms_per_round=t_verify / steps * 1e3,
                                 e2e_accepted_tok_s=accepted / dt,
                                 mean_accepted_drafts=accepted / steps - 1.0))
+
+
+def measure_tree(sess: Session, n: int, kd: int, warmup: int, steps: int):
+    """Self-drafted token trees with routing-aware expansion (MoE).  Each
+    round drafts a chain of n tokens with kd routed experts (spec_draft, with
+    the draft logits and routes); the candidates are the chain tokens and, at
+    every depth, the draft's second choice as a sibling; spec_tree_expand
+    admits candidates by utility (prefix confidence x T_AR over the cost of
+    the experts they add plus their drafting cost) and spec_verify_tree
+    verifies the admitted tree in one pass.  T_AR is a measured one-token
+    step; T_exp one routed expert's share of it (its bytes at the pass's
+    measured bandwidth); a chain token costs one draft pass, a sibling
+    nothing (it comes from the same distribution).  A candidate whose own
+    token the draft did not run (the siblings and the last chain token) is
+    charged the experts of its parent's draft pass.  Compared with chain
+    verification of the same drafts (spec_verify_step with k = n)."""
+    import torch
+    np, B, h = sess.np, sess.B, sess.h
+    spec = sess.spec
+    V, E, NL = spec.vocab, spec.n_experts, spec.n_layers
+    # T_AR: one-token target steps at the prompt's end
+    h.rollback(sess.L0)
+    torch.cuda.synchronize()
+    h.profile(2)
+    t0 = time.perf_counter()
+    for _ in range(8):
+        h.step([sess.pending0], B.SPEC_ACCEPT_NONE)
+        h.rollback(sess.L0)
+    torch.cuda.synchronize()
+    t_ar = (time.perf_counter() - t0) / 8
+    n_p, ms_p, by_p = h.profile_read()["pass"]
+    h.profile(0)
+    wbytes = {"bf16": 2.0, "f32": 4.0, "int4": 0.5 + 2.0 / 128}[spec.weight_dtype]
+    t_exp = 3.0 * spec.d_model * spec.d_ff_expert * wbytes / (by_p / (ms_p / 1e3))
+    lg = torch.empty((n, V), dtype=torch.float32, device="cuda")
+    rt = torch.empty((n, NL, kd), dtype=torch.int32, device="cuda")
+    out = {}
+    for kind in ("chain", "tree"):
+        h.rollback(sess.L0)
+        pending = sess.pending0
+        t_draft = t_pol = t_ver = 0.0
+        acc = nodes = sib_acc = 0
+        c_draft = None
+        for r in range(warmup + steps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            drafts = h.draft(pending, n, kd, lg.data_ptr(), rt.data_ptr())
+            t1 = time.perf_counter()
+            c_draft = (t1 - t0) / n if c_draft is None else 0.8 * c_draft + 0.2 * (t1 - t0) / n
+            if kind == "chain":
+                t2 = t1
+                res = h.step([pending] + drafts, B.SPEC_ACCEPT_GREEDY)
+                m, hit_sib = n + 1, False
+            else:
+                # the draft's two best tokens and their probabilities per depth
+                top_p, top_i = torch.topk(torch.softmax(lg, dim=-1), 2, dim=-1)
+                top_p, top_i = top_p.double().cpu().numpy(), top_i.cpu().numpy()
+                routes = rt.cpu().numpy() + (np.arange(NL) * E)[None, :, None]
+                ids = [routes[i].reshape(-1).tolist() for i in range(n)]
+                par, pp, ex, toks, cd = [], [], [], [], []
+                for i in range(1, n + 1):       # chain token d_i and the sibling of depth i
+                    parent = -1 if i == 1 else len(par) - 2
+                    j = 1 if int(top_i[i - 1, 0]) == drafts[i - 1] else 0   # the sibling: the other of the two
+                    par += [parent, parent]
+                    pp += [float(top_p[i - 1, 1 - j]), float(top_p[i - 1, j])]
+                    ex += [ids[i] if i < n else ids[i - 1], ids[i - 1]]
+                    toks += [drafts[i - 1], int(top_i[i - 1, j])]
+                    cd += [c_draft, 0.0]
+                order, rows = B.tree_expand(par, pp, ex, ids[0], t_ar, t_exp, cd, 15)
+                tokens = [pending] + [toks[c] for c in order]
+                t2 = time.perf_counter()
+                res, path = h.step_tree(tokens, rows)
+                m = len(tokens)
+                hit_sib = any(order[p - 1] % 2 == 1 for p in path)
+            t3 = time.perf_counter()
+            if r >= warmup:
+                t_draft += t1 - t0
+                t_pol += t2 - t1
+                t_ver += t3 - t2
+                acc += res.n_accepted + 1
+                nodes += m
+                sib_acc += int(hit_sib)
+            pending = res.next_token
+        tot = t_draft + t_pol + t_ver
+        out[kind] = dict(mean_rows=round(nodes / steps, 3), mean_tokens_per_round=round(acc / steps, 4),
+                         draft_ms=round(t_draft / steps * 1e3, 4), policy_ms=round(t_pol / steps * 1e3, 4),
+                         verify_ms=round(t_ver / steps * 1e3, 4), e2e_tok_s=round(acc / tot, 2),
+                         rounds_accepting_a_sibling=sib_acc)
+    return dict(n=n, draft_top_k=kd, t_ar_ms=round(t_ar * 1e3, 4), t_exp_us=round(t_exp * 1e6, 3),
+                steps=steps, **out)
 
 
 def reuse_quality(sess: Session, k: int, cap: int, alpha: float, n_blocks: int = 8):
@@ -627,6 +719,12 @@ def main():
         line["config"]["workload"] = line["config"]["workload"].replace(
             f"draft corruption {wl.corruption}", f"self-speculative draft with {args.draft_top_k} routed expert(s)")
         line["self_draft"] = {kk: round(v, 4) if isinstance(v, float) else v for kk, v in r["self_draft"].items()}
+    if args.tree:
+        if args.draft != "self":
+            raise SystemExit("--tree expands self-drafted candidates: use it with --draft self")
+        with torch.cuda.stream(stream):
+            line["tree"] = measure_tree(sess, k, args.draft_top_k, args.warmup, args.steps)
+        log(f"[bench] token trees: {line['tree']}")
     if args.k_sweep:
         def frac(v):
             t = v["timed"]
