@@ -87,7 +87,11 @@ typedef struct {
                             table); otherwise the logical pages are mapped to physical pages
                             by a permutation drawn from this seed (results are identical;
                             a test knob for the page indirection). */
-  int32_t reserved[6];   /* must be zero */
+  int32_t n_seqs;        /* sequences the handle holds (0 or 1: one), at most 64.  Each has
+                            its own cache of max_ctx positions and committed length;
+                            sequence 0 is the one the single-sequence calls work on, the
+                            others are stepped by spec_verify_batch. */
+  int32_t reserved[5];   /* must be zero */
 } spec_config;
 
 /* Weight tensor kinds.  Matrices are row-major [K][N] with y = x . W. */
@@ -210,6 +214,38 @@ int spec_verify_step_noalloc(spec_verify_t* h, const int32_t* tokens, int32_t k,
  * Errors as in spec_verify_step (SPEC_EINVAL for a malformed tree). */
 int spec_verify_tree(spec_verify_t* h, const int32_t* tokens, const int32_t* parents, int32_t m,
                      spec_step_result* out, int32_t* path, float* logits_dev);
+
+/* Several sequences verified in one pass: their blocks share one stream
+ * of the weights (the essay's "What is not here" sets batching aside; the
+ * rows of the pass are what batching spends).  Sequence i of the call is
+ * seqs[i] (distinct, in [0, n_seqs)), with block tokens[r_i .. r_i + ks[i]]
+ * = [pending_i, d_1 .. d_k] (r_i = sum of ks[j] + 1 over j < i); the
+ * blocks' rows sum(ks[i] + 1) must not exceed max_k + 1.  Each row attends
+ * to its own sequence's committed cache and earlier rows only, at that
+ * sequence's positions, so every sequence gets the result a step of its
+ * own block would give (up to summation order).
+ *   mode: SPEC_ACCEPT_GREEDY or SPEC_ACCEPT_NONE (commit every row, e.g.
+ *         to append a sequence's prompt).
+ *   out:  host [n], one result per sequence in call order.
+ *   logits_dev: NULL or device fp32 [sum(ks[i] + 1)][vocab], rows in call
+ *         order.
+ * Errors as in spec_verify_step, plus SPEC_EINVAL for a bad or repeated
+ * sequence id; nothing changes on an error. */
+int spec_verify_batch(spec_verify_t* h, int32_t n, const int32_t* seqs, const int32_t* tokens, const int32_t* ks,
+                      int32_t mode, spec_step_result* out, float* logits_dev);
+
+/* Committed length of sequence seq (-1 for a bad handle or id). */
+int32_t spec_seq_kv_len(const spec_verify_t* h, int32_t seq);
+
+/* Commit / rollback for sequence seq (new_kv_len <= its length), as
+ * spec_kv_commit_rollback does for sequence 0. */
+int spec_seq_rollback(spec_verify_t* h, int32_t seq, int32_t new_kv_len);
+
+/* Replaces sequence seq's cache with a prompt cache: host arrays laid out
+ * as spec_verify_create's prompt_k / prompt_v, prompt_len <= max_ctx (else
+ * SPEC_ECAPACITY); the sequence's committed length becomes prompt_len.
+ * Allocates and frees a device staging buffer. */
+int spec_seq_import(spec_verify_t* h, int32_t seq, const void* prompt_k, const void* prompt_v, int32_t prompt_len);
 
 /* Self-speculative draft of a MoE target by expert sparsity (S2-MoE,
  * section 2.3 and section 5 "Draft configuration", Table 1: the draft is

@@ -33,7 +33,8 @@ class SpecConfig(ctypes.Structure):
                  "n_experts", "top_k", "n_shared", "d_ff_expert", "weight_dtype", "kv_dtype")] + \
                [("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("max_ctx", ctypes.c_int32), ("max_k", ctypes.c_int32), ("gemm_k_split", ctypes.c_int32),
-                ("kv_page_seed", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6)]
+                ("kv_page_seed", ctypes.c_int32), ("n_seqs", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 5)]
 
 
 class SpecTensor(ctypes.Structure):
@@ -83,6 +84,11 @@ def _load():
                                  ctypes.POINTER(D), I, ctypes.POINTER(ctypes.c_int32),
                                  ctypes.POINTER(ctypes.c_int32)]),
         "spec_adaptive_k": (I, [I, I, I]),
+        "spec_verify_batch": (I, [P, I, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+                                  ctypes.POINTER(ctypes.c_int32), I, ctypes.POINTER(SpecStepResult), P]),
+        "spec_seq_kv_len": (I, [P, I]),
+        "spec_seq_rollback": (I, [P, I, I]),
+        "spec_seq_import": (I, [P, I, P, P, I]),
         "spec_verify_tree": (I, [P, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), I,
                                  ctypes.POINTER(SpecStepResult), ctypes.POINTER(ctypes.c_int32), P]),
         "spec_verify_step_reuse": (I, [P, ctypes.POINTER(ctypes.c_int32), I, I, P, P, P, I, F,
@@ -119,6 +125,10 @@ spec_draft = lib.spec_draft
 spec_adaptive_k = lib.spec_adaptive_k
 spec_verify_tree = lib.spec_verify_tree
 spec_tree_expand = lib.spec_tree_expand
+spec_verify_batch = lib.spec_verify_batch
+spec_seq_kv_len = lib.spec_seq_kv_len
+spec_seq_rollback = lib.spec_seq_rollback
+spec_seq_import = lib.spec_seq_import
 spec_verify_step_reuse = lib.spec_verify_step_reuse
 spec_verify_step_noalloc = lib.spec_verify_step_noalloc
 
@@ -132,7 +142,8 @@ class SpecError(RuntimeError):
 _DT = {"f32": SPEC_DT_F32, "bf16": SPEC_DT_BF16, "int4g128": SPEC_DT_INT4G128}
 
 
-def make_config(spec, max_ctx: int, max_k: int, gemm_k_split: int = 0, kv_page_seed: int = 0) -> SpecConfig:
+def make_config(spec, max_ctx: int, max_k: int, gemm_k_split: int = 0, kv_page_seed: int = 0,
+                n_seqs: int = 0) -> SpecConfig:
     c = SpecConfig()
     c.n_layers, c.d_model = spec.n_layers, spec.d_model
     c.n_q_heads, c.n_kv_heads, c.head_dim = spec.n_q_heads, spec.n_kv_heads, spec.head_dim
@@ -142,6 +153,7 @@ def make_config(spec, max_ctx: int, max_k: int, gemm_k_split: int = 0, kv_page_s
     c.rope_theta, c.rms_eps = spec.rope_theta, spec.rms_eps
     c.max_ctx, c.max_k, c.gemm_k_split = max_ctx, max_k, gemm_k_split
     c.kv_page_seed = kv_page_seed
+    c.n_seqs = n_seqs
     return c
 
 
@@ -191,9 +203,9 @@ class Verifier:
 
     def __init__(self, spec, W, prompt_k: Optional[np.ndarray], prompt_v: Optional[np.ndarray],
                  prompt_len: int, max_ctx: int, max_k: int, stream: int = 0, gemm_k_split: int = 0,
-                 kv_page_seed: int = 0):
+                 kv_page_seed: int = 0, n_seqs: int = 0):
         self.spec = spec
-        self.cfg = make_config(spec, max_ctx, max_k, gemm_k_split, kv_page_seed)
+        self.cfg = make_config(spec, max_ctx, max_k, gemm_k_split, kv_page_seed, n_seqs)
         tens, keep = make_tensors(W)
         pk = pv = None
         if prompt_len > 0:
@@ -263,6 +275,36 @@ class Verifier:
         if rc != SPEC_OK:
             raise SpecError(rc, self.last_error())
         return res, [int(path[i]) for i in range(res.n_accepted)]
+
+    def step_batch(self, seqs: Sequence[int], blocks, mode: int = SPEC_ACCEPT_GREEDY, logits_ptr: int = 0):
+        """Several sequences' blocks in one pass (spec_verify_batch):
+        blocks[i] = [pending, d_1 .. d_k] of sequence seqs[i].  Returns one
+        result per sequence."""
+        n = len(seqs)
+        sq = np.ascontiguousarray(np.asarray(seqs, dtype=np.int32))
+        ks = np.ascontiguousarray(np.asarray([len(b) - 1 for b in blocks], dtype=np.int32))
+        tk = np.ascontiguousarray(np.concatenate([np.asarray(b, dtype=np.int32) for b in blocks]))
+        out = (SpecStepResult * n)()
+        P32 = ctypes.POINTER(ctypes.c_int32)
+        rc = spec_verify_batch(self.h, n, sq.ctypes.data_as(P32), tk.ctypes.data_as(P32), ks.ctypes.data_as(P32),
+                               int(mode), out, logits_ptr or None)
+        if rc != SPEC_OK:
+            raise SpecError(rc, self.last_error())
+        return [out[i] for i in range(n)]
+
+    def seq_len(self, seq: int) -> int:
+        return int(spec_seq_kv_len(self.h, int(seq)))
+
+    def seq_rollback(self, seq: int, new_len: int) -> None:
+        rc = spec_seq_rollback(self.h, int(seq), int(new_len))
+        if rc != SPEC_OK:
+            raise SpecError(rc, self.last_error())
+
+    def seq_import(self, seq: int, k: np.ndarray, v: np.ndarray, length: int) -> None:
+        kk, vv = np.ascontiguousarray(k), np.ascontiguousarray(v)
+        rc = spec_seq_import(self.h, int(seq), kk.ctypes.data, vv.ctypes.data, int(length))
+        if rc != SPEC_OK:
+            raise SpecError(rc, self.last_error())
 
     def rollback(self, new_len: int) -> None:
         rc = spec_kv_commit_rollback(self.h, new_len)

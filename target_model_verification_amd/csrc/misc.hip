@@ -83,6 +83,22 @@ __global__ __launch_bounds__(1024) void k_accept(AcceptParams p) {
     }
     return;
   }
+  if (p.mode == kAcceptBatchGreedy || p.mode == kAcceptBatchNone) {   // several sequences' blocks
+    if (tid < p.n_seq) {
+      const int r0 = p.seq_info[3 * tid + 0], k = p.seq_info[3 * tid + 1], L = p.seq_info[3 * tid + 2];
+      int n = 0;
+      if (p.mode == kAcceptBatchGreedy) {
+        while (n < k && p.tokens[r0 + n + 1] == amax[r0 + n]) ++n;
+      } else {
+        n = k;
+      }
+      p.result[4 * tid + 0] = n;
+      p.result[4 * tid + 1] = amax[r0 + n];
+      p.result[4 * tid + 2] = L + 1 + n;
+      p.result[4 * tid + 3] = 0;
+    }
+    return;
+  }
   if (p.mode != 1) {               // greedy / none
     if (tid == 0) {
       int n = 0;

@@ -419,8 +419,8 @@ __device__ __forceinline__ void qkv_pre(const PassP& P, int unit, QkvPre& q) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = min(4 * rg + i, P.m - 1);
-    const int t = P.L + row;                                           // cache slot
-    const int tp = P.tree_pos ? P.L + P.tree_pos[row] : t;             // rotary position
+    const int t = P.row_slot ? P.row_slot[row] : P.L + row;   // cache slot
+    const int tp = P.row_rope ? P.row_rope[row] : t;          // rotary position
     q.pg[i] = (long long)P.page_table[t / kPage] * P.Hkv;
     q.cs[i] = rot_col ? P.rope_cs[((long long)tp * H + ii) * 2 + 0] : 0.f;
     q.sn[i] = rot_col ? P.rope_cs[((long long)tp * H + ii) * 2 + 1] : 0.f;
@@ -506,7 +506,7 @@ __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const Gem
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * rg + i;
       if (row < P.m && col < M.N) {
-        const int t = P.L + row;
+        const int t = P.row_slot ? P.row_slot[row] : P.L + row;
         if (rot_col) {
           const float a = odd ? pv[i] : v[i], b = odd ? v[i] : pv[i];   // x[ii], x[ii + H]
           const float rot = odd ? (b * cs[i] + a * sn[i]) : (a * cs[i] - b * sn[i]);
@@ -1182,7 +1182,7 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
   const int R = P.m * P.G;
   const int NRT = (R + 15) >> 4;   // row tiles per KV head: one per work item
   const int RT = MAXRT;            // row tiles of this item
-  const int T = P.L + P.m;
+  const int T = P.T;
   constexpr int PSW = (ONE ? kGroupPos : kPage) + 4;  // floats per score row
   u4* Qf = reinterpret_cast<u4*>(smem);                              // [RT][KDC][2][64] (two-pass path)
   float* Ps = reinterpret_cast<float*>(smem + (size_t)RT * KDC * 2 * 1024);   // [RT*16][PSW]
@@ -1274,7 +1274,7 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
     // scores of this wave's 16 keys of sub-chunk sc for row tile rt, masked
     auto scores = [&](int sc, int rt, const u4 (&kr)[4 * W]) -> f32x4 {
       const int t0 = gt0 + sc * kPage;
-      const int nkeys = min(kPage, T - t0);
+      const int nkeys = P.page_live ? P.page_live[t0 / kPage] : min(kPage, T - t0);
       f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
@@ -1308,10 +1308,12 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
       for (int i = 0; i < 4; ++i) {
         const int r = rb + rt * 16 + 4 * (lane >> 4) + i;
         // causal: block row j sees positions up to L + j; a token tree: the
-        // committed cache and the rows of its ancestor mask
+        // committed cache and the rows of its ancestor mask; several
+        // sequences: the row's own slot interval
         bool seen = tk <= P.L + r / P.G;
         if (P.tree_anc && tk >= P.L && tk - P.L < kMaxRows && r < R)
           seen = ((P.tree_anc[r / P.G] >> (tk - P.L)) & 1u) != 0u;
+        if (P.row_hi && r < R) seen = tk >= P.row_lo[r / P.G] && tk <= P.row_hi[r / P.G];
         const bool vis = r < R && key < nkeys && seen;
         s4[i] = vis ? s4[i] : -INFINITY;
       }
@@ -1324,7 +1326,7 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
 #pragma unroll
       for (int q = 0; q < 2; ++q) acc[rt][q] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto pv = [&](int sc, int pc, u4 (&vr)[2][2 * W]) {
-      const int nkeys = min(kPage, T - (gt0 + sc * kPage));
+      const int nkeys = P.page_live ? P.page_live[gt0 / kPage + sc] : min(kPage, T - (gt0 + sc * kPage));
       u4 vh[2][2], vl[2][2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {

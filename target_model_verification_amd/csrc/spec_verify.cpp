@@ -57,8 +57,15 @@ struct spec_verify {
   // KV cache
   void* kv = nullptr;
   long long kv_layer_elems = 0;
-  int n_pages = 0;
-  int* page_table = nullptr;
+  int n_pages = 0;              // all sequences' pages
+  int* page_table = nullptr;    // [n_seqs][pps]: sequence s's logical page i -> physical page
+  std::vector<int> pt_host;     // host copy of the page table
+  int n_seqs = 1, pps = 0;      // sequences, pages per sequence
+  std::vector<int> seq_len;     // committed lengths of sequences 1.. (sequence 0: kv_len)
+  int* batch_dev = nullptr;     // several sequences: row placement, sequence records, virtual page table
+  int* batch_host = nullptr;    // pinned staging of batch_dev
+  int* batch_res = nullptr;     // [kMaxRows][4] per-sequence outcomes (device)
+  int* batch_res_host = nullptr;
   float* rope_cs = nullptr;
   // activations / scratch
   int ldx = 0, ldl = 0, n_ss = 0, n_stat = 0, ldr = 0;
@@ -125,6 +132,13 @@ struct spec_verify {
 namespace {
 
 const char* kNullMsg = "null handle";
+
+// Several sequences in one pass, device words: row slots, rotary positions,
+// slot intervals [4][kMaxRows], sequence records [kMaxRows][3], then the
+// virtual page table and the live slots of each virtual page.
+constexpr int kBatchSlot = 0, kBatchRope = kMaxRows, kBatchLo = 2 * kMaxRows, kBatchHi = 3 * kMaxRows,
+              kBatchSeq = 4 * kMaxRows, kBatchPages = 7 * kMaxRows;
+size_t batch_words(const spec_verify* h) { return kBatchPages + 2 * (size_t)h->n_pages; }
 
 int fail(spec_verify* h, int code, const std::string& msg) {
   if (h) h->err = msg;
@@ -198,8 +212,9 @@ bool check_cfg(const spec_config* c, std::string& msg) {
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return bad("rope_theta must be > 0 and rms_eps >= 0");
   if (c->gemm_k_split < 0 || c->gemm_k_split % 128 != 0 || c->gemm_k_split > 2048)
     return bad("gemm_k_split must be a multiple of 128 in [0, 2048]");
-  for (int i = 0; i < 6; ++i)
+  for (int i = 0; i < 5; ++i)
     if (c->reserved[i] != 0) return bad("reserved fields must be zero");
+  if (c->n_seqs < 0 || c->n_seqs > 64) return bad("n_seqs must be in [0, 64]");
   const bool moe = c->n_experts > 0;
   if (moe) {
     if (c->n_experts > 256) return bad("n_experts must be <= 256");
@@ -570,7 +585,9 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   if ((rc = up.put(h->lm_head, SPEC_T_LM_HEAD, -1, -1, d, V, 0, 1, 0))) return rc;
 
   // KV cache pages and the page table (identity, or a seeded permutation)
-  h->n_pages = cdiv(c.max_ctx, kPage);
+  h->n_seqs = c.n_seqs > 0 ? c.n_seqs : 1;
+  h->pps = cdiv(c.max_ctx, kPage);
+  h->n_pages = h->n_seqs * h->pps;
   h->kv_layer_elems = (long long)h->n_pages * Hkv * 2 * kPage * D;
   if ((rc = dalloc_z(h, reinterpret_cast<char**>(&h->kv), (size_t)h->kv_layer_elems * c.n_layers * kv_elem)))
     return rc;
@@ -592,7 +609,9 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
     }
     if ((rc = dalloc_t(h, &h->page_table, h->n_pages))) return rc;
     HIPCHK(hipMemcpy(h->page_table, pt.data(), sizeof(int) * h->n_pages, hipMemcpyHostToDevice));
+    h->pt_host = pt;
   }
+  h->seq_len.assign(h->n_seqs, 0);
   if (prompt_len > 0) {
     const size_t lb = (size_t)Hkv * prompt_len * D * kv_elem;
     for (int l = 0; l < c.n_layers; ++l) {
@@ -652,7 +671,8 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   if ((rc = dalloc_z(h, &h->st_sum, 16 * (size_t)h->n_stat))) return rc;
   if ((rc = dalloc_z(h, &h->st_idx, 16 * (size_t)h->n_stat))) return rc;
   const size_t Rmax = (size_t)max_rows_attn(&c);
-  const size_t max_groups = cdiv(c.max_ctx, kGroupPos);
+  // (several sequences: one slot space of all of them, page-aligned)
+  const size_t max_groups = cdiv((size_t)h->n_pages * kPage, (size_t)kGroupPos);
   if ((rc = dalloc_z(h, &h->pm, Hkv * max_groups * Rmax))) return rc;
   if ((rc = dalloc_z(h, &h->ps, Hkv * max_groups * Rmax))) return rc;
   if ((rc = dalloc_z(h, &h->pacc, Hkv * max_groups * Rmax * D))) return rc;
@@ -681,6 +701,10 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->result_host), 4 * sizeof(int), hipHostMallocDefault));
   if ((rc = dalloc_z(h, &h->draft_res, (size_t)kMaxRows * 4))) return rc;
   if ((rc = dalloc_z(h, &h->tree_dev, (size_t)kMaxRows * 4))) return rc;
+  if ((rc = dalloc_z(h, &h->batch_dev, (size_t)batch_words(h)))) return rc;
+  if ((rc = dalloc_z(h, &h->batch_res, (size_t)kMaxRows * 4))) return rc;
+  HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->batch_host), batch_words(h) * sizeof(int), hipHostMallocDefault));
+  HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->batch_res_host), kMaxRows * 4 * sizeof(int), hipHostMallocDefault));
   HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->tree_host), kMaxRows * 4 * sizeof(int), hipHostMallocDefault));
   HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->draft_host), (kMaxRows * 4 + 4) * sizeof(int),
                        hipHostMallocDefault));
@@ -816,6 +840,8 @@ void free_all(spec_verify* h) {
   if (h->result_host) (void)hipHostFree(h->result_host);
   if (h->draft_host) (void)hipHostFree(h->draft_host);
   if (h->tree_host) (void)hipHostFree(h->tree_host);
+  if (h->batch_host) (void)hipHostFree(h->batch_host);
+  if (h->batch_res_host) (void)hipHostFree(h->batch_res_host);
   for (auto& e : h->ev)
     if (e) (void)hipEventDestroy(e);
 }
@@ -847,14 +873,15 @@ double phase_bytes(const spec_verify* h, int i, int m, int L, int experts_loaded
 // Parameters of one pass over m block rows at committed length L, reading
 // the block's token ids from tokens_dev, with top_k routed experts per token
 // (MoE).
-PassP pass_params(const spec_verify* h, int m, int L, const int* tokens_dev, int top_k) {
+PassP pass_params(const spec_verify* h, int m, int L, const int* tokens_dev, int top_k, int T = -1) {
   const spec_config& c = h->cfg;
   const bool moe = c.n_experts > 0;
   PassP p{};
   p.m = m; p.L = L; p.n_layers = c.n_layers; p.d = c.d_model; p.Hq = c.n_q_heads; p.Hkv = c.n_kv_heads;
   p.D = c.head_dim; p.V = c.vocab; p.G = c.n_q_heads / c.n_kv_heads; p.E = c.n_experts; p.top_k = top_k;
   p.n_shared = c.n_shared; p.F = moe ? c.d_ff_expert : c.d_ff;
-  p.n_groups = cdiv(L + m, kGroupPos);
+  p.T = T >= 0 ? T : L + m;
+  p.n_groups = cdiv(p.T, kGroupPos);
   // heads whose merge is small are merged by their last attention item;
   // the merge phases (one per layer) then run without a barrier
   p.attn_inline = (long long)m * p.G * c.head_dim * p.n_groups <= kInlineMergeElems ? 1 : 0;
@@ -1131,9 +1158,9 @@ int spec_verify_tree(spec_verify_t* h, const int32_t* tokens, const int32_t* par
   for (int i = 0; i < m; ++i)
     if (tokens[i] < 0 || tokens[i] >= c.vocab) return fail(h, SPEC_EINVAL, "token id out of range");
   if (parents[0] != -1) return fail(h, SPEC_EINVAL, "row 0 (the pending token) is the root: parents[0] must be -1");
-  int* depth = h->tree_host + kMaxRows;
+  int* depth = h->tree_host + kMaxRows;   // rotary positions L + depth
   unsigned* anc = reinterpret_cast<unsigned*>(h->tree_host + 2 * kMaxRows);
-  depth[0] = 0;
+  depth[0] = h->kv_len;
   anc[0] = 1u;
   for (int i = 1; i < m; ++i) {
     if (parents[i] < 0 || parents[i] >= i) return fail(h, SPEC_EINVAL, "every parent must precede its row");
@@ -1148,7 +1175,7 @@ int spec_verify_tree(spec_verify_t* h, const int32_t* tokens, const int32_t* par
   if (he == hipSuccess)
     he = hipMemcpyAsync(h->tree_dev, h->tree_host, sizeof(int) * 3 * kMaxRows, hipMemcpyHostToDevice, h->stream);
   PassP p = pass_params(h, m, L, h->tokens_dev, c.top_k);
-  p.tree_pos = h->tree_dev + kMaxRows;
+  p.row_rope = h->tree_dev + kMaxRows;
   p.tree_anc = reinterpret_cast<const unsigned*>(h->tree_dev + 2 * kMaxRows);
   if (he == hipSuccess) he = launch_counted(h, p);
   AcceptParams a{};
@@ -1183,6 +1210,151 @@ int spec_verify_tree(spec_verify_t* h, const int32_t* tokens, const int32_t* par
   out->kv_len = h->result_host[2];
   for (int i = 0; i < out->n_accepted; ++i) path[i] = h->tree_host[3 * kMaxRows + i];
   h->kv_len = out->kv_len;
+  h->err.clear();
+  return SPEC_OK;
+}
+
+int spec_verify_batch(spec_verify_t* h, int32_t n, const int32_t* seqs, const int32_t* tokens, const int32_t* ks,
+                      int32_t mode, spec_step_result* out, float* logits_dev) {
+  if (!h) return SPEC_EINVAL;
+  if (h->broken) return fail(h, SPEC_ESTATE, "handle unusable after an earlier GPU error");
+  const spec_config& c = h->cfg;
+  if (!seqs || !tokens || !ks || !out) return fail(h, SPEC_EINVAL, "seqs, tokens, ks and out are required");
+  if (n < 1 || n > h->n_seqs || n > kMaxRows) return fail(h, SPEC_EINVAL, "n must be in [1, n_seqs]");
+  if (mode != SPEC_ACCEPT_GREEDY && mode != SPEC_ACCEPT_NONE)
+    return fail(h, SPEC_EINVAL, "several sequences step with greedy acceptance or none");
+  int m = 0;
+  for (int i = 0; i < n; ++i) {
+    if (seqs[i] < 0 || seqs[i] >= h->n_seqs) return fail(h, SPEC_EINVAL, "sequence id out of range");
+    for (int j = 0; j < i; ++j)
+      if (seqs[j] == seqs[i]) return fail(h, SPEC_EINVAL, "a sequence appears twice");
+    if (ks[i] < 0) return fail(h, SPEC_EINVAL, "k must be >= 0");
+    m += ks[i] + 1;
+  }
+  if (m > c.max_k + 1) return fail(h, SPEC_EINVAL, "the blocks' rows (sum of k + 1) exceed max_k + 1");
+  for (int i = 0; i < m; ++i)
+    if (tokens[i] < 0 || tokens[i] >= c.vocab) return fail(h, SPEC_EINVAL, "token id out of range");
+  auto len = [&](int s) { return s == 0 ? h->kv_len : h->seq_len[s]; };
+  for (int i = 0; i < n; ++i)
+    if ((long long)len(seqs[i]) + ks[i] + 1 > c.max_ctx) return fail(h, SPEC_ECAPACITY, "a block exceeds max_ctx");
+  // one slot space: the sequences' live pages side by side, in call order
+  int* B = h->batch_host;
+  int* vpt = B + kBatchPages;
+  int* live = vpt + h->n_pages;
+  int V = 0, r = 0, T = 0;
+  for (int i = 0; i < n; ++i) {
+    const int s = seqs[i], L = len(s), mi = ks[i] + 1, np = cdiv(L + mi, kPage);
+    for (int pg = 0; pg < np; ++pg) {
+      vpt[V / kPage + pg] = h->pt_host[(size_t)s * h->pps + pg];
+      live[V / kPage + pg] = std::min(kPage, L + mi - pg * kPage);
+    }
+    B[kBatchSeq + 3 * i + 0] = r;
+    B[kBatchSeq + 3 * i + 1] = ks[i];
+    B[kBatchSeq + 3 * i + 2] = L;
+    for (int j = 0; j < mi; ++j, ++r) {
+      B[kBatchSlot + r] = V + L + j;
+      B[kBatchRope + r] = L + j;
+      B[kBatchLo + r] = V;
+      B[kBatchHi + r] = V + L + j;
+    }
+    T = V + L + mi;
+    V += np * kPage;
+  }
+  std::memcpy(h->tokens_host, tokens, sizeof(int32_t) * m);
+  hipError_t he = hipMemcpyAsync(h->tokens_dev, h->tokens_host, sizeof(int32_t) * m, hipMemcpyHostToDevice, h->stream);
+  if (he == hipSuccess)
+    he = hipMemcpyAsync(h->batch_dev, B, sizeof(int) * (kBatchPages + 2 * (size_t)h->n_pages), hipMemcpyHostToDevice,
+                        h->stream);
+  PassP p = pass_params(h, m, 0, h->tokens_dev, c.top_k, T);
+  p.page_table = h->batch_dev + kBatchPages;
+  p.page_live = h->batch_dev + kBatchPages + h->n_pages;
+  p.row_slot = h->batch_dev + kBatchSlot;
+  p.row_rope = h->batch_dev + kBatchRope;
+  p.row_lo = h->batch_dev + kBatchLo;
+  p.row_hi = h->batch_dev + kBatchHi;
+  if (he == hipSuccess) he = launch_counted(h, p);
+  AcceptParams a{};
+  a.k = m - 1; a.V = c.vocab; a.L = 0; a.n_stat = h->n_stat;
+  a.mode = mode == SPEC_ACCEPT_GREEDY ? kAcceptBatchGreedy : kAcceptBatchNone;
+  a.n_seq = n; a.seq_info = h->batch_dev + kBatchSeq;
+  a.tokens = h->tokens_dev;
+  a.st_max = h->st_max; a.st_sum = h->st_sum; a.st_idx = h->st_idx;
+  a.logits = h->logits; a.ldl = h->ldl;
+  a.result = h->batch_res;
+  if (he == hipSuccess) he = launch_accept(a, h->stream);
+  if (he == hipSuccess)
+    he = hipMemcpyAsync(h->batch_res_host, h->batch_res, sizeof(int) * 4 * n, hipMemcpyDeviceToHost, h->stream);
+  if (he == hipSuccess)
+    he = hipMemcpyAsync(h->result_host, h->result_dev, 4 * sizeof(int), hipMemcpyDeviceToHost, h->stream);
+  if (he == hipSuccess && logits_dev)
+    he = hipMemcpy2DAsync(logits_dev, (size_t)c.vocab * 4, h->logits, (size_t)h->ldl * 4, (size_t)c.vocab * 4, m,
+                          hipMemcpyDeviceToDevice, h->stream);
+  if (he == hipSuccess) he = hipStreamSynchronize(h->stream);
+  if (he != hipSuccess) {
+    h->broken = true;
+    return fail(h, SPEC_EHIP, std::string("batch step: ") + hipGetErrorString(he));
+  }
+  if (h->result_host[3] != 0) {
+    h->broken = true;
+    return fail(h, SPEC_EHIP, "grid barrier wait timed out inside the pass");
+  }
+  for (int i = 0; i < n; ++i) {
+    out[i].n_accepted = h->batch_res_host[4 * i + 0];
+    out[i].next_token = h->batch_res_host[4 * i + 1];
+    out[i].kv_len = h->batch_res_host[4 * i + 2];
+    if (seqs[i] == 0) h->kv_len = out[i].kv_len;
+    else h->seq_len[seqs[i]] = out[i].kv_len;
+  }
+  h->err.clear();
+  return SPEC_OK;
+}
+
+int32_t spec_seq_kv_len(const spec_verify_t* h, int32_t seq) {
+  if (!h || seq < 0 || seq >= h->n_seqs) return -1;
+  return seq == 0 ? h->kv_len : h->seq_len[seq];
+}
+
+int spec_seq_rollback(spec_verify_t* h, int32_t seq, int32_t new_kv_len) {
+  if (!h) return SPEC_EINVAL;
+  if (h->broken) return fail(h, SPEC_ESTATE, "handle unusable after an earlier GPU error");
+  if (seq < 0 || seq >= h->n_seqs) return fail(h, SPEC_EINVAL, "sequence id out of range");
+  int& len = seq == 0 ? h->kv_len : h->seq_len[seq];
+  if (new_kv_len < 0 || new_kv_len > len) return fail(h, SPEC_EINVAL, "rollback length must be in [0, kv_len]");
+  len = new_kv_len;
+  h->err.clear();
+  return SPEC_OK;
+}
+
+int spec_seq_import(spec_verify_t* h, int32_t seq, const void* prompt_k, const void* prompt_v, int32_t prompt_len) {
+  if (!h) return SPEC_EINVAL;
+  if (h->broken) return fail(h, SPEC_ESTATE, "handle unusable after an earlier GPU error");
+  const spec_config& c = h->cfg;
+  if (seq < 0 || seq >= h->n_seqs) return fail(h, SPEC_EINVAL, "sequence id out of range");
+  if (prompt_len < 0 || prompt_len > c.max_ctx) return fail(h, SPEC_ECAPACITY, "prompt exceeds max_ctx");
+  if (prompt_len > 0 && (!prompt_k || !prompt_v)) return fail(h, SPEC_EINVAL, "prompt_k and prompt_v are required");
+  const size_t kv_elem = c.kv_dtype == SPEC_DT_F32 ? 4 : 2;
+  const size_t lb = (size_t)c.n_kv_heads * prompt_len * c.head_dim * kv_elem;
+  if (prompt_len > 0) {
+    void* staging = nullptr;
+    HIPCHK(hipMalloc(&staging, 2 * lb));
+    hipError_t he = hipSuccess;
+    for (int l = 0; l < c.n_layers && he == hipSuccess; ++l) {
+      he = hipMemcpyAsync(staging, static_cast<const char*>(prompt_k) + l * lb, lb, hipMemcpyHostToDevice, h->stream);
+      if (he == hipSuccess)
+        he = hipMemcpyAsync(static_cast<char*>(staging) + lb, static_cast<const char*>(prompt_v) + l * lb, lb,
+                            hipMemcpyHostToDevice, h->stream);
+      if (he == hipSuccess)
+        he = launch_kv_import(c.kv_dtype == SPEC_DT_F32, staging, prompt_len, c.n_kv_heads, c.head_dim,
+                              h->layers[l].kv, h->page_table + (size_t)seq * h->pps, h->stream);
+      if (he == hipSuccess) he = hipStreamSynchronize(h->stream);
+    }
+    (void)hipFree(staging);
+    if (he != hipSuccess) {
+      h->broken = true;
+      return fail(h, SPEC_EHIP, std::string("import: ") + hipGetErrorString(he));
+    }
+  }
+  (seq == 0 ? h->kv_len : h->seq_len[seq]) = prompt_len;
   h->err.clear();
   return SPEC_OK;
 }

@@ -141,18 +141,31 @@ struct PassP {
   // get a per-row bias reuse_alpha * (top-1 logit - (top_k+1)-th logit)
   int reuse_cap; float reuse_alpha;
   const float* reuse_w;      // [m] row confidences (null: 1)
-  // token tree (null: the block is a chain): row j sits at position L +
-  // tree_pos[j] (its depth) for the rotary embedding, while its cache entry
-  // is written at slot L + j; it attends to the committed cache and to the
-  // block rows whose bits are set in tree_anc[j] (its ancestors and itself)
-  const int* tree_pos;
+  // Per-row placement (each null: one sequence, row j at cache slot L + j,
+  // rotary position L + j, causal over slots 0 .. L + j):
+  //   row_slot[j]  cache slot of row j's new key and value;
+  //   row_rope[j]  its rotary position;
+  //   row_lo/hi[j] the slots it attends to, lo .. hi (several sequences in
+  //                one slot space: each row sees its own sequence only);
+  //   page_live[p] live slots of page p (the rest are another sequence's
+  //                padding: their keys and values are never used).
+  // A token tree: rows attend to the committed cache and to the block rows
+  // whose bits are set in tree_anc[j] (ancestors and itself).
+  const int* row_slot;
+  const int* row_rope;
+  const int* row_lo;
+  const int* row_hi;
+  const int* page_live;
   const unsigned* tree_anc;
+  int T;                     // slots the attention reads: L + m (one sequence) or the batch's extent
   unsigned long long* stamps;   // [n_phases + 1] wall clock at phase ends (workgroup 0)
   unsigned long long* wstamps;  // [n_phases][n_wg][4] per-workgroup phase stamps (nullable)
 };
 
 struct AcceptParams {
   int k, V, L, mode, n_stat;
+  int n_seq;                 // several sequences (mode kAcceptBatch*): their count
+  const int* seq_info;       // [n_seq][3]: first row, k, committed length
   const int* tokens;
   const int* parents;   // token tree: parent row of every row (mode kAcceptTree)
   int* path;            // token tree: accepted rows, root excluded
@@ -165,6 +178,10 @@ struct AcceptParams {
 // Acceptance kernel mode for a token tree (greedy; the C ABI's modes are
 // 0..2).
 constexpr int kAcceptTree = 3;
+// Several sequences in one block: greedy per sequence, or every row
+// committed (results [n_seq][4]: n_accepted, next token, new length).
+constexpr int kAcceptBatchGreedy = 4;
+constexpr int kAcceptBatchNone = 5;
 
 // MoE routing record in global memory (int32 words):
 //   [0] union size U; [1 .. E] union list (ascending expert id);

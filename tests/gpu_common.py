@@ -28,10 +28,12 @@ def logit_tol(spec) -> float:
     return 1e-4 if spec.weight_dtype == "f32" else 2e-2
 
 
-def make_verifier(pw: PreparedWorkload, max_k: int, gemm_k_split: int = 0, max_ctx: Optional[int] = None):
+def make_verifier(pw: PreparedWorkload, max_k: int, gemm_k_split: int = 0, max_ctx: Optional[int] = None,
+                  n_seqs: int = 0, kv_page_seed: int = 0):
     K, V = kv_to_host_arrays(pw)
     stream = torch.cuda.current_stream().cuda_stream
-    return B.Verifier(pw.wl.spec, pw.W, K, V, pw.kv0.length, max_ctx or pw.max_ctx, max_k, stream, gemm_k_split)
+    return B.Verifier(pw.wl.spec, pw.W, K, V, pw.kv0.length, max_ctx or pw.max_ctx, max_k, stream, gemm_k_split,
+                      kv_page_seed, n_seqs)
 
 
 def gpu_step(h: B.Verifier, ri: RoundInputs, mode: str, vocab: int, trace_layers: int = 0):
