@@ -78,6 +78,8 @@ def parse():
     ap.add_argument("--reuse-cap", type=int, default=0,
                     help="MoE: verify with reuse-aware expert gating (lossy) over this many preferred experts")
     ap.add_argument("--reuse-alpha", type=float, default=0.5, help="bias scale of reuse-aware gating")
+    ap.add_argument("--batch", type=int, nargs="*", default=None, metavar="N",
+                    help="also verify N sequences per pass (k = 16/N - 1 each); default N in 2 4 8 16")
     ap.add_argument("--tree", action="store_true",
                     help="also run self-drafted token trees with routing-aware expansion (--draft self)")
     ap.add_argument("--adaptive-k", action="store_true",
@@ -128,7 +130,7 @@ class Session:
     """A verifier for one workload with its prompt prefilled on the GPU and
     the target's greedy continuation (the drafts' source) computed once."""
 
-    def __init__(self, wl, W, max_k: int, rounds: int, stream):
+    def __init__(self, wl, W, max_k: int, rounds: int, stream, n_seqs: int = 1):
         import numpy as np
         from target_model_verification_amd import binding as B
         from target_model_verification_amd import synth
@@ -140,7 +142,7 @@ class Session:
         self.n_ref = rounds * (max_k + 1) + 1
         self.max_ctx = wl.context + self.n_ref + 2 * (max_k + 1) + 64
         t = time.time()
-        self.h = B.Verifier(wl.spec, W, None, None, 0, self.max_ctx, 15, stream)
+        self.h = B.Verifier(wl.spec, W, None, None, 0, self.max_ctx, 15, stream, n_seqs=n_seqs)
         log(f"[bench] verifier created in {time.time() - t:.1f} s (max_ctx {self.max_ctx})")
         # prompt: appended in blocks of 16 (accept mode NONE commits the block)
         t = time.time()
@@ -420,6 +422,73 @@ def measure_tree(sess: Session, n: int, kd: int, warmup: int, steps: int):
                 steps=steps, **out)
 
 
+def measure_batch(sess: Session, n_seq: int, warmup: int, steps: int):
+    """n_seq sequences verified together (spec_verify_batch): each has its
+    own seeded prompt of the workload's context (appended on the GPU), its
+    own greedy continuation and corrupted drafts; the blocks share one pass
+    with k = 16 / n_seq - 1 drafts each.  Aggregate accepted tok/s over the
+    timed steps (wall clock per step, pass time from HIP events)."""
+    import dataclasses
+    import torch
+    from target_model_verification_amd import synth
+    np, B, h, wl = sess.np, sess.B, sess.h, sess.wl
+    k = 16 // n_seq - 1
+    seqs = list(range(n_seq))
+    wls = [wl] + [dataclasses.replace(wl, seed=wl.seed + 7919 * s) for s in range(1, n_seq)]
+    h.rollback(sess.L0)
+    pend = [sess.pending0]
+    for s in range(1, n_seq):   # prompts of the other sequences, 16 positions per pass
+        h.seq_rollback(s, 0)
+        prompt = synth.prompt_ids(wls[s])
+        res = None
+        for i in range(0, len(prompt), 16):
+            res = h.step_batch([s], [prompt[i:i + 16]], B.SPEC_ACCEPT_NONE)[0]
+        pend.append(int(res.next_token))
+    L0 = [h.seq_len(s) for s in seqs]
+    # every sequence's greedy continuation, all sequences one token per pass
+    n_ref = (warmup + steps) * (k + 1) + 1
+    ref = [[p] for p in pend]
+    for _ in range(n_ref):
+        out = h.step_batch(seqs, [[r[-1]] for r in ref], B.SPEC_ACCEPT_GREEDY)
+        for s in seqs:
+            ref[s].append(int(out[s].next_token))
+    for s in seqs:
+        h.seq_rollback(s, L0[s])
+    ref = [np.asarray(r, dtype=np.int64) for r in ref]
+    corr = [[synth.draft_corruption(wls[s], r, k) for r in range(warmup + steps)] for s in seqs]
+    pos = [0] * n_seq
+    acc, dt = 0, 0.0
+    per_seq = [0] * n_seq
+    for r in range(warmup + steps):
+        if r == warmup:
+            h.profile(2)
+        blocks = []
+        for s in seqs:
+            flags, ids = corr[s][r]
+            d = np.where(flags, ids, ref[s][pos[s] + 1:pos[s] + 1 + k])
+            blocks.append([int(ref[s][pos[s]])] + [int(x) for x in d])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        out = h.step_batch(seqs, blocks, B.SPEC_ACCEPT_GREEDY)
+        el = time.perf_counter() - t0
+        for s in seqs:
+            pos[s] += out[s].n_accepted + 1
+            if r >= warmup:
+                per_seq[s] += out[s].n_accepted + 1
+        if r >= warmup:
+            dt += el
+            acc += sum(o.n_accepted + 1 for o in out)
+    n_p, ms_p, by_p = h.profile_read()["pass"]
+    h.profile(0)
+    for s in range(1, n_seq):
+        h.seq_rollback(s, 0)
+    return dict(n_seq=n_seq, k=k, rows=n_seq * (k + 1), steps=steps, ms_per_step=round(dt / steps * 1e3, 4),
+                accepted_tok_s=round(acc / dt, 2), tokens_per_step=round(acc / steps, 4),
+                tokens_per_step_per_seq=[round(v / steps, 3) for v in per_seq],
+                us_per_pass=round(ms_p / n_p * 1e3, 1), pass_gb=round(by_p / n_p / 1e9, 4),
+                pass_hbm_frac=round(by_p / (ms_p / 1e3) / 1e9 / HBM_PEAK_GBS, 4))
+
+
 def reuse_quality(sess: Session, k: int, cap: int, alpha: float, n_blocks: int = 8):
     """Reuse-aware gating against the exact pass on the same blocks (untimed):
     experts loaded per layer and the output consistency metrics of S2-MoE
@@ -626,7 +695,9 @@ def main():
         f"{time.time() - t:.1f} s")
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
-        sess = Session(wl, W, 15 if args.adaptive_k else max(ks), args.warmup + args.steps, stream.cuda_stream)
+        n_seqs = max(args.batch or [2, 4, 8, 16]) if args.batch is not None else 1
+        sess = Session(wl, W, 15 if args.adaptive_k else max(ks), args.warmup + args.steps, stream.cuda_stream,
+                       n_seqs)
         if args.calib_copy:
             a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
             b = torch.empty_like(a)
@@ -719,6 +790,14 @@ def main():
         line["config"]["workload"] = line["config"]["workload"].replace(
             f"draft corruption {wl.corruption}", f"self-speculative draft with {args.draft_top_k} routed expert(s)")
         line["self_draft"] = {kk: round(v, 4) if isinstance(v, float) else v for kk, v in r["self_draft"].items()}
+    if args.batch is not None:
+        if wl.accept != "greedy" or args.draft != "synthetic":
+            raise SystemExit("--batch runs greedy rounds with the workload's synthetic drafts")
+        line["batch"] = {}
+        with torch.cuda.stream(stream):
+            for nb in (args.batch or [2, 4, 8, 16]):
+                line["batch"][str(nb)] = measure_batch(sess, nb, args.warmup, args.steps)
+                log(f"[bench] {nb} sequences per pass: {line['batch'][str(nb)]}")
     if args.tree:
         if args.draft != "self":
             raise SystemExit("--tree expands self-drafted candidates: use it with --draft self")

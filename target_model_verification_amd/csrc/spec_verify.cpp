@@ -1272,7 +1272,11 @@ int spec_verify_batch(spec_verify_t* h, int32_t n, const int32_t* seqs, const in
   p.row_rope = h->batch_dev + kBatchRope;
   p.row_lo = h->batch_dev + kBatchLo;
   p.row_hi = h->batch_dev + kBatchHi;
+  const bool moe = c.n_experts > 0;
+  if (h->profiling && moe) p.union_hist = h->union_dev_prof;
+  if (he == hipSuccess && h->profiling) he = hipEventRecord(h->ev[0], h->stream);
   if (he == hipSuccess) he = launch_counted(h, p);
+  if (he == hipSuccess && h->profiling) he = hipEventRecord(h->ev[1], h->stream);
   AcceptParams a{};
   a.k = m - 1; a.V = c.vocab; a.L = 0; a.n_stat = h->n_stat;
   a.mode = mode == SPEC_ACCEPT_GREEDY ? kAcceptBatchGreedy : kAcceptBatchNone;
@@ -1282,6 +1286,9 @@ int spec_verify_batch(spec_verify_t* h, int32_t n, const int32_t* seqs, const in
   a.logits = h->logits; a.ldl = h->ldl;
   a.result = h->batch_res;
   if (he == hipSuccess) he = launch_accept(a, h->stream);
+  if (he == hipSuccess && h->profiling && moe)
+    he = hipMemcpyAsync(h->union_host.data(), h->union_dev_prof, sizeof(int) * c.n_layers, hipMemcpyDeviceToHost,
+                        h->stream);
   if (he == hipSuccess)
     he = hipMemcpyAsync(h->batch_res_host, h->batch_res, sizeof(int) * 4 * n, hipMemcpyDeviceToHost, h->stream);
   if (he == hipSuccess)
@@ -1297,6 +1304,17 @@ int spec_verify_batch(spec_verify_t* h, int32_t n, const int32_t* seqs, const in
   if (h->result_host[3] != 0) {
     h->broken = true;
     return fail(h, SPEC_EHIP, "grid barrier wait timed out inside the pass");
+  }
+  if (h->profiling) {   // the pass's events; per-phase stamps are not taken for several sequences
+    float pass_ms = 0.f;
+    (void)hipEventElapsedTime(&pass_ms, h->ev[0], h->ev[1]);
+    long long experts_loaded = 0, sum_L = 0;
+    if (moe)
+      for (int l = 0; l < c.n_layers; ++l) experts_loaded += h->union_host[l];
+    for (int i = 0; i < n; ++i) sum_L += B[kBatchSeq + 3 * i + 2];
+    h->prof_launches[SPEC_K_PASS] += 1;
+    h->prof_ms[SPEC_K_PASS] += pass_ms;
+    h->prof_bytes[SPEC_K_PASS] += spec_pass_bytes(h, (int32_t)sum_L, m - 1, SPEC_ACCEPT_GREEDY, experts_loaded);
   }
   for (int i = 0; i < n; ++i) {
     out[i].n_accepted = h->batch_res_host[4 * i + 0];
