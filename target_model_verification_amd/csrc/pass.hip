@@ -408,6 +408,7 @@ struct QkvPre {
   float cs[4], sn[4];
   long long pg[4];
 };
+template <bool GEN>
 __device__ __forceinline__ void qkv_pre(const PassP& P, int unit, QkvPre& q) {
   const int lane = threadIdx.x & 63;
   const int col = unit * kTileN + (lane & 15), rg = lane >> 4;
@@ -419,8 +420,8 @@ __device__ __forceinline__ void qkv_pre(const PassP& P, int unit, QkvPre& q) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = min(4 * rg + i, P.m - 1);
-    const int t = P.row_slot ? P.row_slot[row] : P.L + row;   // cache slot
-    const int tp = P.row_rope ? P.row_rope[row] : t;          // rotary position
+    const int t = GEN && P.row_slot ? P.row_slot[row] : P.L + row;   // cache slot
+    const int tp = GEN && P.row_rope ? P.row_rope[row] : t;          // rotary position
     q.pg[i] = (long long)P.page_table[t / kPage] * P.Hkv;
     q.cs[i] = rot_col ? P.rope_cs[((long long)tp * H + ii) * 2 + 0] : 0.f;
     q.sn[i] = rot_col ? P.rope_cs[((long long)tp * H + ii) * 2 + 1] : 0.f;
@@ -429,7 +430,7 @@ __device__ __forceinline__ void qkv_pre(const PassP& P, int unit, QkvPre& q) {
 
 // Epilogue of one finished unit (one wave, acc[t] = tile t of the unit).
 // QKV takes the unit's rotary factors and pages (qkv_pre).
-template <int WF, int EPI, int TPU>
+template <int WF, int EPI, int TPU, bool GEN>
 __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const GemmIO& io, const float* rs, int slot,
                                          int unit, f32x4 (&acc)[TPU], const QkvPre* qp = nullptr) {
   // the lane index is made opaque here, so the compiler cannot hoist the
@@ -506,7 +507,7 @@ __device__ __forceinline__ void epilogue(const PassP& P, const Mat& M, const Gem
     for (int i = 0; i < 4; ++i) {
       const int row = 4 * rg + i;
       if (row < P.m && col < M.N) {
-        const int t = P.row_slot ? P.row_slot[row] : P.L + row;
+        const int t = GEN && P.row_slot ? P.row_slot[row] : P.L + row;
         if (rot_col) {
           const float a = odd ? pv[i] : v[i], b = odd ? v[i] : pv[i];   // x[ii], x[ii + H]
           const float rot = odd ? (b * cs[i] + a * sn[i]) : (a * cs[i] - b * sn[i]);
@@ -659,7 +660,7 @@ __device__ __forceinline__ void wait_window(const PassP& P, const GemmIO& io, in
 }
 
 // One weight-streaming phase over `sm.n_slots` slots (experts) of M.
-template <int WF, int EPI, int TPU>
+template <int WF, int EPI, int TPU, bool GEN>
 __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const GemmIO io, const SlotMap sm,
                                         bool slot_major, Ring& ring, unsigned char* smem, unsigned long long* wst) {
   using F = Fmt<WF, TPU>;
@@ -843,8 +844,8 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     if (live) {
       if (nseg == 1) {
         QkvPre qp;
-        if constexpr (EPI == EPI_QKV) qkv_pre(P, cc.sg * kWaves + wave, qp);
-        epilogue<WF, EPI, TPU>(P, M, io, C->rs, cc.slot, cc.sg * kWaves + wave, acc, &qp);
+        if constexpr (EPI == EPI_QKV) qkv_pre<GEN>(P, cc.sg * kWaves + wave, qp);
+        epilogue<WF, EPI, TPU, GEN>(P, M, io, C->rs, cc.slot, cc.sg * kWaves + wave, acc, &qp);
       } else {
         float* p = io.ws + ((((long long)cc.slot * M.n_sg + cc.sg) * M.max_seg + idx) * kWaves + wave) * TPU * 256;
 #pragma unroll
@@ -874,12 +875,53 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
   }
 
   wstamp(wst, 2);
-  // ---- split blocks: every workgroup announces its segments (no waiting),
-  // then reduces the blocks assigned to it (an even share of all blocks),
-  // summing their partials in K order once every segment is in
+  // ---- split blocks.  The partials of a block are summed in K order and
+  // the epilogue applied (by whichever workgroup reduces it: the result is
+  // the same bit for bit).
   release_all_waves();
   __syncthreads();
   const int np = C->pend_n;
+  constexpr int RB = TPU == 1 ? 16 : 8;   // partial loads in flight per lane (a block's usual count)
+  auto pre = [&](int sg, QkvPre& qp) {   // QKV: rotary factors and cache pages of the block's rows
+    if constexpr (EPI == EPI_QKV) {
+      if (sg * kWaves + wave < M.n_units) qkv_pre<GEN>(P, sg * kWaves + wave, qp);
+    }
+  };
+  auto reduce = [&](int s, int sg, int n, const QkvPre& qp) {
+    const int unit = sg * kWaves + wave;
+    if (unit < M.n_units) {
+      f32x4 sum[TPU];
+#pragma unroll
+      for (int t = 0; t < TPU; ++t) sum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const float* p = io.ws + ((((long long)s * M.n_sg + sg) * M.max_seg) * kWaves + wave) * TPU * 256 + lane * 4;
+      for (int j0 = 0; j0 < n; j0 += RB) {
+        f32x4 v[RB][TPU];
+#pragma unroll
+        for (int q = 0; q < RB; ++q) {
+#pragma unroll
+          for (int t = 0; t < TPU; ++t)
+            v[q][t] = j0 + q < n ? cld4(p + (long long)(j0 + q) * kWaves * TPU * 256 + t * 256)
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int q = 0; q < RB; ++q) {
+          if (j0 + q < n) {
+#pragma unroll
+            for (int t = 0; t < TPU; ++t) sum[t] += v[q][t];
+          }
+        }
+      }
+      epilogue<WF, EPI, TPU, GEN>(P, M, io, C->rs, s, unit, sum, &qp);
+    }
+    if (io.notify) {
+      release_all_waves();
+      __syncthreads();
+      if (threadIdx.x == 0) notify_block(P, io, sg);
+    }
+  };
+  // every workgroup announces its segments (no waiting), then reduces the
+  // blocks assigned to it (an even share of all blocks) once every segment
+  // of the block is in
   for (int k = threadIdx.x; k < np; k += kThreads) {
     const int e = C->pend[k];
     const int s = (e >> 20) & 0x7ff, sg = e & 0xfffff;
@@ -888,16 +930,13 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
   }
   const int nb = L.n_slots * M.n_sg;
   const int b0 = range_begin(nb, g, G), b1 = range_begin(nb, g + 1, G);
-  constexpr int RB = TPU == 1 ? 16 : 8;   // partial loads in flight per lane (a block's usual count)
   for (int b = b0; b < b1; ++b) {
     const int s = b / M.n_sg, sg = b - s * M.n_sg;
     int idx, n;
     seg_info(L, s, sg, 0, g, G, idx, n);
     if (n == 1) continue;   // finished inside the stream
     QkvPre qp;
-    if constexpr (EPI == EPI_QKV) {
-      if (sg * kWaves + wave < M.n_units) qkv_pre(P, sg * kWaves + wave, qp);
-    }
+    pre(sg, qp);            // (its loads in flight while polling)
     if (threadIdx.x == 0) {
       unsigned* t = io.tickets + b;
       unsigned spins = 0;
@@ -911,36 +950,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
       __hip_atomic_store(glb(t), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();   // the partials are read with agent-scope loads
-    const int unit = sg * kWaves + wave;
-    if (unit < M.n_units) {
-    f32x4 sum[TPU];
-#pragma unroll
-    for (int t = 0; t < TPU; ++t) sum[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const float* p = io.ws + ((((long long)s * M.n_sg + sg) * M.max_seg) * kWaves + wave) * TPU * 256 + lane * 4;
-    for (int j0 = 0; j0 < n; j0 += RB) {
-      f32x4 v[RB][TPU];
-#pragma unroll
-      for (int q = 0; q < RB; ++q) {
-#pragma unroll
-        for (int t = 0; t < TPU; ++t)
-          v[q][t] = j0 + q < n ? cld4(p + (long long)(j0 + q) * kWaves * TPU * 256 + t * 256)
-                               : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int q = 0; q < RB; ++q) {
-        if (j0 + q < n) {
-#pragma unroll
-          for (int t = 0; t < TPU; ++t) sum[t] += v[q][t];
-        }
-      }
-    }
-    epilogue<WF, EPI, TPU>(P, M, io, C->rs, s, unit, sum, &qp);
-    }
-    if (io.notify) {
-      release_all_waves();
-      __syncthreads();
-      if (threadIdx.x == 0) notify_block(P, io, sg);
-    }
+    reduce(s, sg, n, qp);
   }
 }
 
@@ -1169,7 +1179,7 @@ __device__ __forceinline__ void kv_mask(u4* w, int p0, int nvalid) {
 // bf16 values and one row tile the whole group is scored at once; otherwise
 // scores are recomputed per sub-chunk in the second pass -- the same
 // operations in the same order, so both give identical bits.
-template <bool KVF32, int MAXRT>
+template <bool KVF32, int MAXRT, bool GEN>
 __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const uint4* qf, uint4* a_o,
                                                 unsigned long long* ready, int dep, unsigned char* smem,
                                                 unsigned long long* wst) {
@@ -1274,7 +1284,7 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
     // scores of this wave's 16 keys of sub-chunk sc for row tile rt, masked
     auto scores = [&](int sc, int rt, const u4 (&kr)[4 * W]) -> f32x4 {
       const int t0 = gt0 + sc * kPage;
-      const int nkeys = P.page_live ? P.page_live[t0 / kPage] : min(kPage, T - t0);
+      const int nkeys = GEN && P.page_live ? P.page_live[t0 / kPage] : min(kPage, T - t0);
       f32x4 s4 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
@@ -1311,9 +1321,9 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
         // committed cache and the rows of its ancestor mask; several
         // sequences: the row's own slot interval
         bool seen = tk <= P.L + r / P.G;
-        if (P.tree_anc && tk >= P.L && tk - P.L < kMaxRows && r < R)
+        if (GEN && P.tree_anc && tk >= P.L && tk - P.L < kMaxRows && r < R)
           seen = ((P.tree_anc[r / P.G] >> (tk - P.L)) & 1u) != 0u;
-        if (P.row_hi && r < R) seen = tk >= P.row_lo[r / P.G] && tk <= P.row_hi[r / P.G];
+        if (GEN && P.row_hi && r < R) seen = tk >= P.row_lo[r / P.G] && tk <= P.row_hi[r / P.G];
         const bool vis = r < R && key < nkeys && seen;
         s4[i] = vis ? s4[i] : -INFINITY;
       }
@@ -1326,7 +1336,7 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
 #pragma unroll
       for (int q = 0; q < 2; ++q) acc[rt][q] = f32x4{0.f, 0.f, 0.f, 0.f};
     auto pv = [&](int sc, int pc, u4 (&vr)[2][2 * W]) {
-      const int nkeys = P.page_live ? P.page_live[gt0 / kPage + sc] : min(kPage, T - (gt0 + sc * kPage));
+      const int nkeys = GEN && P.page_live ? P.page_live[gt0 / kPage + sc] : min(kPage, T - (gt0 + sc * kPage));
       u4 vh[2][2], vl[2][2];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
@@ -1895,7 +1905,7 @@ __device__ __forceinline__ void stamp(const PassP& P, int ph) {
 // is inlined once, and the weight ring lives in registers for the whole
 // pass.  Dense and MoE models get separate instances, each holding only the
 // phase kinds its programs use (the kernel's code size shows in its speed).
-template <int WF, bool MOE>
+template <int WF, bool MOE, bool GEN>
 __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
   extern __shared__ __align__(16) unsigned char smem[];
   Ctl* C = ctl(smem, (size_t)P.lds_bytes);
@@ -1947,17 +1957,17 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
         if constexpr (!MOE) break;
         const SlotMap sm = d->slot_mode ? slots : dense;
         sync([&] { gemm_prefetch<WF, 1>(d->M, sm, d->slot_mode == 2, ring); });
-        gemm_phase<WF, EPI_STORE, 1>(P, d->M, io, sm, d->slot_mode == 2, ring, smem, wst);
+        gemm_phase<WF, EPI_STORE, 1, GEN>(P, d->M, io, sm, d->slot_mode == 2, ring, smem, wst);
         break;
       }
       case PH_QKV:
         sync([&] { gemm_prefetch<WF, 1>(d->M, dense, false, ring); });
         io.kv = d->kv;
-        gemm_phase<WF, EPI_QKV, 1>(P, d->M, io, dense, false, ring, smem, wst);
+        gemm_phase<WF, EPI_QKV, 1, GEN>(P, d->M, io, dense, false, ring, smem, wst);
         break;
       case PH_RESID:
         sync([&] { gemm_prefetch<WF, 1>(d->M, dense, false, ring); });
-        gemm_phase<WF, EPI_RESID, 1>(P, d->M, io, dense, false, ring, smem, wst);
+        gemm_phase<WF, EPI_RESID, 1, GEN>(P, d->M, io, dense, false, ring, smem, wst);
         break;
       case PH_ROUTE_SWIGLU:
         if constexpr (!MOE) break;
@@ -1973,23 +1983,23 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
         route_block(P, d->bias, smem, d->layer, zl);
         const SlotMap routed{C->ulist, C->uc, P.E, C->uc + P.n_shared};   // the union just built
         gemm_prefetch<WF, 2>(d->M, routed, false, ring);
-        gemm_phase<WF, EPI_SWIGLU, 2>(P, d->M, io, routed, false, ring, smem, wst);
+        gemm_phase<WF, EPI_SWIGLU, 2, GEN>(P, d->M, io, routed, false, ring, smem, wst);
         break;
       }
       case PH_SWIGLU:
         if constexpr (MOE) break;
         sync([&] { gemm_prefetch<WF, 2>(d->M, dense, false, ring); });
-        gemm_phase<WF, EPI_SWIGLU, 2>(P, d->M, io, dense, false, ring, smem, wst);
+        gemm_phase<WF, EPI_SWIGLU, 2, GEN>(P, d->M, io, dense, false, ring, smem, wst);
         break;
       case PH_LOGITS:
         sync([&] { gemm_prefetch<WF, 1>(d->M, dense, false, ring); });
-        gemm_phase<WF, EPI_LOGITS, 1>(P, d->M, io, dense, false, ring, smem, wst);
+        gemm_phase<WF, EPI_LOGITS, 1, GEN>(P, d->M, io, dense, false, ring, smem, wst);
         break;
       case PH_ATTN:
         sync([] {});
         wstamp(wst, 1);
         wstamp(wst, 2);
-        attention_phase<WF == W_F32, 1>(P, d->kv, d->a, d->a_out, io.ready, io.dep, smem, wst);
+        attention_phase<WF == W_F32, 1, GEN>(P, d->kv, d->a, d->a_out, io.ready, io.dep, smem, wst);
         break;
       case PH_ATTN_MERGE:
         if (P.attn_inline) {
@@ -2026,26 +2036,38 @@ size_t pass_lds_bytes(int wfmt, int max_rows_attn, int D) {
   return b + kCtlBytes;
 }
 
-static const void* pick(int wfmt, bool moe) {
-  if (wfmt == W_F32) return moe ? reinterpret_cast<const void*>(&k_pass<W_F32, true>)
-                                : reinterpret_cast<const void*>(&k_pass<W_F32, false>);
-  if (wfmt == W_BF16) return moe ? reinterpret_cast<const void*>(&k_pass<W_BF16, true>)
-                                 : reinterpret_cast<const void*>(&k_pass<W_BF16, false>);
-  if (wfmt == W_INT4) return moe ? reinterpret_cast<const void*>(&k_pass<W_INT4, true>)
-                                 : reinterpret_cast<const void*>(&k_pass<W_INT4, false>);
+// The pass kernel for a weight format and model kind; gen: the instance
+// that reads per-row placement (token trees, several sequences).
+static const void* pick(int wfmt, bool moe, bool gen) {
+#define SV_PICK(W)                                                                                    \
+  return moe ? (gen ? reinterpret_cast<const void*>(&k_pass<W, true, true>)                         \
+                    : reinterpret_cast<const void*>(&k_pass<W, true, false>))                       \
+             : (gen ? reinterpret_cast<const void*>(&k_pass<W, false, true>)                        \
+                    : reinterpret_cast<const void*>(&k_pass<W, false, false>))
+  if (wfmt == W_F32) SV_PICK(W_F32);
+  if (wfmt == W_BF16) SV_PICK(W_BF16);
+  if (wfmt == W_INT4) SV_PICK(W_INT4);
+#undef SV_PICK
   return nullptr;
 }
 
 hipError_t pass_occupancy(int wfmt, bool moe, size_t lds, int* blocks_per_cu) {
-  const void* f = pick(wfmt, moe);
-  if (!f) return hipErrorInvalidValue;
+  const void* f = pick(wfmt, moe, false);
+  const void* fg = pick(wfmt, moe, true);
+  if (!f || !fg) return hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e == hipSuccess) e = hipFuncSetAttribute(fg, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, f, kThreads, lds);
+  int a = 0, b = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&a, f, kThreads, lds);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, fg, kThreads, lds);
+  *blocks_per_cu = a < b ? a : b;
+  return e;
 }
 
 hipError_t launch_pass(int wfmt, bool moe, const PassP& p, int n_wg, size_t lds, hipStream_t s) {
-  const void* f = pick(wfmt, moe);
+  const bool gen = p.row_slot || p.row_rope || p.row_lo || p.row_hi || p.page_live || p.tree_anc;
+  const void* f = pick(wfmt, moe, gen);
   if (!f) return hipErrorInvalidValue;
   PassP q = p;
   void* args[] = {&q};
