@@ -669,7 +669,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
   const int G = gridDim.x, g = blockIdx.x;
   Ctl* C = ctl(smem, (size_t)P.lds_bytes);
   const Lin L = make_lin(M, sm.n_slots, slot_major, sm.ulist, sm.uc, sm.n_experts);
-  const int u0 = range_begin(L.total, g, G), u1 = range_begin(L.total, g + 1, G);
+  const int u0 = run_begin(L, g, G), u1 = run_begin(L, g + 1, G);
 
   if (threadIdx.x == 0) C->pend_n = 0;
   // the A window of the range's first block (a range that crosses into
@@ -961,7 +961,7 @@ template <int WF, int TPU>
 __device__ __forceinline__ void gemm_prefetch(const Mat M, const SlotMap sm, bool slot_major, Ring& ring) {
   const int G = gridDim.x, g = blockIdx.x;
   const Lin L = make_lin(M, sm.n_slots, slot_major, sm.ulist, sm.uc, sm.n_experts);
-  const int u0 = range_begin(L.total, g, G), u1 = range_begin(L.total, g + 1, G);
+  const int u0 = run_begin(L, g, G), u1 = run_begin(L, g + 1, G);
   if (u0 >= u1) {
 #pragma unroll
     for (int i = 0; i < kRing; ++i) {   // nothing to stream: a defined, unused ring

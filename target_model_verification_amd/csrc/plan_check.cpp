@@ -57,7 +57,7 @@ bool check_gemm_walk(const GemmShape& s, int G, size_t ws_floats, size_t n_ticke
     std::map<std::pair<int, int>, int> announced;             // (slot, sg) -> segment count
 
     for (int g = 0; g < G; ++g) {
-      const int u0 = range_begin(L.total, g, G), u1 = range_begin(L.total, g + 1, G);
+      const int u0 = run_begin(L, g, G), u1 = run_begin(L, g + 1, G);
       if (u0 >= u1) continue;
       const std::string where = at(s, n_slots, g, G);
       auto fail = [&](const std::string& m) {

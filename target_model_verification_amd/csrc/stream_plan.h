@@ -4,11 +4,17 @@
 // launch).
 //
 // A phase over n_slots slots (experts) of one matrix is a flat space of
-// units (slot, window, supergroup, chunk); workgroup g of G owns the run
-// [floor(T g / G), floor(T (g+1) / G)) of the T units.  A "segment" is the
-// part of one (slot, window, supergroup) run of chunks that one workgroup
-// owns; a unit block (slot, supergroup) whose K range is split over several
-// segments is reduced by the last workgroup to arrive, in K order.
+// units (slot, window, supergroup, chunk).  Each (slot, window, supergroup)
+// run of chunks is cut into pieces of U chunks (one weight batch of a wave;
+// the last piece of a run may be shorter), and workgroup g of G owns the
+// pieces [floor(P g / G), floor(P (g+1) / G)) of the P pieces: every
+// workgroup's share starts and ends on a batch boundary, so it streams in
+// the fewest batches its share allows (cutting the flat space into equal
+// runs of chunks instead leaves partial batches at segment ends, and the
+// workgroups with more of them stream longer).  A "segment" is the part of
+// one (slot, window, supergroup) run that one workgroup owns; a unit block
+// (slot, supergroup) whose K range is split over several segments is
+// reduced in K order by a fixed reducer.
 #pragma once
 #include "sv_common.h"
 
@@ -29,6 +35,8 @@ struct Lin {
   int n_slots, n_sg, nkc, W, n_win;
   bool slot_major;
   int total;          // units in the phase (fits in 32 bits for every supported shape)
+  int U, npW, npL;    // chunks per piece; pieces per run of a full / of the last window
+  int P;              // pieces in the phase
   const int* ulist;   // MoE: routed experts of the pass in slot order (null: dense phase)
   int uc, n_experts;
   // expert (stack index) of a slot: routed experts first, then the shared ones
@@ -39,6 +47,35 @@ struct Lin {
   SP_HD int block_start(int slot, int win) const {
     if (slot_major) return slot * n_sg * nkc + n_sg * W * win;
     return n_slots * n_sg * W * win + slot * n_sg * wlen(win);
+  }
+  SP_HD int np(int win) const { return win == n_win - 1 ? npL : npW; }
+  // first piece of the run (slot, win, supergroup 0)
+  SP_HD int piece_start(int slot, int win) const {
+    if (slot_major) return slot * n_sg * ((n_win - 1) * npW + npL) + n_sg * npW * win;
+    return n_slots * n_sg * npW * win + slot * n_sg * np(win);
+  }
+  // first chunk of piece p (total for p = P)
+  SP_HD int piece_chunk(int p) const {
+    if (p >= P) return total;
+    int slot, win, r;
+    if (slot_major) {
+      const int per_slot = n_sg * ((n_win - 1) * npW + npL);
+      slot = p / per_slot;
+      r = p - slot * per_slot;
+      win = r / (n_sg * npW);
+      if (win > n_win - 1) win = n_win - 1;
+      r -= n_sg * npW * win;
+    } else {
+      const int per_win = n_slots * n_sg * npW;
+      win = p / per_win;
+      if (win > n_win - 1) win = n_win - 1;
+      r = p - per_win * win;
+      const int per_slot = n_sg * np(win);
+      slot = r / per_slot;
+      r -= slot * per_slot;
+    }
+    const int sg = r / np(win), q = r - sg * np(win);
+    return block_start(slot, win) + sg * wlen(win) + q * U;
   }
 };
 
@@ -55,6 +92,10 @@ SP_HD Lin make_lin(const Mat& M, int n_slots, bool slot_major, const int* ulist 
   L.n_win = M.n_win;
   L.slot_major = slot_major;
   L.total = n_slots * M.n_sg * M.nkc;
+  L.U = M.U;
+  L.npW = (L.W + L.U - 1) / L.U;
+  L.npL = (L.wlen(L.n_win - 1) + L.U - 1) / L.U;
+  L.P = n_slots * M.n_sg * ((L.n_win - 1) * L.npW + L.npL);
   return L;
 }
 
@@ -77,6 +118,9 @@ SP_HD int range_begin(int total, int g, int G) { return floor_div((long long)tot
 
 // Workgroup owning unit u (the largest g with range_begin(g) <= u).
 SP_HD int wg_of(int u, int T, int G) { return floor_div(((long long)u + 1) * G - 1, T); }
+
+// First chunk of workgroup g's share (run_begin(L, G, G) = L.total).
+SP_HD int run_begin(const Lin& L, int g, int G) { return L.piece_chunk(range_begin(L.P, g, G)); }
 
 // Position in the flattened space (advanced a segment at a time without
 // divisions).
@@ -113,21 +157,21 @@ SP_HD Cur cur_at(const Lin& L, int u) {
 
 // Split-K bookkeeping of unit block (slot, sg): number of segments over all
 // windows and workgroups, and the index of the segment (win, g) in K order.
-// With at least as many units as workgroups every workgroup owns a
-// non-empty run, so the workgroups covering an interval are consecutive;
-// with fewer, each owns at most one unit and a unit's owner is unique.
+// With at least as many pieces as workgroups every workgroup owns a
+// non-empty share, so the workgroups covering a run are consecutive; with
+// fewer, each owns at most one piece and a piece's owner is unique.
 SP_HD void seg_info(const Lin& L, int slot, int sg, int win, int g, int G, int& idx, int& n) {
   n = 0;
   idx = 0;
-  const bool sparse = L.total < G;
+  const bool sparse = L.P < G;
   for (int w = 0; w < L.n_win; ++w) {
-    const int a = L.block_start(slot, w) + sg * L.wlen(w);
-    const int b = a + L.wlen(w) - 1;
+    const int a = L.piece_start(slot, w) + sg * L.np(w);
+    const int b = a + L.np(w) - 1;
     if (sparse) {
-      if (w == win) idx = n + (range_begin(L.total, g, G) - a);
-      n += L.wlen(w);
+      if (w == win) idx = n + (range_begin(L.P, g, G) - a);
+      n += L.np(w);
     } else {
-      const int ga = wg_of(a, L.total, G), gb = wg_of(b, L.total, G);
+      const int ga = wg_of(a, L.P, G), gb = wg_of(b, L.P, G);
       if (w == win) idx = n + (g - ga);
       n += gb - ga + 1;
     }
@@ -196,6 +240,7 @@ inline void mat_geometry(Mat& M, int wf, int K, int N, int n_units, int tpu, int
   M.w_stride = frags * 1024;
   M.w2_stride = wf == W_INT4 ? frags * 32 : (wf == W_F32 ? M.w_stride : 0);
   M.max_seg = 1;
+  M.U = batch_chunks(wf, tpu);
 }
 
 // Largest number of split-K segments of one unit block, and the largest
@@ -209,10 +254,8 @@ inline void seg_bounds(const Mat& M, int n_slots, bool slot_major, int G, int& m
       seg_info(L, s, sg, 0, 0, G, idx, n);
       if (n > max_seg) max_seg = n;
     }
-  const long long range = ((long long)L.total + G - 1) / G;
-  const int last = L.wlen(L.n_win - 1);
-  const int min_len = last < L.W ? last : L.W;
-  max_pend = (int)(range / (min_len > 0 ? min_len : 1)) + 2;
+  // a share of at most ceil(P / G) pieces meets at most that many runs
+  max_pend = (int)(((long long)L.P + G - 1) / G) + 2;
 }
 
 // One weight-streaming phase shape of a pass, with what its walk may touch.

@@ -51,6 +51,7 @@ struct Mat {
   int n_win;              // ceil(nkc / win)
   int K, N;               // logical shape (N: output columns; SwiGLU: activation columns)
   int max_seg;            // workspace slots per unit block (split-K partials)
+  int U;                  // chunks per weight batch of one wave (a piece of the work split)
 };
 
 // One phase of the pass program (a grid barrier separates consecutive
