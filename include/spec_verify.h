@@ -91,7 +91,11 @@ typedef struct {
                             its own cache of max_ctx positions and committed length;
                             sequence 0 is the one the single-sequence calls work on, the
                             others are stepped by spec_verify_batch. */
-  int32_t reserved[5];   /* must be zero */
+  int32_t attn_group_pages; /* cache pages per attention work item: 0 = chosen per pass (3,
+                            or 5 or 6 when fewer, longer items fit the grid in one round);
+                            3, 5 or 6 = fixed (bf16 / int4 models; fp32 models take 3).
+                            Results agree to rounding; a test knob. */
+  int32_t reserved[4];   /* must be zero */
 } spec_config;
 
 /* Weight tensor kinds.  Matrices are row-major [K][N] with y = x . W. */

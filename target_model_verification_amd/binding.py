@@ -34,7 +34,7 @@ class SpecConfig(ctypes.Structure):
                [("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("max_ctx", ctypes.c_int32), ("max_k", ctypes.c_int32), ("gemm_k_split", ctypes.c_int32),
                 ("kv_page_seed", ctypes.c_int32), ("n_seqs", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 5)]
+                ("attn_group_pages", ctypes.c_int32), ("reserved", ctypes.c_int32 * 4)]
 
 
 class SpecTensor(ctypes.Structure):
@@ -143,7 +143,7 @@ _DT = {"f32": SPEC_DT_F32, "bf16": SPEC_DT_BF16, "int4g128": SPEC_DT_INT4G128}
 
 
 def make_config(spec, max_ctx: int, max_k: int, gemm_k_split: int = 0, kv_page_seed: int = 0,
-                n_seqs: int = 0) -> SpecConfig:
+                n_seqs: int = 0, attn_group_pages: int = 0) -> SpecConfig:
     c = SpecConfig()
     c.n_layers, c.d_model = spec.n_layers, spec.d_model
     c.n_q_heads, c.n_kv_heads, c.head_dim = spec.n_q_heads, spec.n_kv_heads, spec.head_dim
@@ -154,6 +154,7 @@ def make_config(spec, max_ctx: int, max_k: int, gemm_k_split: int = 0, kv_page_s
     c.max_ctx, c.max_k, c.gemm_k_split = max_ctx, max_k, gemm_k_split
     c.kv_page_seed = kv_page_seed
     c.n_seqs = n_seqs
+    c.attn_group_pages = attn_group_pages
     return c
 
 
@@ -203,9 +204,9 @@ class Verifier:
 
     def __init__(self, spec, W, prompt_k: Optional[np.ndarray], prompt_v: Optional[np.ndarray],
                  prompt_len: int, max_ctx: int, max_k: int, stream: int = 0, gemm_k_split: int = 0,
-                 kv_page_seed: int = 0, n_seqs: int = 0):
+                 kv_page_seed: int = 0, n_seqs: int = 0, attn_group_pages: int = 0):
         self.spec = spec
-        self.cfg = make_config(spec, max_ctx, max_k, gemm_k_split, kv_page_seed, n_seqs)
+        self.cfg = make_config(spec, max_ctx, max_k, gemm_k_split, kv_page_seed, n_seqs, attn_group_pages)
         tens, keep = make_tensors(W)
         pk = pv = None
         if prompt_len > 0:

@@ -1001,7 +1001,7 @@ __device__ __forceinline__ void embed_phase(const PassP& P, bool emb_f32, uint4*
 }
 
 // ------------------------------------------------------------ attention
-// Work item (kv head g, group of kGroupPos positions); block rows
+// Work item (kv head g, group of GP pages of positions); block rows
 // r = j*G + hh (block row j, query head g*G + hh) see positions t <= L + j.
 // The group is walked in kPage sub-chunks with a running (max, sum, output)
 // per row: S = Q K^T and O += P V on MFMA (Q and P split into bf16 hi + lo;
@@ -1034,10 +1034,11 @@ constexpr int kPsStride = kPage + 4;         // floats per score row in LDS
 
 // LDS of the attention phase: Q fragments [RT][D/32][hi|lo][64 lanes],
 // scores / probabilities [RT*16][kPsStride], running max / sum / rescale.
-// (two-pass path; the one-row-tile path needs 16 rows of kGroupPos + 4)
+// (two-pass path; the one-row-tile path needs 16 rows of a whole group of
+// the largest size + 4)
 __host__ __device__ constexpr size_t attn_lds_bytes(int rt, int D) {
   return (size_t)rt * (D / 32) * 2 * 1024 + (size_t)rt * 16 * kPsStride * 4 + (size_t)3 * rt * 16 * 4 +
-         (size_t)16 * (kGroupPos + 4) * 4;
+         (size_t)16 * (kPage * kMaxGroupPages + 4) * 4;
 }
 
 // One output element (row r, dim d) of KV head g: the groups' partials
@@ -1179,13 +1180,13 @@ __device__ __forceinline__ void kv_mask(u4* w, int p0, int nvalid) {
 // bf16 values and one row tile the whole group is scored at once; otherwise
 // scores are recomputed per sub-chunk in the second pass -- the same
 // operations in the same order, so both give identical bits.
-template <bool KVF32, int MAXRT, bool GEN>
+template <bool KVF32, int MAXRT, bool GEN, int GP>
 __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const uint4* qf, uint4* a_o,
                                                 unsigned long long* ready, int dep, unsigned char* smem,
                                                 unsigned long long* wst) {
   constexpr int W = KVF32 ? 2 : 1;                    // 16-byte words per 8 cache elements
   constexpr bool ONE = !KVF32 && MAXRT == 1;          // the whole group at once
-  constexpr int NPF = ONE ? kGroupPages : 1;          // sub-chunks whose operands are loaded together
+  constexpr int NPF = ONE ? GP : 1;                   // sub-chunks whose operands are loaded together
   const int D = P.D, KDC = D / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   Ctl* C = ctl(smem, (size_t)P.lds_bytes);
@@ -1193,7 +1194,7 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
   const int NRT = (R + 15) >> 4;   // row tiles per KV head: one per work item
   const int RT = MAXRT;            // row tiles of this item
   const int T = P.T;
-  constexpr int PSW = (ONE ? kGroupPos : kPage) + 4;  // floats per score row
+  constexpr int PSW = (ONE ? GP * kPage : kPage) + 4;  // floats per score row
   u4* Qf = reinterpret_cast<u4*>(smem);                              // [RT][KDC][2][64] (two-pass path)
   float* Ps = reinterpret_cast<float*>(smem + (size_t)RT * KDC * 2 * 1024);   // [RT*16][PSW]
   float* mrun = Ps + RT * 16 * PSW;
@@ -1222,8 +1223,8 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
     }
     const int g = pair / P.n_groups, grp = pair % P.n_groups;
     const int rb = rt0 * 16;   // first block row of this item
-    const int gt0 = grp * kGroupPos;
-    const int nsc = min(kGroupPages, (T - gt0 + kPage - 1) / kPage);   // sub-chunks holding positions
+    const int gt0 = grp * GP * kPage;
+    const int nsc = min(GP, (T - gt0 + kPage - 1) / kPage);   // sub-chunks holding positions
     // waits until this KV head's query fragments and new cache rows are written
     auto wait_head = [&]() {
       if (dep == kDepHeads) {
@@ -1256,9 +1257,9 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
     // operand words of one sub-chunk: keys 16*wave.. of this lane (scores)
     // and values of this wave's d tiles (output)
     // pages of the group's sub-chunks, looked up together
-    int phys[kGroupPages];
+    int phys[GP];
 #pragma unroll
-    for (int sc = 0; sc < kGroupPages; ++sc) phys[sc] = P.page_table[min(gt0 / kPage + sc, (T - 1) / kPage)];
+    for (int sc = 0; sc < GP; ++sc) phys[sc] = P.page_table[min(gt0 / kPage + sc, (T - 1) / kPage)];
     auto load_ops = [&](int sc, u4 (&kr)[4 * W], u4 (&vr)[2][2 * W]) {
       const long long kb = (((long long)phys[sc] * P.Hkv + g) * 2 + 0) * kPage * D;
       const long long vb = kb + (long long)kPage * D;
@@ -1434,9 +1435,9 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
         for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
         if ((tid & 15) == 0) mrun[srow] = mx;
         // per-sub-chunk sums (the four trees interleaved), added in order
-        float ls[kGroupPages];
+        float ls[GP];
 #pragma unroll
-        for (int sc = 0; sc < kGroupPages; ++sc) {
+        for (int sc = 0; sc < GP; ++sc) {
           ls[sc] = 0.f;
           if (sc < nsc) {
 #pragma unroll
@@ -1452,7 +1453,7 @@ __device__ __forceinline__ void attention_phase(const PassP& P, void* kv, const 
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1)
 #pragma unroll
-          for (int sc = 0; sc < kGroupPages; ++sc) ls[sc] += __shfl_xor(ls[sc], o, 64);
+          for (int sc = 0; sc < GP; ++sc) ls[sc] += __shfl_xor(ls[sc], o, 64);
         float l = 0.f;
         for (int sc = 0; sc < nsc; ++sc) l += ls[sc];
         if ((tid & 15) == 0) lrun[srow] = l;
@@ -1999,7 +2000,13 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
         sync([] {});
         wstamp(wst, 1);
         wstamp(wst, 2);
-        attention_phase<WF == W_F32, 1, GEN>(P, d->kv, d->a, d->a_out, io.ready, io.dep, smem, wst);
+        // (fp32 caches: groups of 3 pages only)
+        if (WF != W_F32 && P.group_pages == 6)
+          attention_phase<WF == W_F32, 1, GEN, 6>(P, d->kv, d->a, d->a_out, io.ready, io.dep, smem, wst);
+        else if (WF != W_F32 && P.group_pages == 5)
+          attention_phase<WF == W_F32, 1, GEN, 5>(P, d->kv, d->a, d->a_out, io.ready, io.dep, smem, wst);
+        else
+          attention_phase<WF == W_F32, 1, GEN, kGroupPages>(P, d->kv, d->a, d->a_out, io.ready, io.dep, smem, wst);
         break;
       case PH_ATTN_MERGE:
         if (P.attn_inline) {

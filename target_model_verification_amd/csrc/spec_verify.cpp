@@ -212,8 +212,11 @@ bool check_cfg(const spec_config* c, std::string& msg) {
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return bad("rope_theta must be > 0 and rms_eps >= 0");
   if (c->gemm_k_split < 0 || c->gemm_k_split % 128 != 0 || c->gemm_k_split > 2048)
     return bad("gemm_k_split must be a multiple of 128 in [0, 2048]");
-  for (int i = 0; i < 5; ++i)
+  for (int i = 0; i < 4; ++i)
     if (c->reserved[i] != 0) return bad("reserved fields must be zero");
+  if (c->attn_group_pages != 0 && c->attn_group_pages != 3 && c->attn_group_pages != 5 && c->attn_group_pages != 6)
+    return bad("attn_group_pages must be 0, 3, 5 or 6");
+  if (c->weight_dtype == SPEC_DT_F32 && c->attn_group_pages > 3) return bad("fp32 models take 3-page groups");
   if (c->n_seqs < 0 || c->n_seqs > 64) return bad("n_seqs must be in [0, 64]");
   const bool moe = c->n_experts > 0;
   if (moe) {
@@ -881,7 +884,20 @@ PassP pass_params(const spec_verify* h, int m, int L, const int* tokens_dev, int
   p.D = c.head_dim; p.V = c.vocab; p.G = c.n_q_heads / c.n_kv_heads; p.E = c.n_experts; p.top_k = top_k;
   p.n_shared = c.n_shared; p.F = moe ? c.d_ff_expert : c.d_ff;
   p.T = T >= 0 ? T : L + m;
-  p.n_groups = cdiv(p.T, kGroupPos);
+  // attention work items (KV head, group, 16-row tile): groups of 3 pages,
+  // or of 5 or 6 when that is what keeps every item in one round over the
+  // grid (more items than workgroups run in two rounds, each item waiting
+  // on its loads); fp32 caches keep 3
+  const int n_rt = cdiv(m * p.G, 16);
+  p.group_pages = kGroupPages;
+  if (c.attn_group_pages > 0)
+    p.group_pages = c.attn_group_pages;
+  else if (h->wfmt != W_F32)
+    for (int gp : {kGroupPages, 5, 6}) {
+      p.group_pages = gp;
+      if ((long long)c.n_kv_heads * cdiv(p.T, gp * kPage) * n_rt <= h->n_wg) break;
+    }
+  p.n_groups = cdiv(p.T, p.group_pages * kPage);
   // heads whose merge is small are merged by their last attention item;
   // the merge phases (one per layer) then run without a barrier
   p.attn_inline = (long long)m * p.G * c.head_dim * p.n_groups <= kInlineMergeElems ? 1 : 0;

@@ -23,8 +23,9 @@ constexpr int kChunkK = 32;           // k per bf16 / fp32 fragment
 constexpr int kGroupK = 128;          // int4: k per fragment (= scale group)
 constexpr int kMaxRows = 16;          // block rows (k+1) per pass
 constexpr int kPage = 64;             // KV page (positions); attention sub-chunk
-constexpr int kGroupPages = 3;        // pages per attention work item (fixed grid)
+constexpr int kGroupPages = 3;        // pages per attention work item: the smallest group size
 constexpr int kGroupPos = kPage * kGroupPages;
+constexpr int kMaxGroupPages = 6;     // the largest (a pass takes 3, 5 or 6, see group_pages)
 constexpr int kMaxAttnRows = 128;     // (k+1) * (n_q_heads / n_kv_heads) per KV head
 constexpr int kAttnRT = kMaxAttnRows / 16;   // attention row tiles per KV head at most
 constexpr long long kInlineMergeElems = 16384;   // rows * head_dim * groups merged by one workgroup
@@ -159,6 +160,7 @@ struct PassP {
   const int* page_live;
   const unsigned* tree_anc;
   int T;                     // slots the attention reads: L + m (one sequence) or the batch's extent
+  int group_pages;           // pages per attention group (3, 5 or 6; the host picks it per pass)
   unsigned long long* stamps;   // [n_phases + 1] wall clock at phase ends (workgroup 0)
   unsigned long long* wstamps;  // [n_phases][n_wg][4] per-workgroup phase stamps (nullable)
 };

@@ -29,11 +29,11 @@ def logit_tol(spec) -> float:
 
 
 def make_verifier(pw: PreparedWorkload, max_k: int, gemm_k_split: int = 0, max_ctx: Optional[int] = None,
-                  n_seqs: int = 0, kv_page_seed: int = 0):
+                  n_seqs: int = 0, kv_page_seed: int = 0, attn_group_pages: int = 0):
     K, V = kv_to_host_arrays(pw)
     stream = torch.cuda.current_stream().cuda_stream
     return B.Verifier(pw.wl.spec, pw.W, K, V, pw.kv0.length, max_ctx or pw.max_ctx, max_k, stream, gemm_k_split,
-                      kv_page_seed, n_seqs)
+                      kv_page_seed, n_seqs, attn_group_pages)
 
 
 def gpu_step(h: B.Verifier, ri: RoundInputs, mode: str, vocab: int, trace_layers: int = 0):
