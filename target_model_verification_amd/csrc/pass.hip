@@ -662,7 +662,8 @@ __device__ __forceinline__ void wait_window(const PassP& P, const GemmIO& io, in
 // One weight-streaming phase over `sm.n_slots` slots (experts) of M.
 template <int WF, int EPI, int TPU, bool GEN>
 __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const GemmIO io, const SlotMap sm,
-                                        bool slot_major, Ring& ring, unsigned char* smem, unsigned long long* wst) {
+                                        bool slot_major, Ring& ring, unsigned char* smem, unsigned long long* wst,
+                                        bool staged = false) {
   using F = Fmt<WF, TPU>;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -675,15 +676,19 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
   // the A window of the range's first block (a range that crosses into
   // another (key, window) restages: a few workgroups per phase), with the
   // row scales' loads in flight at the same time
+  // (staged: window 0 of a shared A and its row scales are already in LDS)
   int sk = -1, sw = -1;
   if (u0 < u1) {
     const Cur a = cur_at(L, u0);
     sk = slot_major ? a.slot : 0;
     sw = a.win;
-    wait_window(P, io, sw);
-    stage_window<WF>(L, io, sk, sw, smem);
+    if (!(staged && sk == 0 && sw == 0)) {
+      wait_window(P, io, sw);
+      stage_window<WF>(L, io, sk, sw, smem);
+    }
   }
-  if (EPI == EPI_SWIGLU || EPI == EPI_LOGITS || EPI == EPI_QKV || (EPI == EPI_STORE && io.scale)) row_scales(P, io.ss_in, C->rs);
+  if ((EPI == EPI_SWIGLU || EPI == EPI_LOGITS || EPI == EPI_QKV || (EPI == EPI_STORE && io.scale)) && !staged)
+    row_scales(P, io.ss_in, C->rs);
   __builtin_amdgcn_s_waitcnt(0);   // the window's direct loads
   __syncthreads();
   float* const S4 = reinterpret_cast<float*>(smem + kAWindowBytes);   // int4 row sums
@@ -1580,10 +1585,15 @@ __device__ __forceinline__ void attn_merge_phase(const PassP& P, uint4* a_o, uns
 }
 
 // ------------------------------------------------------------ MoE routing
-// LDS of routing: used / sel / selw / probabilities from offset 0, the
-// block's router logits (when computed in the phase) from kRouteZl; both
-// inside the (then dead) A window.
-constexpr int kRouteZl = 32 * 1024;
+// LDS of routing, after the A window (which stays staged for the routed
+// gate/up phase, whose A operand is the router's): used / slot of each
+// expert [256], sel [16][16], selw [16][16], reuse-gating scratch, then one
+// [16][E] float area that holds the block's router logits (when computed in
+// the phase), then the reuse-gating logits, then the probabilities (rows
+// padded to a multiple of 4).
+constexpr int kRouteBase = kAWindowBytes + 1024;   // after the int4 row sums
+constexpr int kRouteZl = kRouteBase + 6 * 1024;
+constexpr int kRouteBytes = 6 * 1024 + 16 * 256 * 4;
 // Every workgroup routes the block redundantly (same inputs, same order):
 // pi = softmax(r + b) over the experts, each row keeps its top_k experts by
 // probability (ties to the lower id), weights = those probabilities; the
@@ -1636,7 +1646,6 @@ __device__ __forceinline__ void router_logits(const PassP& P, const Mat& Mr, con
       acc[j] = a4;
     }
   }
-  __syncthreads();   // every wave is done with the A window (zl lies inside it)
 #pragma unroll
   for (int j = 0; j < UPW; ++j) {
     const int unit = wave + kWaves * j;
@@ -1720,14 +1729,24 @@ __device__ __forceinline__ void reuse_bias(const PassP& P, float* zs, float* gs,
   __syncthreads();   // zs / gs / pref / lam are dead (the probabilities reuse the space)
 }
 
-__device__ __forceinline__ void route_block(const PassP& P, const float* bias, unsigned char* smem, int layer,
+// bz: the router bias of this lane's experts (lane + 64 i), loaded by the
+// caller before the router logits.
+__device__ __forceinline__ void route_bias(const float* bias, int E, float (&bz)[4]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bz[i] = lane + 64 * i < E ? *glb(bias + lane + 64 * i) : 0.f;
+}
+
+__device__ __forceinline__ void route_block(const PassP& P, const float (&bz)[4], unsigned char* smem, int layer,
                                             const float* zl) {
   Ctl* C = ctl(smem, (size_t)P.lds_bytes);
-  int* used = reinterpret_cast<int*>(smem);            // [E] (scratch; A windows not live here)
+  int* used = reinterpret_cast<int*>(smem + kRouteBase);   // [E]: used, then the expert's slot (-1: none)
   int* sel = used + 256;                              // [16][top_k]
   float* selw = reinterpret_cast<float*>(sel + 16 * 16);
-  float* prs = selw + 16 * 16;                        // [16][E] probabilities
+  float* prs = reinterpret_cast<float*>(smem + kRouteZl);   // [16][E4] probabilities (after zl is read)
+  float* rsum = selw + 16 * 16 + 256 + 256 + 32;      // [16] row sums (after the reuse-gating scratch)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E4 = (P.E + 3) & ~3;
   for (int e = tid; e < P.E; e += kThreads) used[e] = 0;
   constexpr int EPL = 4;                 // experts per lane (E <= 256)
   constexpr int RPW = kMaxRows / kWaves;  // rows per wave: row = wave + kWaves k
@@ -1742,9 +1761,7 @@ __device__ __forceinline__ void route_block(const PassP& P, const float* bias, u
       z[k][i] = (row < P.m && e < P.E) ? (zl ? zl[row * P.E + e] : cld(P.rlog + row * P.ldr + e)) : 0.f;
     }
   }
-  float bz[EPL];
-#pragma unroll
-  for (int i = 0; i < EPL; ++i) bz[i] = lane + 64 * i < P.E ? *glb(bias + lane + 64 * i) : 0.f;
+  __syncthreads();   // every wave holds its logits (the area is rewritten below)
   // the gating logits (router logits with bias)
 #pragma unroll
   for (int k = 0; k < RPW; ++k)
@@ -1752,7 +1769,7 @@ __device__ __forceinline__ void route_block(const PassP& P, const float* bias, u
     for (int i = 0; i < EPL; ++i) z[k][i] = lane + 64 * i < P.E ? z[k][i] + bz[i] : -INFINITY;
   if (P.reuse_cap > 0) {
     float* zs = prs;                          // [16][E] (before the probabilities are written)
-    float* gs = prs + 16 * 256;               // [E]
+    float* gs = selw + 16 * 16;               // [E]
     int* pref = reinterpret_cast<int*>(gs + 256);   // [E]
     float* lam = gs + 512;                    // [16][2]
     reuse_bias<RPW, EPL>(P, zs, gs, pref, lam, z);
@@ -1793,43 +1810,45 @@ __device__ __forceinline__ void route_block(const PassP& P, const float* bias, u
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
         const int e = lane + 64 * i;
-        if (e < P.E) prs[row * P.E + e] = z[k][i] == z[k][i] ? z[k][i] : -INFINITY;
+        if (e < E4) prs[row * E4 + e] = e < P.E && z[k][i] == z[k][i] ? z[k][i] : -INFINITY;
       }
+      if (lane == 0) rsum[row] = sum[k];
     }
   }
-  __syncthreads();   // prs and used[] complete
+  __syncthreads();   // prs, the row sums and used[] complete
+  // ranks of the (row, expert) pairs, spread over the workgroup's threads
+  // (a row's probabilities read four at a time with several reads in
+  // flight; the padding is -inf at ids past every expert, so it never
+  // counts; bitwise, not short-circuit, tests: no branches)
+  for (int pi = tid; pi < P.m * P.E; pi += kThreads) {
+    const int row = pi / P.E, e = pi - row * P.E;
+    const float* pr = prs + row * E4;
+    const float pe = pr[e];
+    int rank = 0;
+#pragma unroll 8
+    for (int j = 0; j < E4; j += 4) {
+      const f32x4 q = *reinterpret_cast<const f32x4*>(pr + j);
 #pragma unroll
-  for (int k = 0; k < RPW; ++k) {
-    const int row = wave + kWaves * k;
-    if (row >= P.m) break;
-    const float* pr = prs + row * P.E;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
-      if (e < P.E) {
-        const float pe = pr[e];
-        int rank = 0;
-        for (int j = 0; j < P.E; ++j) {
-          const float pj = pr[j];
-          rank += (pj > pe || (pj == pe && j < e)) ? 1 : 0;
-        }
-        if (rank < P.top_k) {
-          sel[row * P.top_k + rank] = e;
-          selw[row * P.top_k + rank] = z[k][i] / sum[k];
-          used[e] = 1;
-        }
-      }
+      for (int t = 0; t < 4; ++t) rank += (int)(q[t] > pe) | ((int)(q[t] == pe) & (int)(j + t < e));
+    }
+    if (rank < P.top_k) {
+      sel[row * P.top_k + rank] = e;
+      selw[row * P.top_k + rank] = pe / rsum[row];
+      used[e] = 1;
     }
   }
   __syncthreads();
-  // the union in ascending expert id (wave 0: a ballot scan)
+  // the union in ascending expert id (wave 0: a ballot scan); used[e]
+  // becomes the expert's slot, or -1
   if (wave == 0) {
     int cnt = 0;
     for (int e0 = 0; e0 < P.E; e0 += 64) {
       const int e = e0 + lane;
       const bool u = e < P.E && used[e] != 0;
       const unsigned long long bal = __ballot(u);
-      if (u) C->ulist[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = e;
+      const int pos = cnt + __popcll(bal & ((1ull << lane) - 1ull));
+      if (u) C->ulist[pos] = e;
+      if (e < P.E) used[e] = u ? pos : -1;
       cnt += __popcll(bal);
     }
     if (lane == 0) C->uc = cnt;
@@ -1846,10 +1865,7 @@ __device__ __forceinline__ void route_block(const PassP& P, const float* bias, u
       for (int i = tid; i < P.m * K; i += kThreads) P.route_hist[(long long)layer * P.m * K + i] = sel[i];
     for (int e = tid; e < E; e += kThreads) {
       cst(rec + 1 + e, e < C->uc ? C->ulist[e] : -1);
-      int s = -1;
-      for (int q = 0; q < C->uc; ++q)
-        if (C->ulist[q] == e) s = q;
-      cst(rec + 1 + E + e, s);
+      cst(rec + 1 + E + e, used[e]);
     }
     for (int i = tid; i < P.m * K; i += kThreads) {
       cst(rec + 1 + 2 * E + i, sel[i]);
@@ -1975,16 +1991,20 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
         sync([] {});
       {
         float* zl = nullptr;
+        float bz[4];
+        route_bias(d->bias, P.E, bz);
+        bool staged = false;   // the router's A window is the routed experts' one
         if constexpr (WF == W_BF16) {
           if (d->Mr.w) {
             zl = reinterpret_cast<float*>(smem + kRouteZl);
             router_logits<WF>(P, d->Mr, io, smem, zl);
+            staged = d->Mr.win == d->M.win;
           }
         }
-        route_block(P, d->bias, smem, d->layer, zl);
+        route_block(P, bz, smem, d->layer, zl);
         const SlotMap routed{C->ulist, C->uc, P.E, C->uc + P.n_shared};   // the union just built
         gemm_prefetch<WF, 2>(d->M, routed, false, ring);
-        gemm_phase<WF, EPI_SWIGLU, 2, GEN>(P, d->M, io, routed, false, ring, smem, wst);
+        gemm_phase<WF, EPI_SWIGLU, 2, GEN>(P, d->M, io, routed, false, ring, smem, wst, staged);
         break;
       }
       case PH_SWIGLU:
@@ -2037,7 +2057,7 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
 size_t pass_lds_bytes(int wfmt, int max_rows_attn, int D) {
   const size_t gemm = (size_t)kAWindowBytes + (wfmt == W_INT4 ? 16 * 16 * 4 : 0);   // + int4 row sums
   const size_t attn = attn_lds_bytes((max_rows_attn + 15) / 16, D);
-  const size_t route = 4 * (256 + 16 * 16 * 2 + 16 * 256 + 256 * 2 + 32);   // used, sel, selw, probabilities, reuse
+  const size_t route = (size_t)kRouteBase + kRouteBytes;   // after the A window
   size_t b = gemm > attn ? gemm : attn;
   if (route > b) b = route;
   return b + kCtlBytes;
