@@ -238,6 +238,15 @@ int spec_verify_tree(spec_verify_t* h, const int32_t* tokens, const int32_t* par
 int spec_verify_batch(spec_verify_t* h, int32_t n, const int32_t* seqs, const int32_t* tokens, const int32_t* ks,
                       int32_t mode, spec_step_result* out, float* logits_dev);
 
+/* Debugging aid for the error paths (callers: tests): from now on, the
+ * n-th device allocation the library makes (0 = the next one) fails as if
+ * the device were out of memory; n < 0 switches this off.  Process-wide.
+ * Returns the previous setting: the allocations that were still left
+ * before the failure (-1 if none was armed or it has fired).  A failed
+ * spec_verify_create frees everything it allocated and returns
+ * SPEC_ENOMEM. */
+int64_t spec_debug_fail_alloc(int64_t n);
+
 /* Committed length of sequence seq (-1 for a bad handle or id). */
 int32_t spec_seq_kv_len(const spec_verify_t* h, int32_t seq);
 

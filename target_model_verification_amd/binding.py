@@ -87,6 +87,7 @@ def _load():
         "spec_verify_batch": (I, [P, I, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
                                   ctypes.POINTER(ctypes.c_int32), I, ctypes.POINTER(SpecStepResult), P]),
         "spec_seq_kv_len": (I, [P, I]),
+        "spec_debug_fail_alloc": (ctypes.c_int64, [ctypes.c_int64]),
         "spec_seq_rollback": (I, [P, I, I]),
         "spec_seq_import": (I, [P, I, P, P, I]),
         "spec_verify_tree": (I, [P, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), I,
@@ -127,6 +128,7 @@ spec_verify_tree = lib.spec_verify_tree
 spec_tree_expand = lib.spec_tree_expand
 spec_verify_batch = lib.spec_verify_batch
 spec_seq_kv_len = lib.spec_seq_kv_len
+spec_debug_fail_alloc = lib.spec_debug_fail_alloc
 spec_seq_rollback = lib.spec_seq_rollback
 spec_seq_import = lib.spec_seq_import
 spec_verify_step_reuse = lib.spec_verify_step_reuse

@@ -268,10 +268,8 @@ __device__ __forceinline__ void grid_sync(GridBar& gb, PF&& prefetch) {
   raw_barrier();
 }
 
-// ------------------------------------------------------------ LDS plan
-// [0, kAWindowBytes): the staged A window (GEMM phases) / attention
-// working set; then a small control area.
-constexpr int kCtlBytes = 4096;
+// ------------------------------------------------------------ control area
+// (the LDS plan is in the shared header)
 struct Ctl {
   float rs[16];                 // RMSNorm row scales of the current phase
   int pend_n;                   // split units this workgroup flushed in the phase
@@ -1035,16 +1033,7 @@ __device__ __forceinline__ void split8(const float (&v)[8], u4& hi, u4& lo) {
   lo = u4{l[0] | l[1] << 16, l[2] | l[3] << 16, l[4] | l[5] << 16, l[6] | l[7] << 16};
 }
 
-constexpr int kPsStride = kPage + 4;         // floats per score row in LDS
 
-// LDS of the attention phase: Q fragments [RT][D/32][hi|lo][64 lanes],
-// scores / probabilities [RT*16][kPsStride], running max / sum / rescale.
-// (two-pass path; the one-row-tile path needs 16 rows of a whole group of
-// the largest size + 4)
-__host__ __device__ constexpr size_t attn_lds_bytes(int rt, int D) {
-  return (size_t)rt * (D / 32) * 2 * 1024 + (size_t)rt * 16 * kPsStride * 4 + (size_t)3 * rt * 16 * 4 +
-         (size_t)16 * (kPage * kMaxGroupPages + 4) * 4;
-}
 
 // One output element (row r, dim d) of KV head g: the groups' partials
 // combined in ascending group order.
@@ -1585,15 +1574,6 @@ __device__ __forceinline__ void attn_merge_phase(const PassP& P, uint4* a_o, uns
 }
 
 // ------------------------------------------------------------ MoE routing
-// LDS of routing, after the A window (which stays staged for the routed
-// gate/up phase, whose A operand is the router's): used / slot of each
-// expert [256], sel [16][16], selw [16][16], reuse-gating scratch, then one
-// [16][E] float area that holds the block's router logits (when computed in
-// the phase), then the reuse-gating logits, then the probabilities (rows
-// padded to a multiple of 4).
-constexpr int kRouteBase = kAWindowBytes + 1024;   // after the int4 row sums
-constexpr int kRouteZl = kRouteBase + 6 * 1024;
-constexpr int kRouteBytes = 6 * 1024 + 16 * 256 * 4;
 // Every workgroup routes the block redundantly (same inputs, same order):
 // pi = softmax(r + b) over the experts, each row keeps its top_k experts by
 // probability (ties to the lower id), weights = those probabilities; the
@@ -2054,14 +2034,6 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
   if (P.wstamps) wstamp(P.wstamps + ((long long)(P.n_prog - 1) * gridDim.x + blockIdx.x) * 4, 3);
 }
 
-size_t pass_lds_bytes(int wfmt, int max_rows_attn, int D) {
-  const size_t gemm = (size_t)kAWindowBytes + (wfmt == W_INT4 ? 16 * 16 * 4 : 0);   // + int4 row sums
-  const size_t attn = attn_lds_bytes((max_rows_attn + 15) / 16, D);
-  const size_t route = (size_t)kRouteBase + kRouteBytes;   // after the A window
-  size_t b = gemm > attn ? gemm : attn;
-  if (route > b) b = route;
-  return b + kCtlBytes;
-}
 
 // The pass kernel for a weight format and model kind; gen: the instance
 // that reads per-row placement (token trees, several sequences).

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -154,8 +155,22 @@ int fail(spec_verify* h, int code, const std::string& msg) {
     }                                                                             \
   } while (0)
 
+// Debugging aid (spec_debug_fail_alloc): the number of device allocations
+// left before one fails as if the device were out of memory (-1: off).
+std::atomic<long long> g_fail_alloc{-1};
+
 int dalloc(spec_verify* h, void** p, size_t bytes) {
   if (bytes == 0) bytes = 16;
+  for (long long n = g_fail_alloc.load(); n >= 0;) {
+    if (g_fail_alloc.compare_exchange_weak(n, n - 1)) {
+      if (n == 0) {
+        *p = nullptr;
+        h->err = "hipMalloc(" + std::to_string(bytes) + "): injected failure";
+        return SPEC_ENOMEM;
+      }
+      break;
+    }
+  }
   hipError_t e = hipMalloc(p, bytes);
   if (e != hipSuccess) {
     *p = nullptr;
@@ -1516,6 +1531,8 @@ int32_t spec_tree_expand(int32_t n, const int32_t* parents, const double* p, con
   if (row_parents) row_parents[0] = -1;
   return cnt;
 }
+
+int64_t spec_debug_fail_alloc(int64_t n) { return g_fail_alloc.exchange(n < 0 ? -1 : n); }
 
 int32_t spec_adaptive_k(int32_t k, int32_t n_accepted, int32_t max_k) {
   if (max_k < 1 || k < 1 || k > max_k || n_accepted < 0 || n_accepted > k) return -1;

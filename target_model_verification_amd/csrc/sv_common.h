@@ -197,7 +197,6 @@ __host__ __device__ inline int route_words(int E, int top_k) { return 1 + 2 * E 
 // generation by that much per launch).  fp32 weights imply an fp32 KV cache;
 // bf16 / int4 weights a bf16 cache.
 hipError_t launch_pass(int wfmt, bool moe, const PassP& p, int n_wg, size_t lds, hipStream_t s);
-size_t pass_lds_bytes(int wfmt, int max_rows_attn, int D);
 hipError_t pass_occupancy(int wfmt, bool moe, size_t lds, int* blocks_per_cu);
 // split units one workgroup may flush per phase (control-area capacity)
 constexpr int kMaxPending = 512;
@@ -218,5 +217,41 @@ hipError_t launch_kv_poison(int kv_f32, void* base, long long layer_elems, int n
 // (path, count in result[0]) from slots L + path[j] to L + 1 + j.
 hipError_t launch_tree_commit(int kv_f32, void* base, long long layer_elems, int n_layers, int Hkv, int D,
                               const int* page_table, int L, const int* result, const int* path, hipStream_t s);
+
+
+// ------------------------------------------------------------ LDS plan of the pass
+// [0, kAWindowBytes): the staged A window (GEMM phases) / attention working
+// set; [kAWindowBytes, +1 KB) int4 row sums; then the routing scratch (MoE);
+// a control area at the end.
+constexpr int kCtlBytes = 4096;
+constexpr int kPsStride = kPage + 4;         // floats per attention score row in LDS (two-pass path)
+
+// LDS of the attention phase: Q fragments [RT][D/32][hi|lo][64 lanes],
+// scores / probabilities [RT*16][kPsStride], running max / sum / rescale.
+// (two-pass path; the one-row-tile path needs 16 rows of a whole group of
+// the largest size + 4)
+__host__ __device__ constexpr size_t attn_lds_bytes(int rt, int D) {
+  return (size_t)rt * (D / 32) * 2 * 1024 + (size_t)rt * 16 * kPsStride * 4 + (size_t)3 * rt * 16 * 4 +
+         (size_t)16 * (kPage * kMaxGroupPages + 4) * 4;
+}
+
+// LDS of routing, after the A window (which stays staged for the routed
+// gate/up phase, whose A operand is the router's): used / slot of each
+// expert [256], sel [16][16], selw [16][16], reuse-gating scratch, then one
+// [16][E] float area that holds the block's router logits (when computed in
+// the phase), then the reuse-gating logits, then the probabilities (rows
+// padded to a multiple of 4).
+constexpr int kRouteBase = kAWindowBytes + 1024;   // after the int4 row sums
+constexpr int kRouteZl = kRouteBase + 6 * 1024;
+constexpr int kRouteBytes = 6 * 1024 + 16 * 256 * 4;
+
+inline size_t pass_lds_bytes(int wfmt, int max_rows_attn, int D) {
+  const size_t gemm = (size_t)kAWindowBytes + (wfmt == W_INT4 ? 16 * 16 * 4 : 0);   // + int4 row sums
+  const size_t attn = attn_lds_bytes((max_rows_attn + 15) / 16, D);
+  const size_t route = (size_t)kRouteBase + kRouteBytes;   // after the A window
+  size_t b = gemm > attn ? gemm : attn;
+  if (route > b) b = route;
+  return b + kCtlBytes;
+}
 
 }  // namespace sv
