@@ -772,6 +772,15 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if wl.spec.moe and r.get("prof") and r["prof"].get("expert_gateup", (0,))[0]:
+        # the routed union per layer, from the expert gate/up phase's bytes
+        # (each loaded expert's gate and up matrices once, plus the shared ones)
+        n_eg, _, by_eg = r["prof"]["expert_gateup"]
+        wbytes = {"bf16": 2.0, "f32": 4.0, "int4g128": 0.5 + 2.0 / 128}[wl.spec.weight_dtype]
+        per_expert = 2.0 * wl.spec.d_model * wl.spec.d_ff_expert * wbytes
+        union = by_eg / n_eg / per_expert - wl.spec.n_shared
+        line["config"]["experts_per_layer"] = round(union, 3)
+        line["config"]["reuse_ratio"] = round(union / ((k + 1) * wl.spec.top_k), 4)
     if args.reuse_cap:
         with torch.cuda.stream(stream):
             line["reuse_gating"] = reuse_quality(sess, k, args.reuse_cap, args.reuse_alpha)
