@@ -594,13 +594,18 @@ __device__ __forceinline__ void row_scales(const PassP& P, const float* ss, floa
 // window holds a multiple of 128 words, so each wave's 64-word block lies
 // wholly inside it.
 template <int WF>
-__device__ __forceinline__ void stage_window(const Lin& L, const GemmIO& io, int slot, int win, unsigned char* smem) {
+__device__ __forceinline__ void stage_window(const Lin& L, const GemmIO& io, int slot, int win, unsigned char* smem,
+                                             int m) {
   constexpr int ACH = (WF == W_INT4) ? 4 : 1;
   const int n16 = L.wlen(win) * ACH * 128;    // 16-byte words to copy
   const uint4* src = io.a + (long long)slot * io.a_slot + (long long)win * L.W * ACH * 128;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i0 = wave * 64; i0 < n16; i0 += kThreads)
-    __builtin_amdgcn_global_load_lds((gvoid*)(src + i0 + lane), (lvoid*)(smem + (size_t)i0 * 16), 16, 0, 0);
+  // lane l of every 64-word block carries row l % 16: rows past the block's
+  // m are not loaded (what LDS holds there only reaches output rows that
+  // nothing reads)
+  if ((lane & 15) < m)
+    for (int i0 = wave * 64; i0 < n16; i0 += kThreads)
+      __builtin_amdgcn_global_load_lds((gvoid*)(src + i0 + lane), (lvoid*)(smem + (size_t)i0 * 16), 16, 0, 0);
 }
 
 // int4: per 128-k chunk of the staged window and per row, the sum of the A
@@ -682,7 +687,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     sw = a.win;
     if (!(staged && sk == 0 && sw == 0)) {
       wait_window(P, io, sw);
-      stage_window<WF>(L, io, sk, sw, smem);
+      stage_window<WF>(L, io, sk, sw, smem, P.m);
     }
   }
   if ((EPI == EPI_SWIGLU || EPI == EPI_LOGITS || EPI == EPI_QKV || (EPI == EPI_STORE && io.scale)) && !staged)
@@ -870,7 +875,7 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
       sk = key;
       sw = cc.win;
       wait_window(P, io, sw);
-      stage_window<WF>(L, io, sk, sw, smem);
+      stage_window<WF>(L, io, sk, sw, smem, P.m);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if constexpr (WF == W_INT4) int4_rowsums(smem, L.wlen(sw), S4);
@@ -1592,7 +1597,7 @@ __device__ __forceinline__ void router_logits(const PassP& P, const Mat& Mr, con
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const Lin L = make_lin(Mr, 1, false);
-  stage_window<WF>(L, io, 0, 0, smem);
+  stage_window<WF>(L, io, 0, 0, smem, P.m);
   row_scales(P, io.ss_in, C->rs);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
