@@ -96,6 +96,7 @@ struct spec_verify {
   long long qf_layer = 0, a_o_layer = 0;   // uint4 per layer
   int* tokens_dev = nullptr;
   int* result_dev = nullptr;
+  float* acc_ws = nullptr;      // acceptance: tickets, partial statistics, draw tile sums
   int* tokens_host = nullptr;   // pinned
   int* result_host = nullptr;   // pinned
   int* draft_res = nullptr;     // self-speculative draft: [kMaxRows][4] acceptance records (device)
@@ -709,6 +710,7 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   if ((rc = dalloc_z(h, &h->bar, 512))) return rc;
   if ((rc = dalloc_z(h, &h->tokens_dev, 16))) return rc;
   if ((rc = dalloc_z(h, &h->result_dev, 4))) return rc;
+  if ((rc = dalloc_z(h, &h->acc_ws, (size_t)kAccFloats))) return rc;
   if (moe) {
     if ((rc = dalloc_z(h, &h->rlog, 16 * (size_t)h->ldr))) return rc;
     h->ey_slot = 16LL * h->ldx;
@@ -1005,6 +1007,7 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   a.logits = h->logits; a.ldl = h->ldl;
   a.q = q_dev; a.u = u_dev;
   a.result = h->result_dev;
+  a.acc_ws = h->acc_ws;
   if (he == hipSuccess) he = launch_accept(a, h->stream);
   if (he == hipSuccess && h->profiling) he = hipEventRecord(h->ev[2], h->stream);
   if (he == hipSuccess)
@@ -1215,6 +1218,7 @@ int spec_verify_tree(spec_verify_t* h, const int32_t* tokens, const int32_t* par
   a.st_max = h->st_max; a.st_sum = h->st_sum; a.st_idx = h->st_idx;
   a.logits = h->logits; a.ldl = h->ldl;
   a.result = h->result_dev;
+  a.acc_ws = h->acc_ws;
   if (he == hipSuccess) he = launch_accept(a, h->stream);
   // the accepted rows' cache entries to consecutive slots after the pending token's
   if (he == hipSuccess)
@@ -1316,6 +1320,7 @@ int spec_verify_batch(spec_verify_t* h, int32_t n, const int32_t* seqs, const in
   a.st_max = h->st_max; a.st_sum = h->st_sum; a.st_idx = h->st_idx;
   a.logits = h->logits; a.ldl = h->ldl;
   a.result = h->batch_res;
+  a.acc_ws = h->acc_ws;
   if (he == hipSuccess) he = launch_accept(a, h->stream);
   if (he == hipSuccess && h->profiling && moe)
     he = hipMemcpyAsync(h->union_host.data(), h->union_dev_prof, sizeof(int) * c.n_layers, hipMemcpyDeviceToHost,
@@ -1435,6 +1440,7 @@ int spec_draft(spec_verify_t* h, int32_t pending, int32_t n, int32_t draft_top_k
     a.st_max = h->st_max; a.st_sum = h->st_sum; a.st_idx = h->st_idx;
     a.logits = h->logits; a.ldl = h->ldl;
     a.result = h->draft_res + 4 * i;
+    a.acc_ws = h->acc_ws;
     if (he == hipSuccess) he = launch_accept(a, h->stream);
     if (he == hipSuccess && logits_dev)
       he = hipMemcpyAsync(logits_dev + (long long)i * c.vocab, h->logits, (size_t)c.vocab * 4, hipMemcpyDeviceToDevice,

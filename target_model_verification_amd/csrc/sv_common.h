@@ -176,7 +176,20 @@ struct AcceptParams {
   const float* logits; int ldl;
   const float* q; const float* u;
   int* result;          // [3]
+  float* acc_ws;        // kAccFloats words, tickets zero at first use
 };
+
+// Acceptance workspace (words): the decision of the stochastic tests (row of
+// the draw, residual flag, that row's max logit and softmax sum), the arrival
+// tickets of the statistics grid and of the draw grid, then per 64-id tile
+// the residual weight sums and the plain p weight sums, then the row
+// statistics' per-chunk partials [16 rows][kAccMaxChunks][3].
+constexpr int kAccTiles = 4 * 1024;      // 64-id tiles: vocabularies up to 262144 ids
+constexpr int kAccMaxChunks = 4;         // statistics chunks per row (4096 partials each)
+constexpr int kDrawRow = 0, kDrawResid = 1, kDrawM = 2, kDrawS = 3, kDrawTicket = 4, kAccTicket = 5;
+constexpr int kDrawHead = 16;
+constexpr int kAccPart = kDrawHead + 2 * kAccTiles;
+constexpr int kAccFloats = kAccPart + 16 * kAccMaxChunks * 3;
 
 // Acceptance kernel mode for a token tree (greedy; the C ABI's modes are
 // 0..2).
