@@ -663,7 +663,11 @@ __device__ __forceinline__ void wait_window(const PassP& P, const GemmIO& io, in
 }
 
 // One weight-streaming phase over `sm.n_slots` slots (experts) of M.
-template <int WF, int EPI, int TPU, bool GEN>
+// FIXED: the fixed-order split-K of the expert phases (seg_info_fixed):
+// every piece (one batch) is summed from zero and added to the block's
+// running chain in K order, so the result does not depend on how the
+// routed union's size cuts the work.
+template <int WF, int EPI, int TPU, bool GEN, bool FIXED = false>
 __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const GemmIO io, const SlotMap sm,
                                         bool slot_major, Ring& ring, unsigned char* smem, unsigned long long* wst,
                                         bool staged = false) {
@@ -836,36 +840,86 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
     // ---- one segment: (slot, win, sg), chunks [cc.c, cc.c + nch)
     const int nch = seg_left(cc, u1);
     const bool live = cc.sg * kWaves + wave < M.n_units;
-#pragma unroll
-    for (int t = 0; t < TPU; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int c0 = 0; c0 < nch; c0 += F::U) {
-      const int n = min(F::U, nch - c0);
-      compute(cc.c + c0, n, live);
-      next_batch<WF, TPU>(M, L, lc, u1, ring);
-    }
-    cc.u += nch;
-    cc.c += nch;
-    // ---- flush the segment: epilogue if it covers the whole unit, else a
-    // partial for the last arriver
     int idx, nseg;
-    seg_info(L, cc.slot, cc.sg, cc.win, g, G, idx, nseg);
-    if (live) {
-      if (nseg == 1) {
-        QkvPre qp;
-        if constexpr (EPI == EPI_QKV) qkv_pre<GEN>(P, cc.sg * kWaves + wave, qp);
-        epilogue<WF, EPI, TPU, GEN>(P, M, io, C->rs, cc.slot, cc.sg * kWaves + wave, acc, &qp);
-      } else {
-        float* p = io.ws + ((((long long)cc.slot * M.n_sg + cc.sg) * M.max_seg + idx) * kWaves + wave) * TPU * 256;
+    if constexpr (!FIXED) {
 #pragma unroll
-        for (int t = 0; t < TPU; ++t) cst4(p + t * 256 + lane * 4, acc[t]);
+      for (int t = 0; t < TPU; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c0 = 0; c0 < nch; c0 += F::U) {
+        const int n = min(F::U, nch - c0);
+        compute(cc.c + c0, n, live);
+        next_batch<WF, TPU>(M, L, lc, u1, ring);
       }
-    }
-    // split segments (and, for producing phases, blocks finished here) are
-    // listed; bit 31 marks a finished block
-    if ((nseg > 1 || io.notify) && threadIdx.x == 0) {
-      const int k = C->pend_n;   // capacity guaranteed by the host (kMaxPending)
-      C->pend[k] = (nseg > 1 ? 0 : (int)0x80000000u) | cc.slot << 20 | cc.sg;
-      C->pend_n = k + 1;
+      cc.u += nch;
+      cc.c += nch;
+      // ---- flush the segment: epilogue if it covers the whole unit, else a
+      // partial for the last arriver
+      seg_info(L, cc.slot, cc.sg, cc.win, g, G, idx, nseg);
+      if (live) {
+        if (nseg == 1) {
+          QkvPre qp;
+          if constexpr (EPI == EPI_QKV) qkv_pre<GEN>(P, cc.sg * kWaves + wave, qp);
+          epilogue<WF, EPI, TPU, GEN>(P, M, io, C->rs, cc.slot, cc.sg * kWaves + wave, acc, &qp);
+        } else {
+          float* p = io.ws + ((((long long)cc.slot * M.n_sg + cc.sg) * M.max_seg + idx) * kWaves + wave) * TPU * 256;
+#pragma unroll
+          for (int t = 0; t < TPU; ++t) cst4(p + t * 256 + lane * 4, acc[t]);
+        }
+      }
+      // split segments (and, for producing phases, blocks finished here) are
+      // listed; bit 31 marks a finished block
+      if ((nseg > 1 || io.notify) && threadIdx.x == 0) {
+        const int k = C->pend_n;   // capacity guaranteed by the host (kMaxPending)
+        C->pend[k] = (nseg > 1 ? 0 : (int)0x80000000u) | cc.slot << 20 | cc.sg;
+        C->pend_n = k + 1;
+      }
+    } else {
+      // fixed order: every batch (one piece) from zero; a segment holding the
+      // block's first piece adds them to its running chain (kept per lane in
+      // LDS, not live in registers across the batch's MFMAs) and hands the
+      // chain over as partial 0; a later segment hands over each piece
+      seg_info_fixed(L, cc.slot, cc.sg, cc.win, g, G, idx, nseg);
+      auto part = [&](int i) {   // this wave's slot of partial i of the block
+        return io.ws + ((((long long)cc.slot * M.n_sg + cc.sg) * M.max_seg + i) * kWaves + wave) * TPU * 256;
+      };
+      f32x4* const chain = reinterpret_cast<f32x4*>(smem + kChainBase) + wave * TPU * 64 + lane;
+#pragma unroll
+      for (int t = 0; t < TPU; ++t) chain[t * 64] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c0 = 0; c0 < nch; c0 += F::U) {
+        const int n = min(F::U, nch - c0);
+#pragma unroll
+        for (int t = 0; t < TPU; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        compute(cc.c + c0, n, live);
+        next_batch<WF, TPU>(M, L, lc, u1, ring);
+        if (idx == 0) {
+#pragma unroll
+          for (int t = 0; t < TPU; ++t) chain[t * 64] = chain[t * 64] + acc[t];
+        } else if (live) {
+          float* p = part(idx + c0 / F::U);
+#pragma unroll
+          for (int t = 0; t < TPU; ++t) cst4(p + t * 256 + lane * 4, acc[t]);
+        }
+      }
+      cc.u += nch;
+      cc.c += nch;
+      if (live && idx == 0) {
+#pragma unroll
+        for (int t = 0; t < TPU; ++t) acc[t] = chain[t * 64];
+        if (nseg == 1) {
+          QkvPre qp;
+          epilogue<WF, EPI, TPU, GEN>(P, M, io, C->rs, cc.slot, cc.sg * kWaves + wave, acc, &qp);
+        } else {
+          float* p = part(0);
+#pragma unroll
+          for (int t = 0; t < TPU; ++t) cst4(p + t * 256 + lane * 4, acc[t]);
+        }
+      }
+      // one list entry per partial handed over (bit 31: a block finished here)
+      if ((nseg > 1 || io.notify) && threadIdx.x == 0) {
+        const int nparts = nseg > 1 && idx > 0 ? (nch + F::U - 1) / F::U : 1;
+        int k = C->pend_n;   // capacity guaranteed by the host (kMaxPending)
+        for (int i = 0; i < nparts; ++i) C->pend[k++] = (nseg > 1 ? 0 : (int)0x80000000u) | cc.slot << 20 | cc.sg;
+        C->pend_n = k;
+      }
     }
     if (cc.u >= u1) break;
     seg_advance(L, cc);
@@ -941,7 +995,8 @@ __device__ __forceinline__ void gemm_phase(const PassP& P, const Mat M, const Ge
   for (int b = b0; b < b1; ++b) {
     const int s = b / M.n_sg, sg = b - s * M.n_sg;
     int idx, n;
-    seg_info(L, s, sg, 0, g, G, idx, n);
+    if constexpr (FIXED) seg_info_fixed(L, s, sg, 0, g, G, idx, n);
+    else seg_info(L, s, sg, 0, g, G, idx, n);
     if (n == 1) continue;   // finished inside the stream
     QkvPre qp;
     pre(sg, qp);            // (its loads in flight while polling)
@@ -1959,7 +2014,8 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
         if constexpr (!MOE) break;
         const SlotMap sm = d->slot_mode ? slots : dense;
         sync([&] { gemm_prefetch<WF, 1>(d->M, sm, d->slot_mode == 2, ring); });
-        gemm_phase<WF, EPI_STORE, 1, GEN>(P, d->M, io, sm, d->slot_mode == 2, ring, smem, wst);
+        // (the MoE pass's stores: router and expert down, both in fixed order)
+        gemm_phase<WF, EPI_STORE, 1, GEN, true>(P, d->M, io, sm, d->slot_mode == 2, ring, smem, wst);
         break;
       }
       case PH_QKV:
@@ -1989,7 +2045,7 @@ __global__ __launch_bounds__(kThreads) void k_pass(PassP P) {
         route_block(P, bz, smem, d->layer, zl);
         const SlotMap routed{C->ulist, C->uc, P.E, C->uc + P.n_shared};   // the union just built
         gemm_prefetch<WF, 2>(d->M, routed, false, ring);
-        gemm_phase<WF, EPI_SWIGLU, 2, GEN>(P, d->M, io, routed, false, ring, smem, wst, staged);
+        gemm_phase<WF, EPI_SWIGLU, 2, GEN, true>(P, d->M, io, routed, false, ring, smem, wst, staged);
         break;
       }
       case PH_SWIGLU:

@@ -125,22 +125,30 @@ bool check_gemm_walk(const GemmShape& s, int G, size_t ws_floats, size_t n_ticke
         cc.u += nch;
         cc.c += nch;
         int idx = 0, nseg = 0;
-        seg_info(L, cc.slot, cc.sg, cc.win, g, G, idx, nseg);
-        if (nseg < 1 || nseg > M.max_seg || idx < 0 || idx >= nseg) return fail("segment index out of range");
+        if (s.fixed) seg_info_fixed(L, cc.slot, cc.sg, cc.win, g, G, idx, nseg);
+        else seg_info(L, cc.slot, cc.sg, cc.win, g, G, idx, nseg);
+        // partials this segment hands over: one, or (fixed order, a segment
+        // after the block's first) one per piece, i.e. per batch
+        const int nparts = s.fixed && idx > 0 ? (nch + U - 1) / U : 1;
+        if (nseg < 1 || nseg > M.max_seg || idx < 0 || idx + nparts > nseg) return fail("segment index out of range");
         const std::pair<int, int> blk(cc.slot, cc.sg);
         auto an = announced.find(blk);
         if (an == announced.end()) announced[blk] = nseg;
         else if (an->second != nseg) return fail("segment count differs between workgroups");
-        segs[blk].push_back({idx, nseg, cc.win, c_start, nch, g});
-        if (nseg > 1) {
-          const long long last = (((((long long)cc.slot * M.n_sg + cc.sg) * M.max_seg + idx) * kWaves + kWaves - 1) *
-                                      s.tpu * 256) + (long long)(s.tpu - 1) * 256 + 63 * 4 + 4;
-          if (last > (long long)ws_floats) return fail("split-K partial past the workspace");
-          if ((long long)cc.slot * M.n_sg + cc.sg >= (long long)n_tickets) return fail("ticket out of range");
+        for (int b = 0; b < nparts; ++b) {
+          const int c = nparts == 1 ? c_start : c_start + b * U;
+          const int len = nparts == 1 ? nch : std::min(U, nch - b * U);
+          segs[blk].push_back({idx + b, nseg, cc.win, c, len, g});
+          if (nseg > 1) {
+            const long long last = (((((long long)cc.slot * M.n_sg + cc.sg) * M.max_seg + idx + b) * kWaves + kWaves - 1) *
+                                        s.tpu * 256) + (long long)(s.tpu - 1) * 256 + 63 * 4 + 4;
+            if (last > (long long)ws_floats) return fail("split-K partial past the workspace");
+            if ((long long)cc.slot * M.n_sg + cc.sg >= (long long)n_tickets) return fail("ticket out of range");
+          }
+          // every partial may be listed (split ones, and finished blocks of
+          // phases that announce their outputs)
+          if (++pend > kMaxPending) return fail("too many segments for one workgroup's list");
         }
-        // every segment may be listed (split ones, and finished blocks of
-        // phases that announce their outputs)
-        if (++pend > kMaxPending) return fail("too many segments for one workgroup's list");
         if (cc.u >= u1) break;
         seg_advance(L, cc);
         const int nkey = s.slot_major ? cc.slot : 0;

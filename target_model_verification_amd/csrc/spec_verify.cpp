@@ -288,6 +288,7 @@ bool build_plan(const spec_config& c, int wf, int G, PassPlan& P, std::string& e
     s.n_shared = S;
     s.max_slots = n_stack;
     s.slot_major = slot_major;
+    s.fixed = false;
     s.a_slot = a_slot;
     s.a_size = a_size;
     P.used.push_back(&s);
@@ -301,6 +302,10 @@ bool build_plan(const spec_config& c, int wf, int G, PassPlan& P, std::string& e
     shape(P.router, "router", d, E, 1, 1, false, 0, P.a_norm);
     shape(P.ex_gateup, "expert gate/up", d, F, 2, n_slots_max, false, 0, P.a_norm);
     shape(P.ex_down, "expert down", F, d, 1, n_slots_max, true, P.a_act_slot, P.a_act_slot * n_slots_max);
+    // the expert phases' split follows the routed union: fixed summation
+    // order (the router shares the pass kernel's code path with the expert
+    // down projection)
+    P.router.fixed = P.ex_gateup.fixed = P.ex_down.fixed = true;
   }
   shape(P.lm_head, "lm_head", d, V, 1, 1, false, 0, P.a_norm);
   for (GemmShape* s : P.used) {
@@ -308,7 +313,7 @@ bool build_plan(const spec_config& c, int wf, int G, PassPlan& P, std::string& e
     const int lo = s->max_slots > 1 ? std::max(1, S) : 1;
     for (int ns = lo; ns <= s->max_slots; ++ns) {
       int a = 0, b = 0;
-      seg_bounds(s->M, ns, s->slot_major, G, a, b);
+      seg_bounds(s->M, ns, s->slot_major, s->fixed, G, a, b);
       ms = std::max(ms, a);
       mp = std::max(mp, b);
     }

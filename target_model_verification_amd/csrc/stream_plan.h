@@ -178,6 +178,33 @@ SP_HD void seg_info(const Lin& L, int slot, int sg, int win, int g, int G, int& 
   }
 }
 
+// Split-K bookkeeping in a fixed summation order (expert phases, whose
+// slot count, and with it the work split, follows the routed union): the
+// value of unit block (slot, sg) is the chain (((P_0 + P_1) + P_2) + ...)
+// over its pieces in K order, each piece summed from zero, whichever
+// workgroups own them.  The segment holding the block's first piece hands
+// over its own chain as partial 0; every piece of a later segment is a
+// partial of its own.  n: partials of the block; idx: partial index of the
+// first piece of segment (win, g) (0 when it holds the block's first piece).
+SP_HD void seg_info_fixed(const Lin& L, int slot, int sg, int win, int g, int G, int& idx, int& n) {
+  const bool sparse = L.P < G;
+  const int a0 = L.piece_start(slot, 0) + sg * L.np(0);
+  // pieces of the first segment: those of window 0's run owned by the owner
+  // of its first piece (one piece each when pieces are scarcer than workgroups)
+  const int f = sparse ? 1 : sp_min(L.np(0), range_begin(L.P, wg_of(a0, L.P, G) + 1, G) - a0);
+  int tot = 0, j = 0;
+  const int mine = range_begin(L.P, g, G);
+  for (int w = 0; w < L.n_win; ++w) {
+    if (w == win) {
+      const int a = L.piece_start(slot, w) + sg * L.np(w);
+      j = tot + (mine > a ? mine - a : 0);
+    }
+    tot += L.np(w);
+  }
+  n = tot - f + 1;
+  idx = j == 0 ? 0 : j - f + 1;
+}
+
 // Units left in the cursor's current segment, capped by the range end.
 SP_HD int seg_left(const Cur& q, int u1) { return sp_min(q.len - q.c, u1 - q.u); }
 
@@ -243,18 +270,21 @@ inline void mat_geometry(Mat& M, int wf, int K, int N, int n_units, int tpu, int
   M.U = batch_chunks(wf, tpu);
 }
 
-// Largest number of split-K segments of one unit block, and the largest
-// number of split segments one workgroup flushes, for n_slots slots.
-inline void seg_bounds(const Mat& M, int n_slots, bool slot_major, int G, int& max_seg, int& max_pend) {
+// Largest number of split-K partials of one unit block, and the largest
+// number of partials one workgroup flushes, for n_slots slots (fixed: the
+// fixed-order split of the expert phases).
+inline void seg_bounds(const Mat& M, int n_slots, bool slot_major, bool fixed, int G, int& max_seg, int& max_pend) {
   const Lin L = make_lin(M, n_slots, slot_major);
   max_seg = 1;
   for (int s = 0; s < n_slots; ++s)
     for (int sg = 0; sg < M.n_sg; ++sg) {
       int idx = 0, n = 0;
-      seg_info(L, s, sg, 0, 0, G, idx, n);
+      if (fixed) seg_info_fixed(L, s, sg, 0, 0, G, idx, n);
+      else seg_info(L, s, sg, 0, 0, G, idx, n);
       if (n > max_seg) max_seg = n;
     }
-  // a share of at most ceil(P / G) pieces meets at most that many runs
+  // a share of at most ceil(P / G) pieces meets at most that many runs (and
+  // flushes at most one partial per piece)
   max_pend = (int)(((long long)L.P + G - 1) / G) + 2;
 }
 
@@ -267,6 +297,7 @@ struct GemmShape {
   int n_experts, n_shared;
   int max_slots;       // slots per pass: 1, or routed + shared experts
   bool slot_major;
+  bool fixed;          // fixed-order split-K (seg_info_fixed): expert phases
   long long a_slot;    // A operand uint4 per slot (0: one A shared by all slots)
   long long a_size;    // A operand buffer size (uint4)
 };

@@ -257,6 +257,11 @@ __host__ __device__ constexpr size_t attn_lds_bytes(int rt, int D) {
 constexpr int kRouteBase = kAWindowBytes + 1024;   // after the int4 row sums
 constexpr int kRouteZl = kRouteBase + 6 * 1024;
 constexpr int kRouteBytes = 6 * 1024 + 16 * 256 * 4;
+// The expert phases' fixed-order split keeps each segment's running chain
+// (kWaves waves x up to 2 tiles x 64 lanes x 16 bytes) in the routing
+// scratch, which is free once the union is built.
+constexpr int kChainBase = kRouteBase;
+static_assert(kWaves * 2 * 64 * 16 <= kRouteBytes, "chain area exceeds the routing scratch");
 
 inline size_t pass_lds_bytes(int wfmt, int max_rows_attn, int D) {
   const size_t gemm = (size_t)kAWindowBytes + (wfmt == W_INT4 ? 16 * 16 * 4 : 0);   // + int4 row sums
