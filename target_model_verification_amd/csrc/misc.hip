@@ -13,6 +13,21 @@ namespace sv {
 // running sum in ascending id order.  result = {n_acc, next, kv_len}.
 constexpr int kAccWaves = 16;            // 1024 threads
 
+// The step's result {n_acc, next, kv_len} and, when the caller gave a
+// host-visible mirror (pinned host memory), the same three words plus the
+// pass's error flag (result[3], written by the pass kernel) stored there with
+// system-scope stores, so the host reads them without a device-to-host copy.
+__device__ __forceinline__ void put_result(const AcceptParams& p, int n, int next, int len) {
+  p.result[0] = n;
+  p.result[1] = next;
+  p.result[2] = len;
+  if (p.result_mirror) {
+    const int w[4] = {n, next, len, p.result[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) __hip_atomic_store(p.result_mirror + i, w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
+
 // Cross-workgroup hand-off inside one launch without L2 fences (an agent
 // fence in every wave would write back and invalidate its XCD's L2 each
 // time): partial results are stored write-through (agent-scope relaxed
@@ -184,9 +199,7 @@ __global__ __launch_bounds__(1024) void k_accept(AcceptParams p) {
       } else {
         n = p.k;
       }
-      p.result[0] = n;
-      p.result[1] = amax[n];
-      p.result[2] = p.L + 1 + n;
+      put_result(p, n, amax[n], p.L + 1 + n);
     }
     return;
   }
@@ -354,9 +367,7 @@ __global__ __launch_bounds__(1024) void k_draw(AcceptParams p) {
     if (lane == 0) {
       const int n = di[kDrawRow];
       const int xs = hit ? t * 64 + __builtin_ctzll(hit) : (pos ? t * 64 + 63 - __builtin_clzll(pos) : 0);
-      p.result[0] = n;
-      p.result[1] = xs;
-      p.result[2] = p.L + 1 + n;
+      put_result(p, n, xs, p.L + 1 + n);
     }
   }
 }

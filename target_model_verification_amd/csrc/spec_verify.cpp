@@ -99,6 +99,7 @@ struct spec_verify {
   float* acc_ws = nullptr;      // acceptance: tickets, partial statistics, draw tile sums
   int* tokens_host = nullptr;   // pinned
   int* result_host = nullptr;   // pinned
+  int* result_mirror = nullptr;   // device view of result_host (the step's acceptance writes it), or null
   int* draft_res = nullptr;     // self-speculative draft: [kMaxRows][4] acceptance records (device)
   int* tree_dev = nullptr;      // token tree: parents [16], depths [16], ancestor masks [16], path [16]
   int* tree_host = nullptr;     // pinned staging of the tree arrays and the returned path
@@ -724,6 +725,8 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
   }
   HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->tokens_host), 16 * sizeof(int), hipHostMallocDefault));
   HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->result_host), 4 * sizeof(int), hipHostMallocDefault));
+  if (hipHostGetDevicePointer(reinterpret_cast<void**>(&h->result_mirror), h->result_host, 0) != hipSuccess)
+    h->result_mirror = nullptr;   // the step then copies the result back
   if ((rc = dalloc_z(h, &h->draft_res, (size_t)kMaxRows * 4))) return rc;
   if ((rc = dalloc_z(h, &h->tree_dev, (size_t)kMaxRows * 4))) return rc;
   if ((rc = dalloc_z(h, &h->batch_dev, (size_t)batch_words(h)))) return rc;
@@ -1013,9 +1016,10 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   a.q = q_dev; a.u = u_dev;
   a.result = h->result_dev;
   a.acc_ws = h->acc_ws;
+  a.result_mirror = h->result_mirror;   // the acceptance writes the result to the host itself
   if (he == hipSuccess) he = launch_accept(a, h->stream);
   if (he == hipSuccess && h->profiling) he = hipEventRecord(h->ev[2], h->stream);
-  if (he == hipSuccess)
+  if (he == hipSuccess && !a.result_mirror)
     he = hipMemcpyAsync(h->result_host, h->result_dev, 4 * sizeof(int), hipMemcpyDeviceToHost, h->stream);
   if (he == hipSuccess && logits_dev)
     he = hipMemcpy2DAsync(logits_dev, (size_t)c.vocab * 4, h->logits, (size_t)h->ldl * 4, (size_t)c.vocab * 4, m,

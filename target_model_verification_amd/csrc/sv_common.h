@@ -177,6 +177,7 @@ struct AcceptParams {
   const float* q; const float* u;
   int* result;          // [3]
   float* acc_ws;        // kAccFloats words, tickets zero at first use
+  int* result_mirror;   // single-sequence step: result[0..3] also here (pinned host memory), else null
 };
 
 // Acceptance workspace (words): the decision of the stochastic tests (row of
