@@ -182,6 +182,12 @@ bool check_gemm_walk(const GemmShape& s, int G, size_t ws_floats, size_t n_ticke
           err = std::string(s.name) + ": split-K segments out of K order or not covering K";
           return false;
         }
+        // fixed order: every partial after the first is one piece (aligned,
+        // at most one batch), so the sum does not depend on the work split
+        if (s.fixed && i > 0 && (q.len > U || q.c % U != 0)) {
+          err = std::string(s.name) + ": a fixed-order partial after the first is not one piece";
+          return false;
+        }
         k += q.len;
       }
       if (k != M.nkc) {
