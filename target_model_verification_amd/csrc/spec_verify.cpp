@@ -98,6 +98,7 @@ struct spec_verify {
   int* result_dev = nullptr;
   float* acc_ws = nullptr;      // acceptance: tickets, partial statistics, draw tile sums
   int* tokens_host = nullptr;   // pinned
+  int* tokens_mapped = nullptr;   // device view of tokens_host (the step's kernels read the ids there), or null
   int* result_host = nullptr;   // pinned
   int* result_mirror = nullptr;   // device view of result_host (the step's acceptance writes it), or null
   int* draft_res = nullptr;     // self-speculative draft: [kMaxRows][4] acceptance records (device)
@@ -724,6 +725,8 @@ int create_impl(spec_verify* h, const spec_tensor* tensors, int32_t n_tensors, c
     if ((rc = dalloc_z(h, &h->route, (size_t)route_words(E, c.top_k)))) return rc;
   }
   HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->tokens_host), 16 * sizeof(int), hipHostMallocDefault));
+  if (hipHostGetDevicePointer(reinterpret_cast<void**>(&h->tokens_mapped), h->tokens_host, 0) != hipSuccess)
+    h->tokens_mapped = nullptr;   // the step then uploads the ids
   HIPCHK(hipHostMalloc(reinterpret_cast<void**>(&h->result_host), 4 * sizeof(int), hipHostMallocDefault));
   if (hipHostGetDevicePointer(reinterpret_cast<void**>(&h->result_mirror), h->result_host, 0) != hipSuccess)
     h->result_mirror = nullptr;   // the step then copies the result back
@@ -981,10 +984,14 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   if (!union_rec && h->profiling && moe) union_rec = h->union_dev_prof;   // allocated at create
   const bool stamps = h->prof_mode == 1;
 
+  // the kernels read the ids from pinned host memory (no upload), unless
+  // the device cannot map it
   std::memcpy(h->tokens_host, tokens, sizeof(int32_t) * m);
-  hipError_t he = hipMemcpyAsync(h->tokens_dev, h->tokens_host, sizeof(int32_t) * m, hipMemcpyHostToDevice,
-                                 h->stream);
-  PassP p = pass_params(h, m, L, h->tokens_dev, c.top_k);
+  const int* tok = h->tokens_mapped ? h->tokens_mapped : h->tokens_dev;
+  hipError_t he = h->tokens_mapped ? hipSuccess
+                                   : hipMemcpyAsync(h->tokens_dev, h->tokens_host, sizeof(int32_t) * m,
+                                                    hipMemcpyHostToDevice, h->stream);
+  PassP p = pass_params(h, m, L, tok, c.top_k);
   p.reuse_cap = reuse_cap;
   p.reuse_alpha = reuse_alpha;
   p.reuse_w = reuse_w;
@@ -1010,7 +1017,7 @@ int step_impl(spec_verify* h, const int32_t* tokens, int32_t k, int32_t mode, co
   if (h->profiling) he = hipEventRecord(h->ev[1], h->stream);
   AcceptParams a{};
   a.k = k; a.V = c.vocab; a.L = L; a.mode = mode; a.n_stat = h->n_stat;
-  a.tokens = h->tokens_dev;
+  a.tokens = tok;
   a.st_max = h->st_max; a.st_sum = h->st_sum; a.st_idx = h->st_idx;
   a.logits = h->logits; a.ldl = h->ldl;
   a.q = q_dev; a.u = u_dev;
