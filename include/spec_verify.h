@@ -174,8 +174,11 @@ int spec_verify_create(const spec_config* cfg, const spec_tensor* tensors, int32
  *   logits_dev: NULL or device fp32 [k+1][vocab] receiving the block's logits.
  * Requires kv_len + k + 1 <= max_ctx (else SPEC_ECAPACITY).  Enqueues the
  * pass on the handle's stream and returns after the 12-byte result has
- * reached the host (one stream synchronization; the acceptance kernel
- * writes it into pinned host memory of the handle).  The committed length
+ * reached the host (one stream synchronization).  No copy runs in either
+ * direction: the ids are staged in pinned host memory of the handle, which
+ * the kernels read through its device mapping, and the acceptance kernel
+ * writes the result into pinned host memory of the handle.  The caller's
+ * tokens array is read before the call returns only.  The committed length
  * becomes out->kv_len; cache entries at or beyond it are dead. */
 int spec_verify_step(spec_verify_t* h, const int32_t* tokens, int32_t k, int32_t mode,
                      const float* q_dev, const float* u_dev, spec_step_result* out,
