@@ -178,7 +178,7 @@ int spec_verify_create(const spec_config* cfg, const spec_tensor* tensors, int32
  * direction: the ids are staged in pinned host memory of the handle, which
  * the kernels read through its device mapping, and the acceptance kernel
  * writes the result into pinned host memory of the handle.  The caller's
- * tokens array is read before the call returns only.  The committed length
+ * tokens array is copied before any work is enqueued.  The committed length
  * becomes out->kv_len; cache entries at or beyond it are dead. */
 int spec_verify_step(spec_verify_t* h, const int32_t* tokens, int32_t k, int32_t mode,
                      const float* q_dev, const float* u_dev, spec_step_result* out,
